@@ -1,0 +1,153 @@
+"""CPU oracle for the Engram forward path -- TEST INFRASTRUCTURE ONLY.
+
+Python loader for `liboracle.so` (plain C, `engram_oracle.c`).  Only `tests/`,
+`__graft_entry__.smoke()` and the CPU-baseline leg of `bench.py` may import
+this package; the product (`gram_hash_embedding_amd`) never does.
+
+Every wrapper takes and returns numpy arrays.  bf16 values travel as their
+uint16 bit patterns.  The hash, gather and dequant are exact; the projection
+and gate return float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = [os.path.join(_HERE, "engram_oracle.c")]
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so with gcc (no GPU toolchain involved)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp", *SOURCES, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.oracle_hash.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p]
+        L.oracle_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p]
+        L.oracle_wkv.argtypes = [p, p, p, i64, i32, i32]
+        L.oracle_gate_dot.argtypes = [p, p, i64, p, p, ctypes.c_double, p, i64, i32, i32]
+        L.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3fn_decode.restype = ctypes.c_float
+        L.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise OracleError(f"{name} returned {rc}")
+
+
+def hash(input_ids, start_pos, token_mask, token_map, cache, multipliers, primes, offsets, pad_id,
+         dead=-1):
+    """ids int64 [B, L, E, C]; `cache` (int64 [cache_B, cache_L], C-contiguous) is updated in place."""
+    ids = _c(input_ids, np.int64)
+    B, L = ids.shape
+    mask = _c(token_mask, np.uint8)
+    tmap = _c(token_map, np.int64)
+    mult = _c(multipliers, np.int64)
+    pr = _c(primes, np.int64)
+    off = _c(offsets, np.int64)
+    if not (cache.flags.c_contiguous and cache.dtype == np.int64):
+        raise ValueError("cache must be a C-contiguous int64 array")
+    E, N = mult.shape
+    H = pr.shape[2]
+    out = np.empty((B, L, E, (N - 1) * H), dtype=np.int64)
+    rc = lib().oracle_hash(_ptr(ids), B, L, start_pos, _ptr(mask), _ptr(tmap), tmap.size, _ptr(cache),
+                           cache.shape[0], cache.shape[1], _ptr(mult), _ptr(pr), _ptr(off), E, N, H,
+                           pad_id, dead, _ptr(out))
+    _check(rc, "oracle_hash")
+    return out
+
+
+def gather_dequant(hash_ids, weight, scale, row_start=0, block_size=32, n_cols=None, want_raw=False):
+    """hash_ids int64 [T, stride] (first `n_cols` columns used) -> bf16 bits uint16 [T, C, D]
+    (and, if want_raw, the gathered bytes [T, C, D] and scales [T, C, D/blk])."""
+    ids = _c(hash_ids, np.int64)
+    T, stride = ids.shape
+    C = stride if n_cols is None else n_cols
+    w = _c(weight, np.uint8)
+    s = _c(scale, np.float32)
+    R, D = w.shape
+    out = np.empty((T, C, D), dtype=np.uint16)
+    raw = np.empty((T, C, D), dtype=np.uint8) if want_raw else None
+    rsc = np.empty((T, C, D // block_size), dtype=np.float32) if want_raw else None
+    rc = lib().oracle_gather_dequant(_ptr(ids), T, stride, C, _ptr(w), _ptr(s), R, row_start, D, block_size,
+                                     _ptr(out), _ptr(raw), _ptr(rsc))
+    _check(rc, "oracle_gather_dequant")
+    return (out, raw, rsc) if want_raw else out
+
+
+def wkv(a_bits, w_bits):
+    """a [T, K], w [Nout, K] as bf16 bits -> float64 [T, Nout]."""
+    a = _c(a_bits, np.uint16)
+    w = _c(w_bits, np.uint16)
+    T, K = a.shape
+    Nout = w.shape[0]
+    out = np.empty((T, Nout), dtype=np.float64)
+    _check(lib().oracle_wkv(_ptr(a), _ptr(w), _ptr(out), T, K, Nout), "oracle_wkv")
+    return out
+
+
+def gate_dot(x_bits, kv_bits, q_bits, k_bits, eps):
+    """x [T, hc, dim]; kv [T, >= hc*dim] (key = first hc*dim columns); q, k [hc, dim];
+    all bf16 bits -> float64 dot [T, hc]."""
+    x = _c(x_bits, np.uint16)
+    kv = _c(kv_bits, np.uint16)
+    q = _c(q_bits, np.uint16)
+    k = _c(k_bits, np.uint16)
+    T, hc, dim = x.shape
+    out = np.empty((T, hc), dtype=np.float64)
+    rc = lib().oracle_gate_dot(_ptr(x), _ptr(kv), kv.shape[1], _ptr(q), _ptr(k), float(eps), _ptr(out), T, hc,
+                               dim)
+    _check(rc, "oracle_gate_dot")
+    return out
+
+
+def e4m3fn_decode(byte: int) -> float:
+    return float(lib().oracle_e4m3fn_decode(byte))
+
+
+def bf16_rne(values) -> np.ndarray:
+    """float32 -> bf16 bits, one value at a time through the oracle's rounding."""
+    v = np.asarray(values, dtype=np.float32).reshape(-1)
+    f = lib().oracle_bf16_rne
+    return np.array([f(float(x)) for x in v], dtype=np.uint16)
+
+
+def bf16_bits_to_float(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)

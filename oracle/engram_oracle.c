@@ -1,0 +1,222 @@
+/*
+ * CPU oracle for the Engram forward path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct host implementation of what the path
+ * computes, written from the DeepSeek V4.1 model pages
+ * (open-model-atlas "stack-hashes" page and its duplicates on the
+ * atlas.klimoza.dev "engram-first/lookup" and "engram-first/streams" pages):
+ *
+ *   hash         -- the engram hash module's forward (stack-hashes page)
+ *   gather+dequant -- ParallelEngramEmbedding.forward
+ *   wkv          -- the `wkv` Linear of Engram.forward
+ *   gate dot     -- Engram.forward up to the gate pre-activation `dot`
+ *
+ * Only tests, the smoke entry point and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or constant with the
+ * HIP library: it includes nothing but the C standard library.
+ *
+ * Floating point: the dequant follows the pages' precision exactly (fp32
+ * product, then bf16), everything else is accumulated in double.  Built with
+ * -ffp-contract=off so no multiply-add is fused behind the source's back.
+ *
+ * Parity pins (tests/test_oracle_*.py): the hash against a Python big-int
+ * brute force and against invariants the pages state; the decode against
+ * torch's float8_e4m3fn for all 256 bytes; bf16 rounding against torch; the
+ * projection against numpy's float64 matmul; the gate on hand-built vectors
+ * with closed-form results.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "engram_oracle.h"
+
+/* ------------------------------------------------------------------------ */
+/* step 1: hash                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* torch's `%` on int64 takes the sign of the divisor (floor modulo). */
+static int64_t floor_mod(int64_t a, int64_t p) {
+    int64_t r = a % p; /* C truncates toward zero */
+    if (r != 0 && ((r < 0) != (p < 0))) r += p;
+    return r;
+}
+
+/* int64 product with two's-complement wrap, as torch's int64 `*` does. */
+static int64_t wrap_mul(int64_t a, int64_t b) {
+    return (int64_t)((uint64_t)a * (uint64_t)b);
+}
+
+int oracle_hash(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                int64_t* cache, int64_t cache_B, int64_t cache_L,
+                const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                int E, int N, int H, int64_t pad_id, int64_t dead, int64_t* hash_ids) {
+    if (B < 0 || L < 0 || start_pos < 0 || E < 1 || N < 2 || H < 1) return ORACLE_EINVAL;
+    if (B > cache_B || start_pos + L > cache_L) return ORACLE_ERANGE;
+    const int C = (N - 1) * H;
+
+    /* compressed = token_map[input_ids]; masked -> DEAD; write the cache.
+     * (An id outside the vocabulary is treated like a masked token.) */
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            int64_t id = input_ids[b * L + l];
+            int64_t c = (id >= 0 && id < vocab) ? token_map[id] : dead;
+            if (token_mask && !token_mask[b * L + l]) c = dead;
+            cache[b * cache_L + start_pos + l] = c;
+        }
+    }
+
+    int64_t* tokens = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    int64_t* products = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (!tokens || !products) { free(tokens); free(products); return ORACLE_ENOMEM; }
+
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t p = start_pos + l;
+            /* one lookback at a time; once a slot is blocked (before the start of
+             * the sequence, or a masked source) every longer lookback is too */
+            int blocked = 0;
+            for (int s = 0; s < N; ++s) {
+                int64_t q = p - s;
+                if (q < 0) q = 0;
+                int64_t source = cache[b * cache_L + q];
+                if (p < s || source == dead) blocked = 1;
+                tokens[s] = blocked ? pad_id : source;
+            }
+            int64_t* out = hash_ids + (b * L + l) * (int64_t)E * C;
+            for (int e = 0; e < E; ++e) {
+                for (int s = 0; s < N; ++s) products[s] = wrap_mul(tokens[s], multipliers[e * N + s]);
+                /* after XOR-ing lookback i the running value is the (i+1)-gram hash */
+                int64_t rolling = products[0];
+                for (int i = 1; i < N; ++i) {
+                    rolling ^= products[i];
+                    for (int h = 0; h < H; ++h) {
+                        const int col = (i - 1) * H + h;
+                        const int64_t prime = primes[((int64_t)e * (N - 1) + (i - 1)) * H + h];
+                        out[e * C + col] = floor_mod(rolling, prime) + offsets[e * C + col];
+                    }
+                }
+            }
+        }
+    }
+    free(tokens);
+    free(products);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 2+3: gather and block dequant                                        */
+/* ------------------------------------------------------------------------ */
+
+/* float8_e4m3fn from the OCP 8-bit floating point definition: 1 sign bit,
+ * 4 exponent bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 = NaN. */
+float oracle_e4m3fn_decode(uint8_t byte) {
+    const int sign = byte >> 7;
+    const int expo = (byte >> 3) & 0xF;
+    const int mant = byte & 0x7;
+    float v;
+    if (expo == 0xF && mant == 0x7) return NAN;
+    if (expo == 0)
+        v = ldexpf((float)mant, -9);              /* subnormal: m * 2^-6 / 8 */
+    else
+        v = ldexpf((float)(8 + mant), expo - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* float -> bfloat16 bit pattern, round to nearest, ties to even. */
+uint16_t oracle_bf16_rne(float f) {
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) /* NaN: keep sign, quiet it */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep = u >> 16, rest = u & 0xFFFFu;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+    return (uint16_t)keep;
+}
+
+int oracle_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int C,
+                          const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
+                          int D, int blk, uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale) {
+    if (T < 0 || C < 1 || D < 1 || blk < 1 || D % blk != 0 || R < 1) return ORACLE_EINVAL;
+    const int S = D / blk;
+    const int64_t vocab_end = row_start + R;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int c = 0; c < C; ++c) {
+            const int64_t idx = hash_ids[t * id_token_stride + c];
+            const int masked = idx < row_start || idx >= vocab_end;
+            const int64_t local = masked ? 0 : idx - row_start;
+            const uint8_t* w = weight + local * D;
+            const float* sc = scale + local * S;
+            const int64_t o = (t * C + c);
+            for (int j = 0; j < D; ++j) {
+                /* fp32 product (one rounding) then bf16 (a second rounding) */
+                float prod = oracle_e4m3fn_decode(w[j]) * sc[j / blk];
+                out_bf16[o * D + j] = masked ? 0 : oracle_bf16_rne(prod);
+                if (out_fp8) out_fp8[o * D + j] = w[j];
+            }
+            if (out_scale)
+                for (int s = 0; s < S; ++s) out_scale[o * S + s] = sc[s];
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 4: wkv projection                                                    */
+/* ------------------------------------------------------------------------ */
+
+double oracle_bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+int oracle_wkv(const uint16_t* a, const uint16_t* w, double* kv, int64_t T, int K, int Nout) {
+    if (T < 0 || K < 1 || Nout < 1) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int o = 0; o < Nout; ++o) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += oracle_bf16_to_double(a[t * K + k]) * oracle_bf16_to_double(w[(int64_t)o * K + k]);
+            kv[t * Nout + o] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* step 5: gate pre-activation                                               */
+/* ------------------------------------------------------------------------ */
+
+int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
+                    const uint16_t* k_weight, double eps, double* dot, int64_t T, int hc, int dim) {
+    if (T < 0 || hc < 1 || dim < 1 || ld_kv < (int64_t)hc * dim) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int c = 0; c < hc; ++c) {
+            const uint16_t* h = x + (t * hc + c) * (int64_t)dim;
+            const uint16_t* key = kv + t * ld_kv + (int64_t)c * dim;
+            double hh = 0.0, kk = 0.0, hwk = 0.0;
+            for (int j = 0; j < dim; ++j) {
+                const double hv = oracle_bf16_to_double(h[j]);
+                const double kv_ = oracle_bf16_to_double(key[j]);
+                /* the two weights are only ever used as their product */
+                const double wv = oracle_bf16_to_double(q_weight[c * dim + j]) *
+                                  oracle_bf16_to_double(k_weight[c * dim + j]);
+                hh += hv * hv;
+                kk += kv_ * kv_;
+                hwk += hv * wv * kv_;
+            }
+            /* normalised per (token, copy) over dim, not jointly over the copies */
+            const double rstd = (1.0 / sqrt(hh / dim + eps)) * (1.0 / sqrt(kk / dim + eps));
+            dot[t * hc + c] = hwk * rstd / sqrt((double)dim);
+        }
+    }
+    return ORACLE_OK;
+}
