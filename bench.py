@@ -1,0 +1,259 @@
+"""Benchmark of the Engram forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: the hash of all tokens, then per engram layer the
+fp8 gather + dequant, the wkv projection and the gate pre-activation dot.
+The default workload is the long prefill: one sequence of 65,536 tokens, one
+engram layer with the released 384,006,168-row fp8 table (24.6 GB, D = 64,
+8 hash heads, n-grams up to 4), dim 5120, hc_mult 4.
+
+Prints one JSON line: whole-job tokens/s, per-kernel timings, the roofline
+of the dominant kernel (wkv, bf16 MFMA) from HIP events on the launch
+stream, and the CPU oracle's throughput on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Engram fwd tokens/s on 1 MI355X; gather HBM GB/s & wkv MFMA % of peak"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, has_mask: bool):
+    """Bytes / flops each kernel must move or do per token (per layer for the per-layer kernels)."""
+    E, C, D, blk = cfg.n_layers, cfg.n_hash_cols, cfg.head_dim, cfg.block_size
+    return {
+        # input id, mask byte, token_map entry, cache write, E*C int64 ids out
+        "hash_bytes": 8 + (1 if has_mask else 0) + 8 + 8 + 8 * E * C,
+        # per column: int64 id in, D fp8 bytes + D/blk fp32 scales gathered, D bf16 out
+        "gather_bytes": C * (8 + D + 4 * (D // blk) + 2 * D),
+        "wkv_flops": 2 * cfg.K * cfg.n_out,
+        # A row in, kv row out (the W read is once per launch, added separately)
+        "wkv_bytes": 2 * cfg.K + 2 * cfg.n_out,
+        # x copy rows + key rows in (bf16), hc fp32 dots out
+        "gate_bytes": 2 * cfg.hc_mult * cfg.dim * 2 + 4 * cfg.hc_mult,
+    }
+
+
+def source_sha(name: str) -> str:
+    path = os.path.join(ROOT, "gram_hash_embedding_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{os.path.splitext(kernel_file)[0]}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, sample_tokens: int):
+    """The CPU oracle, as it stands, over the first `sample_tokens` tokens of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    cfg, hi = wl.cfg, wl.host
+    B, L = hi.input_ids.shape
+    S = min(sample_tokens, L)
+    ids_in = np.ascontiguousarray(hi.input_ids[:1, :S])
+    mask = None if hi.token_mask is None else np.ascontiguousarray(hi.token_mask[:1, :S])
+    timings = {}
+    t0 = time.perf_counter()
+    ids = oracle.hash(ids_in, 0, mask, hi.token_map, np.zeros((1, S), np.int64), hi.multipliers, hi.primes,
+                      hi.offsets, cfg.pad_id, synth.DEAD)
+    timings["hash"] = time.perf_counter() - t0
+    C, D, blk = cfg.n_hash_cols, cfg.head_dim, cfg.block_size
+    x_bits = wl.x[0][:S].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    for e in range(cfg.n_layers):
+        lw = wl.fwd.layers[e]
+        cw, cs, remap = synth.compact_table(ids.reshape(S, cfg.n_layers, C)[:, e], cfg.rows_alloc[e],
+                                            synth.table_seed(cfg, e), D, blk)
+        w_bits = lw.wkv.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        q_bits = lw.q_weight.view(torch.int16).cpu().numpy().view(np.uint16)
+        k_bits = lw.k_weight.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        a = oracle.gather_dequant(remap, cw, cs, block_size=blk)
+        t1 = time.perf_counter()
+        kv = oracle.wkv(a.reshape(S, C * D), w_bits)
+        t2 = time.perf_counter()
+        kv_bf16 = torch.from_numpy(kv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        t3 = time.perf_counter()
+        oracle.gate_dot(x_bits, kv_bf16, q_bits, k_bits, cfg.eps)
+        t4 = time.perf_counter()
+        timings["gather_dequant"] = timings.get("gather_dequant", 0.0) + (t1 - t0)
+        timings["wkv"] = timings.get("wkv", 0.0) + (t2 - t1)
+        timings["gate_dot"] = timings.get("gate_dot", 0.0) + (t4 - t3)
+    total = sum(timings.values())
+    return {
+        "value": round(S / total, 3),
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {S} tokens of the workload through the whole path (hash, gather+dequant, wkv, gate dot); "
+                  f"{total:.2f} s of CPU time",
+        "seconds": {k: round(v, 3) for k, v in timings.items()},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload (1..5); 3 = long prefill")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the CPU oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a counter reference for rocprofv3)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange; only the one-GPU share is built)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import synth.workload as sw
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {args.copy_probe_mb} MiB device-to-device")
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.decode_steps:
+        print("bench.py: the decode workload is a parity case, not a bench line", file=sys.stderr)
+        return 2
+    log(f"building workload {cfg.name} ...")
+    t_build = time.perf_counter()
+    wl = sw.build(cfg, device=dev)
+    torch.cuda.synchronize()
+    log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
+    fwd = wl.fwd
+
+    def step(events=None):
+        fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    T = cfg.tokens
+    value = T / (wall / args.steps)
+
+    algo = algorithmic(cfg, wl.token_mask is not None)
+    kern = {}
+    for name, pairs in events.items():
+        ms = [s.elapsed_time(e) for s, e in pairs]
+        kern[name] = {"launches": len(ms), "avg_us": round(1e3 * sum(ms) / len(ms), 2)}
+    E = cfg.n_layers
+    W_bytes = 2 * cfg.K * cfg.n_out
+    if "hash" in kern:
+        kern["hash"]["GB/s"] = round(T * algo["hash_bytes"] / (kern["hash"]["avg_us"] * 1e3), 1)
+    g = kern["gather_dequant"]
+    g["GB/s"] = round(T * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
+    g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
+    w = kern["wkv"]
+    w["TFLOP/s"] = round(T * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
+    w["frac_mfma"] = round(w["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
+    gd = kern["gate_dot"]
+    gd["GB/s"] = round(T * algo["gate_bytes"] / (gd["avg_us"] * 1e3), 1)
+    gd["frac_hbm"] = round(gd["GB/s"] / PEAK_HBM_GBS, 4)
+
+    workload = cfg.name
+    traffic = load_traffic("wkv.hip", workload)
+    roofline = {
+        "kernel": "wkv",
+        "bound": "mfma",
+        "achieved": w["TFLOP/s"],
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": w["frac_mfma"],
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": T * algo["wkv_bytes"] + W_bytes,
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: Zipf(1.1) token ids, counter-generated fp8 table, N(0,1)/N(0,0.02) bf16)",
+        "config": {
+            "workload": f"{workload}: B={cfg.batch} L={cfg.seqlen} start_pos={cfg.start_pos}, {E} engram layer(s) "
+                        f"of {cfg.rows_alloc[0]:,} fp8 rows x D={cfg.head_dim}, {cfg.n_heads} hash heads, "
+                        f"max n-gram {cfg.max_ngram_size}, dim={cfg.dim}, hc_mult={cfg.hc_mult}",
+            "global_batch": cfg.batch,
+            "seq_len": cfg.seqlen,
+            "tokens_per_step": T,
+            "engram_layers": E,
+            "table_rows": list(cfg.rows_alloc[:E]),
+            "head_dim": cfg.head_dim,
+            "n_hash_cols": cfg.n_hash_cols,
+            "dim": cfg.dim,
+            "hc_mult": cfg.hc_mult,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "kernels": kern,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline on {args.cpu_sample} tokens ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

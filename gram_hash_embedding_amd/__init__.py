@@ -1,0 +1,195 @@
+"""Engram forward hot path on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libengram.so (include/engram.h).  Each function
+has the name of its C entry point, takes torch tensors that already live on
+the GPU, checks dtype/shape/contiguity, and passes raw device pointers plus
+the current HIP stream.  Every step of the path runs in the library's HIP
+kernels; there is no fallback: if libengram.so is missing or a call fails,
+an exception is raised.
+
+    engram_hash            -- n-gram hash ids (+ compressed-id cache update)
+    engram_gather_dequant  -- fp8 row gather + block-scale dequant -> bf16
+    engram_wkv             -- kv = A @ W^T on bf16 matrix cores
+    engram_gate_dot        -- per-(token, copy) RMS-normalised gate pre-activation
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_ERANGE, ENGRAM_EHIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libengram.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with `python -m gram_hash_embedding_amd.build` "
+                              "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, p, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+        L.engram_hash.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p, p]
+        L.engram_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p, p]
+        L.engram_wkv.argtypes = [p, p, p, i64, i32, i32, p]
+        L.engram_gate_dot.argtypes = [p, p, i64, p, p, f32, p, i64, i32, i32, p]
+        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_wkv, L.engram_gate_dot, L.engram_abi_version):
+            f.restype = ctypes.c_int
+        L.engram_status_string.argtypes = [ctypes.c_int]
+        L.engram_status_string.restype = ctypes.c_char_p
+        L.engram_last_error.argtypes = []
+        L.engram_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != ENGRAM_OK:
+        raise EngramError(status, lib().engram_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype, ndim=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def engram_hash(input_ids, start_pos, token_mask, token_map, cache, multipliers, primes, offsets, pad_id,
+                dead=-1, out=None, stream=None):
+    """Hash ids int64 [B, L, E, (N-1)*H]; `cache` (int64 [cache_B, cache_L]) is updated in place."""
+    import torch
+
+    B, L = input_ids.shape
+    E, N = multipliers.shape
+    H = primes.shape[2]
+    C = (N - 1) * H
+    if out is None:
+        out = torch.empty((B, L, E, C), dtype=torch.int64, device=input_ids.device)
+    if tuple(out.shape) != (B, L, E, C):
+        raise ValueError("out has the wrong shape")
+    if tuple(primes.shape) != (E, N - 1, H) or tuple(offsets.shape) != (E, C):
+        raise ValueError("primes must be [E, N-1, H] and offsets [E, (N-1)*H]")
+    mask_p = None
+    if token_mask is not None:
+        if tuple(token_mask.shape) != (B, L):
+            raise ValueError("token_mask must be [B, L]")
+        if token_mask.dtype == torch.bool:
+            token_mask = token_mask.view(torch.uint8)
+        mask_p = _dev(token_mask, "token_mask", torch.uint8, 2)
+    _check(lib().engram_hash(
+        _dev(input_ids, "input_ids", torch.int64, 2), B, L, int(start_pos), mask_p,
+        _dev(token_map, "token_map", torch.int64, 1), token_map.numel(),
+        _dev(cache, "cache", torch.int64, 2), cache.shape[0], cache.shape[1],
+        _dev(multipliers, "multipliers", torch.int64, 2), _dev(primes, "primes", torch.int64, 3),
+        _dev(offsets, "offsets", torch.int64, 2), E, N, H, int(pad_id), int(dead),
+        _dev(out, "out", torch.int64, 4), _stream(stream)))
+    return out
+
+
+def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n_cols=None, layer=0,
+                          out=None, out_fp8=None, out_scale=None, stream=None):
+    """bf16 [T, C, D] rows for one layer's ids.
+
+    hash_ids: int64 [B, L, E, C] (engram_hash's output; `layer` picks e) or [T, C].
+    weight: float8_e4m3fn or uint8 [R, D]; scale: float32 [R, D/block_size].
+    Optional out_fp8 (uint8 [T, C, D]) and out_scale (float32 [T, C, D/blk]) receive the raw gathered bytes/scales.
+    """
+    import torch
+
+    if hash_ids.dim() == 4:
+        B, L, E, C = hash_ids.shape
+        T, stride, base = B * L, E * C, layer * C
+    elif hash_ids.dim() == 2:
+        T, C = hash_ids.shape
+        stride, base = C, 0
+    else:
+        raise ValueError("hash_ids must be [B, L, E, C] or [T, C]")
+    if n_cols is not None:
+        C = n_cols
+    if not hash_ids.is_contiguous() or hash_ids.dtype != torch.int64 or not hash_ids.is_cuda:
+        raise ValueError("hash_ids must be a contiguous int64 GPU tensor")
+    ids_ptr = ctypes.c_void_p(hash_ids.data_ptr() + 8 * base)
+    if weight.dtype == torch.float8_e4m3fn:
+        weight = weight.view(torch.uint8)
+    R, D = weight.shape
+    if out is None:
+        out = torch.empty((T, C, D), dtype=torch.bfloat16, device=hash_ids.device)
+    if out.numel() != T * C * D:
+        raise ValueError("out has the wrong size")
+    if tuple(scale.shape) != (R, D // block_size):
+        raise ValueError("scale must be [R, D/block_size]")
+    p8 = None if out_fp8 is None else _dev(out_fp8, "out_fp8", torch.uint8)
+    ps = None if out_scale is None else _dev(out_scale, "out_scale", torch.float32)
+    _check(lib().engram_gather_dequant(
+        ids_ptr, T, stride, C, _dev(weight, "weight", torch.uint8, 2), _dev(scale, "scale", torch.float32, 2),
+        R, int(row_start), D, int(block_size), _dev(out, "out", torch.bfloat16), p8, ps, _stream(stream)))
+    return out
+
+
+def engram_wkv(a, w, out=None, stream=None):
+    """kv bf16 [T, Nout] = a [T, K] @ w[Nout, K]^T (bf16 in, fp32 accumulation)."""
+    import torch
+
+    a2 = a.reshape(a.shape[0], -1) if a.dim() == 3 else a
+    T, K = a2.shape
+    Nout, K2 = w.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: a has {K}, w has {K2}")
+    if out is None:
+        out = torch.empty((T, Nout), dtype=torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (T, Nout):
+        raise ValueError("out must be [T, Nout]")
+    _check(lib().engram_wkv(_dev(a2, "a", torch.bfloat16, 2), _dev(w, "w", torch.bfloat16, 2),
+                            _dev(out, "out", torch.bfloat16, 2), T, K, Nout, _stream(stream)))
+    return out
+
+
+def engram_gate_dot(x, kv, q_weight, k_weight, eps, out=None, stream=None):
+    """dot float32 [T, hc] from x bf16 [T, hc, dim] (or [B, L, hc, dim]) and the keys in kv [T, >= hc*dim]."""
+    import torch
+
+    x3 = x.reshape(-1, x.shape[-2], x.shape[-1])
+    T, hc, dim = x3.shape
+    if kv.dim() != 2 or kv.shape[0] != T:
+        raise ValueError("kv must be [T, ld]")
+    if tuple(q_weight.shape) != (hc, dim) or tuple(k_weight.shape) != (hc, dim):
+        raise ValueError("q_weight and k_weight must be [hc, dim]")
+    if out is None:
+        out = torch.empty((T, hc), dtype=torch.float32, device=x.device)
+    _check(lib().engram_gate_dot(
+        _dev(x3, "x", torch.bfloat16, 3), _dev(kv, "kv", torch.bfloat16, 2), kv.shape[1],
+        _dev(q_weight, "q_weight", torch.bfloat16, 2), _dev(k_weight, "k_weight", torch.bfloat16, 2),
+        float(eps), _dev(out, "out", torch.float32), T, hc, dim, _stream(stream)))
+    return out
+
+
+__all__ = ["engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "EngramError", "lib",
+           "LIB_PATH"]

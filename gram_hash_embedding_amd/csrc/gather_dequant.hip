@@ -1,0 +1,180 @@
+// engram_gather_dequant: fused fp8 row gather + block-scale dequant to bf16.
+//
+// Computes ParallelEngramEmbedding.forward of the DeepSeek V4.1
+// "stack-hashes" page for one rank's rows [row_start, row_start + R): the
+// range mask, the two embedding lookups (fp8 row and its fp32 block scales),
+// the dequant (fp32 product, then bf16) and the zero fill of out-of-range
+// ids.  The table stays fp8 in HBM; only gathered rows are ever widened.
+//
+// Design (gfx950): HBM-bound random gather.
+// - A table row is D bytes (64 at the released shape): D/16 lanes each move
+//   one 16-byte piece with a single dwordx4 load, and the same lanes fetch
+//   the row's fp32 scale (lanes of one 32-wide block read the same word).
+// - Every lane handles U rows: all U ids are loaded first, then all U row
+//   and scale loads are issued back to back, and only then is anything
+//   converted, so U * (16 + 4) bytes per lane are in flight to cover the
+//   latency of random HBM reads.
+// - Decode: v_cvt_pk_f32_fp8 (OCP E4M3FN on gfx950) two bytes at a time,
+//   v_mul_f32 by the scale (round to nearest even), v_cvt_pk_bf16_f32 (round
+//   to nearest even): the same two roundings as the page.
+// - Output rows (t, c) are laid out consecutively, so a wave's stores for
+//   one u cover 64/(D/16) whole rows: 2 KB contiguous at D = 64.
+#include "common.h"
+
+namespace engram {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct GatherArgs {
+    const int64_t* ids;
+    int64_t stride;
+    int64_t W;  // rows to produce = T * C
+    int C;
+    const uint8_t* weight;
+    const float* scale;
+    int64_t R, row_start;
+    int blk;
+    uint16_t* out;
+    uint8_t* out_fp8;
+    float* out_scale;
+};
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16 fp8 bytes times the scale -> 16 bf16 (two 16-byte vectors).
+__device__ inline void dequant16(const u32x4& v, float s, u32x4& o0, u32x4& o1) {
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[i]), false);  // bytes 0, 1
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[i]), true);   // bytes 2, 3
+        r[2 * i] = pack_bf16(a.x * s, a.y * s);
+        r[2 * i + 1] = pack_bf16(b.x * s, b.y * s);
+    }
+    o0 = u32x4{r[0], r[1], r[2], r[3]};
+    o1 = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+template <int D, int U>
+__global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) {
+    constexpr int LPR = D / 16;              // lanes per row
+    constexpr int RPS = kThreads / LPR;      // rows per step of the block
+    const int lane_in_row = threadIdx.x % LPR;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (RPS * U) + threadIdx.x / LPR;
+    const int S = D / a.blk;
+    const int sidx = (lane_in_row * 16) / a.blk;  // this lane's scale block
+
+    int64_t row[U];
+    bool ok[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = base + static_cast<int64_t>(u) * RPS;
+        live[u] = w < a.W;
+        int64_t id = 0;
+        if (live[u]) {
+            int64_t t, c;
+            if (a.W <= 0xFFFFFFFFll) {
+                const uint32_t w32 = static_cast<uint32_t>(w);
+                const uint32_t t32 = w32 / static_cast<uint32_t>(a.C);
+                t = t32;
+                c = w32 - t32 * static_cast<uint32_t>(a.C);
+            } else {
+                t = w / a.C;
+                c = w - t * a.C;
+            }
+            id = a.ids[t * a.stride + c];
+        }
+        const int64_t local = id - a.row_start;
+        ok[u] = live[u] && local >= 0 && local < a.R;
+        row[u] = ok[u] ? local : 0;
+    }
+
+    u32x4 v[U];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        v[u] = *reinterpret_cast<const u32x4*>(a.weight + row[u] * D + lane_in_row * 16);
+        sc[u] = a.scale[row[u] * S + sidx];
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!live[u]) continue;
+        const int64_t w = base + static_cast<int64_t>(u) * RPS;
+        u32x4 o0, o1;
+        if (ok[u]) {
+            dequant16(v[u], sc[u], o0, o1);
+        } else {
+            o0 = u32x4{0, 0, 0, 0};
+            o1 = o0;
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(a.out + w * D + lane_in_row * 16);
+        dst[0] = o0;
+        dst[1] = o1;
+        if (a.out_fp8) *reinterpret_cast<u32x4*>(a.out_fp8 + w * D + lane_in_row * 16) = v[u];
+        if (a.out_scale && (lane_in_row * 16) % a.blk == 0) a.out_scale[w * S + sidx] = sc[u];
+    }
+}
+
+template <int D>
+int launch(const GatherArgs& a, hipStream_t stream) {
+    constexpr int U = 8;
+    constexpr int rows_per_block = (kThreads / (D / 16)) * U;
+    const int64_t blocks = (a.W + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gather_dequant: too many rows");
+    hipLaunchKernelGGL((gather_dequant_kernel<D, U>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
+    return check_launch("engram_gather_dequant");
+}
+
+}  // namespace
+}  // namespace engram
+
+using namespace engram;
+
+extern "C" int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                     const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
+                                     int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                                     float* out_scale, void* stream) {
+    if (T < 0) return fail(ENGRAM_EINVAL, "engram_gather_dequant: T < 0");
+    if (C < 1 || C > 1024) return fail(ENGRAM_EINVAL, "engram_gather_dequant: C=%d outside [1, 1024]", C);
+    if (id_token_stride < C) return fail(ENGRAM_EINVAL, "engram_gather_dequant: id_token_stride < C");
+    if (D != 32 && D != 64 && D != 128 && D != 256)
+        return fail(ENGRAM_EINVAL, "engram_gather_dequant: D=%d not in {32, 64, 128, 256}", D);
+    if (blk < 16 || blk % 16 != 0 || D % blk != 0)
+        return fail(ENGRAM_EINVAL, "engram_gather_dequant: blk=%d must be a multiple of 16 dividing D=%d", blk, D);
+    if (R < 1) return fail(ENGRAM_EINVAL, "engram_gather_dequant: R < 1");
+    if (T == 0) return ENGRAM_OK;
+    if (!hash_ids || !weight || !scale || !out_bf16) return fail(ENGRAM_EINVAL, "engram_gather_dequant: null pointer");
+    if (!aligned(hash_ids, 8) || !aligned(weight, 16) || !aligned(scale, 4) || !aligned(out_bf16, 16) ||
+        (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, 4)))
+        return fail(ENGRAM_EINVAL, "engram_gather_dequant: misaligned pointer");
+
+    GatherArgs a;
+    a.ids = hash_ids;
+    a.stride = id_token_stride;
+    a.W = T * C;
+    a.C = C;
+    a.weight = weight;
+    a.scale = scale;
+    a.R = R;
+    a.row_start = row_start;
+    a.blk = blk;
+    a.out = out_bf16;
+    a.out_fp8 = out_fp8;
+    a.out_scale = out_scale;
+    hipStream_t s = as_stream(stream);
+    switch (D) {
+        case 32: return launch<32>(a, s);
+        case 64: return launch<64>(a, s);
+        case 128: return launch<128>(a, s);
+        default: return launch<256>(a, s);
+    }
+}

@@ -1,0 +1,130 @@
+"""One Engram forward pass over the four entry points, with reusable buffers.
+
+The order of the steps is that of the DeepSeek V4.1 "stack-hashes" page: the
+model forward hashes once for all engram layers, then each engram layer
+gathers its rows from its own slice of the ids, projects them with `wkv`
+and forms the gate pre-activation against the residual stream.  This module
+only allocates outputs and calls the HIP entry points in that order.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List
+
+from . import engram_gate_dot, engram_gather_dequant, engram_hash, engram_wkv
+
+
+@dataclasses.dataclass
+class HashState:
+    """Device tensors of the hash module (all int64)."""
+
+    token_map: "torch.Tensor"      # [vocab]
+    cache: "torch.Tensor"          # [max_batch, max_seq]
+    multipliers: "torch.Tensor"    # [E, N]
+    primes: "torch.Tensor"         # [E, N-1, H]
+    offsets: "torch.Tensor"        # [E, (N-1)*H]
+    pad_id: int
+    dead: int = -1
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    """One engram layer: its fp8 table (this GPU's rows), projection and gate weights."""
+
+    weight: "torch.Tensor"         # uint8 / float8_e4m3fn [R, D]
+    scale: "torch.Tensor"          # float32 [R, D/block_size]
+    wkv: "torch.Tensor"            # bf16 [dim*(hc+1), C*D]
+    q_weight: "torch.Tensor"       # bf16 [hc, dim]
+    k_weight: "torch.Tensor"       # bf16 [hc, dim]
+    block_size: int
+    row_start: int = 0
+
+
+class EngramForward:
+    """Runs hash -> (gather+dequant -> wkv -> gate dot) per layer on the current stream."""
+
+    def __init__(self, state: HashState, layers: List[LayerWeights], eps: float):
+        self.state = state
+        self.layers = layers
+        self.eps = eps
+        self.E, self.N = state.multipliers.shape
+        self.H = state.primes.shape[2]
+        self.C = (self.N - 1) * self.H
+        if len(layers) != self.E:
+            raise ValueError("one LayerWeights per hashed engram layer")
+        self._bufs = {}
+
+    def _buf(self, key, shape, dtype, device):
+        import torch
+
+        b = self._bufs.get(key)
+        if b is None or b.numel() < _numel(shape) or b.dtype != dtype:
+            b = torch.empty(_numel(shape), dtype=dtype, device=device)
+            self._bufs[key] = b
+        return b[: _numel(shape)].view(shape)
+
+    @staticmethod
+    def _timed(events, name, fn):
+        """Run fn(); if `events` is a dict, bracket the launch with timing events on the current stream."""
+        if events is None:
+            return fn()
+        import torch
+
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        r = fn()
+        end.record()
+        events.setdefault(name, []).append((start, end))
+        return r
+
+    def hash(self, input_ids, start_pos: int, token_mask=None, events=None):
+        import torch
+
+        B, L = input_ids.shape
+        out = self._buf("ids", (B, L, self.E, self.C), torch.int64, input_ids.device)
+        s = self.state
+        return self._timed(events, "hash", lambda: engram_hash(
+            input_ids, start_pos, token_mask, s.token_map, s.cache, s.multipliers, s.primes, s.offsets, s.pad_id,
+            s.dead, out=out))
+
+    def layer(self, e: int, hash_ids, x, events=None):
+        """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim].
+
+        The three tensors are this object's buffers for layer e: the next call for the same
+        layer overwrites them."""
+        import torch
+
+        lw = self.layers[e]
+        T = hash_ids.shape[0] * hash_ids.shape[1]
+        D = lw.weight.shape[1]
+        dev = hash_ids.device
+        a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
+        self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
+            hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
+        kv = self._buf(("kv", e), (T, lw.wkv.shape[0]), torch.bfloat16, dev)
+        self._timed(events, "wkv", lambda: engram_wkv(a.view(T, -1), lw.wkv, out=kv))
+        x3 = x.reshape(T, x.shape[-2], x.shape[-1])
+        dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
+        self._timed(events, "gate_dot", lambda: engram_gate_dot(x3, kv, lw.q_weight, lw.k_weight, self.eps, out=dot))
+        return a, kv, dot
+
+    def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None):
+        """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
+        (or one tensor shared by all layers).  Returns the per-layer gate pre-activations.
+        `events`: optional dict that collects (start, end) timing events per entry point."""
+        ids = self.hash(input_ids, start_pos, token_mask, events)
+        dots = []
+        for e in range(self.E):
+            x = xs[e] if isinstance(xs, (list, tuple)) else xs
+            dots.append(self.layer(e, ids, x, events)[2])
+        return dots
+
+
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+__all__ = ["HashState", "LayerWeights", "EngramForward"]

@@ -1,0 +1,162 @@
+/*
+ * engram.h -- C ABI of libengram.so, the Engram forward hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations are those of the DeepSeek V4.1 model pages
+ * (open-model-atlas.klimov-ivan-k.chatgpt.site, "stack-hashes" page; the same
+ * classes appear on atlas.klimoza.dev "engram-first/lookup" and
+ * "engram-first/streams"):
+ *
+ *   engram_hash            -- the engram hash module's forward
+ *   engram_gather_dequant  -- ParallelEngramEmbedding.forward (one rank)
+ *   engram_wkv             -- the `wkv` Linear inside Engram.forward
+ *   engram_gate_dot        -- Engram.forward up to the gate pre-activation `dot`
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer (memory the caller allocated on
+ *   the current HIP device), row-major and contiguous unless a stride is
+ *   given.  The caller owns all memory; the library allocates nothing and
+ *   keeps no pointer after a call returns.
+ * - bf16 values are passed as their 16-bit patterns (uint16_t).
+ * - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *   kernels on it and never synchronise; results are ready when the stream
+ *   reaches them.
+ * - Arguments are validated on the host before anything is enqueued.  A call
+ *   returns ENGRAM_OK, or an error status and enqueues nothing (ENGRAM_EHIP
+ *   is the exception: the launch itself failed).  engram_last_error() gives
+ *   a one-line description of the last failure on the calling thread.
+ * - A size of zero tokens is valid and enqueues nothing.
+ * - Pointers to arrays read or written with 16-byte vector accesses must be
+ *   16-byte aligned; this is stated per argument below.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum engram_status {
+    ENGRAM_OK = 0,
+    ENGRAM_EINVAL = 1, /* a null pointer, a bad size, an unsupported shape or a misaligned pointer */
+    ENGRAM_ERANGE = 2, /* the compressed-id cache is too small for the batch / positions */
+    ENGRAM_EHIP = 3    /* the HIP runtime rejected a launch */
+};
+
+/* Static description of a status code. */
+const char* engram_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* engram_last_error(void);
+
+/* Version of the ABI described here (currently 1). */
+int engram_abi_version(void);
+
+/*
+ * engram_hash -- n-gram hash ids of a chunk of tokens (stack-hashes page: the
+ * hash module's forward).
+ *
+ * For each sequence b < B and position p = start_pos + l (l < L):
+ *   c[p] = token_map[input_ids[b,l]], or `dead` where token_mask[b,l] == 0
+ *          (an id outside [0, vocab) is treated the same way);
+ *   cache[b, p] = c[p];
+ *   slot s = 0..N-1 holds c[p-s], read from this chunk when p-s >= start_pos
+ *          and from the cache when p-s < start_pos; once a slot is blocked
+ *          (p < s, or c[p-s] == dead) it and every longer slot hold pad_id;
+ *   r_n = XOR over s < n of (slot_s * multipliers[e,s]), int64 wrap-around;
+ *   hash_ids[b,l,e,(n-2)*H + h] = floormod(r_n, primes[e,n-2,h]) + offsets[e,(n-2)*H + h]
+ *          for n = 2..N, h < H (floormod takes the divisor's sign).
+ *
+ * input_ids    int64 [B, L]
+ * token_mask   uint8 [B, L], nonzero = the token takes part; NULL = all take part
+ * token_map    int64 [vocab], values in [0, compressed vocab)
+ * cache        int64 [cache_B, cache_L], in/out.  Positions [start_pos, start_pos+L)
+ *              of rows 0..B-1 are written; positions [start_pos-N+1, start_pos)
+ *              are read.  Row b is sequence b across calls.
+ * multipliers  int64 [E, N]
+ * primes       int64 [E, N-1, H], every entry > 0
+ * offsets      int64 [E, (N-1)*H]
+ * dead         the sentinel stored for masked positions; must differ from every
+ *              token_map value
+ * hash_ids     int64 [B, L, E, (N-1)*H], out
+ * Limits: B, L >= 0; start_pos >= 0; 2 <= N <= 8; 1 <= E <= 8; H >= 1;
+ *         (N-1)*H <= 1024.  ERANGE if B > cache_B or start_pos + L > cache_L.
+ * Calls that share a cache row must be ordered on one stream.
+ */
+int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                int64_t* cache, int64_t cache_B, int64_t cache_L,
+                const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                int64_t* hash_ids, void* stream);
+
+/*
+ * engram_gather_dequant -- fetch and dequantise the fp8 rows of one layer's
+ * hash ids (stack-hashes page: ParallelEngramEmbedding.forward, one rank's
+ * rows [row_start, row_start + R)).
+ *
+ * For token t < T and column c < C, id = hash_ids[t * id_token_stride + c]:
+ *   ok   = row_start <= id < row_start + R;  row = ok ? id - row_start : 0
+ *   out_bf16[t,c,j]  = ok ? bf16(fp32(e4m3fn(weight[row,j])) * scale[row, j/blk]) : +0
+ *                      (fp32 product rounded to nearest even, then bf16 rounded
+ *                      to nearest even: two roundings, as the page does)
+ *   out_fp8[t,c,j]   = weight[row,j]        (optional)
+ *   out_scale[t,c,s] = scale[row,s]         (optional)
+ * The bf16 output is the [T, C*D] operand of engram_wkv.
+ *
+ * hash_ids         int64, row stride id_token_stride >= C (e.g. layer e of
+ *                  engram_hash's output: hash_ids + e*C with stride E*C); 8-byte aligned
+ * weight           uint8 [R, D], float8_e4m3fn (OCP E4M3FN) bytes; 16-byte aligned
+ * scale            float32 [R, D/blk]; 4-byte aligned
+ * out_bf16         uint16 [T, C, D] bf16 bits, out; 16-byte aligned
+ * out_fp8          uint8 [T, C, D] or NULL; 16-byte aligned
+ * out_scale        float32 [T, C, D/blk] or NULL
+ * Limits: D in {32, 64, 128, 256}; blk a multiple of 16 that divides D;
+ *         1 <= C <= 1024; R >= 1; T >= 0.
+ */
+int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                          const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
+                          int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                          float* out_scale, void* stream);
+
+/*
+ * engram_wkv -- the projection kv = A * W^T (stack-hashes page: Engram's
+ * `wkv` Linear, n_hash_cols*head_dim -> dim*(hc_mult+1), no bias).
+ *
+ * a    uint16 [T, K] bf16 bits (the flattened gathered rows); 16-byte aligned
+ * w    uint16 [Nout, K] bf16 bits; 16-byte aligned
+ * kv   uint16 [T, Nout] bf16 bits, out: fp32 accumulation, rounded to nearest
+ *      even once.  Columns [0, hc*dim) are the hc keys, [hc*dim, Nout) the value.
+ *      16-byte aligned.
+ * Limits: T >= 0; K >= 8 and K % 8 == 0; Nout >= 1 and Nout % 8 == 0.
+ */
+int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t T, int32_t K, int32_t Nout,
+               void* stream);
+
+/*
+ * engram_gate_dot -- the gate pre-activation per (token, hc copy)
+ * (stack-hashes page: Engram.forward, `rstd` and `dot`).
+ *
+ *   w[c,j]   = fp32(q_weight[c,j]) * fp32(k_weight[c,j])
+ *   dot[t,c] = sum_j h[j] w[c,j] key[j]
+ *              * rsqrt(mean_j h[j]^2 + eps) * rsqrt(mean_j key[j]^2 + eps) * dim^-1/2
+ *   with h = x[t,c,:], key = kv[t, c*dim : (c+1)*dim]; sums in fp32.
+ *
+ * x          uint16 [T, hc, dim] bf16 bits; 16-byte aligned
+ * kv         uint16 bf16 bits, row stride ld_kv >= hc*dim (engram_wkv's output,
+ *            ld_kv = Nout); 16-byte aligned, ld_kv % 8 == 0
+ * q_weight, k_weight  uint16 [hc, dim] bf16 bits; 16-byte aligned
+ * dot        float32 [T, hc], out
+ * Limits: T >= 0; 1 <= hc <= 64; dim >= 8 and dim % 8 == 0.
+ */
+int engram_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
+                    const uint16_t* k_weight, float eps, float* dot, int64_t T, int32_t hc, int32_t dim,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENGRAM_H */

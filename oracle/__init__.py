@@ -49,6 +49,7 @@ def lib():
         L.oracle_e4m3fn_decode.restype = ctypes.c_float
         L.oracle_bf16_rne.argtypes = [ctypes.c_float]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_num_threads.restype = ctypes.c_int
         for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot):
             f.restype = ctypes.c_int
         _lib = L
@@ -151,3 +152,8 @@ def bf16_rne(values) -> np.ndarray:
 
 def bf16_bits_to_float(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())

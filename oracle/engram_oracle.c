@@ -29,6 +29,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #include "engram_oracle.h"
 
@@ -219,4 +222,13 @@ int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const 
         }
     }
     return ORACLE_OK;
+}
+
+/* Threads the parallel loops above use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -44,6 +44,7 @@ int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const 
 float oracle_e4m3fn_decode(uint8_t byte);
 uint16_t oracle_bf16_rne(float f);
 double oracle_bf16_to_double(uint16_t h);
+int oracle_num_threads(void);
 
 #ifdef __cplusplus
 }

@@ -412,6 +412,23 @@ def rows_used(primes: np.ndarray) -> list:
     return [int(x) for x in primes.reshape(primes.shape[0], -1).sum(axis=1)]
 
 
+def compact_table(ids: np.ndarray, n_rows: int, seed: int, head_dim: int, block_size: int):
+    """The rows that `ids` reach in an `n_rows`-row seeded table, as a compact host table.
+
+    Returns (weight [U, D], scale [U, D/blk], remapped ids): in-range ids are
+    replaced by their index among the sorted distinct rows, out-of-range ids by
+    -1 (still out of range for the compact table).  Lets a host consumer see
+    exactly the rows of a table that only exists on the GPU.
+    """
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    ok = (flat >= 0) & (flat < n_rows)
+    uniq = np.unique(flat[ok])
+    w, s = table_rows(seed, uniq, head_dim, block_size)
+    remap = np.full(flat.shape, -1, dtype=np.int64)
+    remap[ok] = np.searchsorted(uniq, flat[ok])
+    return w, s, remap.reshape(np.shape(ids))
+
+
 def table_rows_alloc(cfg: EngramConfig) -> list:
     return list(cfg.rows_alloc[: cfg.n_layers])
 

@@ -1,0 +1,116 @@
+"""The C ABI: libengram.so loads without a GPU, exports every entry point that
+include/engram.h declares, and validates arguments on the host (statuses come
+back before anything is enqueued, so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gram_hash_embedding_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "engram.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) >= {"engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot",
+                          "engram_status_string", "engram_last_error", "engram_abi_version"}
+    L = g.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = g.lib()
+    assert L.engram_abi_version() == 1
+    for s in range(4):
+        assert L.engram_status_string(s)
+    assert L.engram_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def _err():
+    return g.lib().engram_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    (dict(B=-1), 1, "negative"),
+    (dict(N=1), 1, "N=1"),
+    (dict(N=9), 1, "N=9"),
+    (dict(E=0), 1, "E=0"),
+    (dict(E=9), 1, "E=9"),
+    (dict(H=0), 1, "H=0"),
+    (dict(H=400), 1, "columns"),
+    (dict(cache_B=1), 2, "cache"),
+    (dict(cache_L=63), 2, "cache"),
+    (dict(start_pos=1), 2, "cache"),
+    (dict(input_ids=None), 1, "null"),
+    (dict(out=None), 1, "null"),
+    (dict(input_ids=ctypes.c_void_p(0x100004)), 1, "aligned"),
+])
+def test_hash_validation(args, status, msg):
+    a = dict(input_ids=FAKE, B=2, L=64, start_pos=0, mask=None, token_map=FAKE, vocab=10, cache=FAKE, cache_B=2,
+             cache_L=64, mult=FAKE, primes=FAKE, offsets=FAKE, E=1, N=4, H=2, pad=2, dead=-1, out=FAKE)
+    a.update(args)
+    rc = g.lib().engram_hash(a["input_ids"], a["B"], a["L"], a["start_pos"], a["mask"], a["token_map"], a["vocab"],
+                             a["cache"], a["cache_B"], a["cache_L"], a["mult"], a["primes"], a["offsets"], a["E"],
+                             a["N"], a["H"], a["pad"], a["dead"], a["out"], None)
+    assert rc == status
+    assert msg in _err()
+
+
+def test_zero_tokens_is_a_valid_no_op():
+    L = g.lib()
+    assert L.engram_hash(None, 0, 5, 0, None, None, 10, None, 0, 5, None, None, None, 1, 4, 2, 2, -1, None, None) == 0
+    assert L.engram_gather_dequant(None, 0, 24, 24, None, None, 10, 0, 64, 32, None, None, None, None) == 0
+    assert L.engram_wkv(None, None, None, 0, 64, 64, None) == 0
+    assert L.engram_gate_dot(None, None, 64, None, None, 1e-20, None, 0, 4, 16, None) == 0
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(D=48), "D=48"),
+    (dict(blk=8), "blk=8"),
+    (dict(blk=48), "blk=48"),
+    (dict(C=0), "C=0"),
+    (dict(stride=3), "stride"),
+    (dict(R=0), "R < 1"),
+    (dict(weight=None), "null"),
+    (dict(weight=ctypes.c_void_p(0x100008)), "misaligned"),
+])
+def test_gather_validation(kw, msg):
+    a = dict(ids=FAKE, T=10, stride=24, C=24, weight=FAKE, scale=FAKE, R=100, row_start=0, D=64, blk=32, out=FAKE)
+    a.update(kw)
+    rc = g.lib().engram_gather_dequant(a["ids"], a["T"], a["stride"], a["C"], a["weight"], a["scale"], a["R"],
+                                       a["row_start"], a["D"], a["blk"], a["out"], None, None, None)
+    assert rc == 1
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("K,N,msg", [(0, 64, "K=0"), (12, 64, "K=12"), (64, 4, "Nout=4"), (64, 36, "Nout=36")])
+def test_wkv_validation(K, N, msg):
+    assert g.lib().engram_wkv(FAKE, FAKE, FAKE, 10, K, N, None) == 1
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("ld,hc,dim,msg", [(64, 0, 16, "hc=0"), (64, 65, 16, "hc=65"), (64, 4, 12, "dim=12"),
+                                           (60, 4, 16, "ld_kv"), (68, 4, 16, "ld_kv")])
+def test_gate_validation(ld, hc, dim, msg):
+    assert g.lib().engram_gate_dot(FAKE, FAKE, ld, FAKE, FAKE, 1e-20, FAKE, 10, hc, dim, None) == 1
+    assert msg in _err()
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(g, "_lib", None)
+    with pytest.raises(ImportError):
+        g.lib()
