@@ -5,21 +5,33 @@
 // keys followed by the shared value), fp32 accumulation, one bf16 rounding.
 //
 // Design (gfx950, dense contraction -> MFMA):
-// - Both operands are K-contiguous (A [T,K], W [Nout,K]), so one loader
-//   serves both: 16-byte global loads, 8 lanes per 128-byte row segment.
-// - Workgroup tile 256 x 256 x 64, four waves in a 2 x 2 grid, each wave a
-//   128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 blocks held in 256 fp32
-//   accumulators (AGPRs).
-// - LDS double buffer (2 x 72 KB of the CU's 160 KB); rows padded to 144 bytes
-//   so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
-//   The next K slab is fetched from HBM into registers while the current one
-//   is multiplied, then written to the other buffer: one barrier per slab.
-// - Epilogue: accumulators -> bf16 -> LDS (reusing the buffers) -> 16-byte
-//   row-contiguous global stores.
-// - Tile order: workgroups are dispatched round-robin over the 8 XCDs; the
-//   block index is remapped so each XCD walks a contiguous run of tiles, and
-//   runs are grouped 8 M-tiles deep so concurrently resident tiles share A and
-//   W panels in that XCD's L2.
+// - Workgroup tile 256 x 256, four waves in a 2 x 2 grid, each wave a
+//   128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 blocks in 256 fp32 accumulators
+//   (AGPRs); one wave per SIMD, one workgroup per CU.  A 128 x 128 wave tile
+//   is what keeps LDS fragment traffic (64 B/clk/CU at full MFMA rate) inside
+//   the LDS bandwidth.
+// - Main kernel (K a multiple of 64): persistent, one workgroup per CU walks
+//   its tiles; A and W slabs of 64 along K go HBM/L2 -> LDS with the gfx950
+//   direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging, no
+//   ds_write instructions), two 64 KB stages.  Rows are 128 B with the 16-byte
+//   pieces XOR-swizzled by (row/2) mod 8, so the fragment reads of 16
+//   consecutive rows hit 16 distinct bank groups.
+// - One barrier per slab, placed before the last of its four k-steps: it
+//   publishes the next slab (already landed) and frees the current stage for
+//   the slab after next, whose loads are issued right away; the first
+//   fragments of the next slab are then read while the last 16 MFMAs of this
+//   one run.  The load stream runs across tile boundaries, so the next tile's
+//   first slabs arrive during the current tile's last ones and its epilogue.
+// - Fragment reads of k-step s+1 are interleaved with the 16 MFMAs of step s.
+// - The MFMA is issued as W-fragment x A-fragment, so each lane ends up with
+//   4 consecutive output columns of one token.  The persistent kernel's
+//   epilogue turns them into full 128-byte-line, non-temporal 16-byte stores
+//   through a per-wave 8 KB LDS region (the remaining 32 KB of the CU's LDS);
+//   scattered 8-byte stores measured 15% slower here.
+// - Tile order: workgroups are dispatched round-robin over the 8 XCDs; tiles
+//   are renumbered so each XCD walks a contiguous run, grouped 8 M-tiles deep,
+//   so the 32 tiles resident on an XCD share A and W panels in its L2.
+// - K not a multiple of 64: a register-staged variant with a zero-filled K tail.
 #include "common.h"
 
 namespace engram {
@@ -28,14 +40,22 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int LDA = BK + 8;               // padded LDS row (elements): 144 bytes
-constexpr int kTileElems = BM * LDA;      // one operand tile in LDS
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
-constexpr int EPI_LD = 128 + 8;           // epilogue LDS row (elements) of a wave's 128x128 tile
+constexpr int kCUs = 256;
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitLgkmcnt0 = 0xC07F;  // lgkmcnt == 0 only (vmcnt 63, expcnt 7 left at their maxima)
 
 struct WkvArgs {
     const uint16_t* a;
@@ -46,14 +66,12 @@ struct WkvArgs {
     int tiles_m, tiles_n;
 };
 
-__device__ inline void tile_coords(const WkvArgs& p, int& tm, int& tn) {
+// pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
+__device__ inline void tile_coords(const WkvArgs& p, int pid, int& tm, int& tn) {
     const int n = p.tiles_m * p.tiles_n;
-    const int pid = blockIdx.x;
-    // contiguous run of tiles per XCD
     const int xcd = pid % kXcds, idx = pid / kXcds;
     const int per = n / kXcds, rem = n % kXcds;
     const int logical = xcd * per + min(xcd, rem) + idx;
-    // grouped ordering: kGroupM M-tiles share each sweep over N
     const int in_group = kGroupM * p.tiles_n;
     const int group = logical / in_group;
     const int first_m = group * kGroupM;
@@ -63,11 +81,237 @@ __device__ inline void tile_coords(const WkvArgs& p, int& tm, int& tn) {
     tn = r / gsize;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void wkv_kernel(WkvArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTileElems];  // [buf][A|B][BM][LDA]
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc[i][j] = W-block j (32 outputs) x A-block i (32 tokens): element r of a lane is output
+// 32j + 8(r/4) + 4(lane/32) + r%4 of token 32i + lane%32.
+__device__ inline void mfma_step(f32x16 (&acc)[4][4], const bf16x8* fa, const bf16x8* fw) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// the 8 fragment reads of the next k-step spread among the 16 MFMAs of this one
+__device__ inline void interleave_reads() {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+}
+
+__device__ inline void zero(f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// 4 consecutive outputs per lane and block row -> one 8-byte bf16 store
+__device__ inline void store_tile(const WkvArgs& p, const f32x16 (&acc)[4][4], int64_t m0, int n0, int wm, int wn,
+                                  int lane) {
+    const int64_t tok0 = m0 + wm * 128 + (lane & 31);
+    const int col0 = n0 + wn * 128 + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = tok0 + 32 * i;
+        if (m >= p.M) continue;
+        uint16_t* row = p.kv + m * p.N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = col0 + 32 * j + 8 * g;
+                if (n < p.N) {
+                    const u32x2 v = {pack_bf16(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
+                                     pack_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                    *reinterpret_cast<u32x2*>(row + n) = v;
+                }
+            }
+    }
+}
+
+// Epilogue through an 8 KB LDS region per wave: 4 rounds of 32 tokens x 128 outputs (16-byte pieces
+// XOR-swizzled by row so both the 8-byte writes and the 16-byte reads are bank-conflict free), then
+// 16 lanes per 256-byte output row: every store instruction writes whole 128-byte lines, streamed
+// past the caches (non-temporal) since kv is not read again by this kernel.
+__device__ inline void store_tile_staged(const WkvArgs& p, const f32x16 (&acc)[4][4], int64_t m0, int n0, int wm,
+                                         int wn, int lane, uint8_t* ep) {
+    const int64_t tok_base = m0 + wm * 128;
+    const int col_base = n0 + wn * 128;
+    const int r = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * j + 8 * g + 4 * (lane >> 5);  // output inside the wave's 128
+                const u32x2 v = {pack_bf16(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
+                                 pack_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                *reinterpret_cast<u32x2*>(ep + r * 256 + (((col >> 3) ^ (r & 15)) << 4) + ((col >> 2) & 1) * 8) = v;
+            }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // this wave's writes are in LDS before it reads them back
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int rr = q * 4 + (lane >> 4);
+            const int chunk = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rr * 256 + ((chunk ^ (rr & 15)) << 4));
+            const int64_t m = tok_base + 32 * i + rr;
+            const int n = col_base + chunk * 8;
+            if (m < p.M && n < p.N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.kv + m * p.N + n));
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // reads done before the next round overwrites the region
+    }
+}
+
+// ============================================================================
+// main kernel: persistent, direct-to-LDS loads (K % 64 == 0)
+// ============================================================================
+constexpr int kOpBytes = BM * BK * 2;          // one operand slab: 256 rows x 128 B = 32 KB
+constexpr int kStageBytes = 2 * kOpBytes;      // A slab + W slab
+constexpr int kEpiBytes = 8192;                // per-wave epilogue staging region
+
+// byte offset of 16-byte piece c of row r inside an operand slab
+__device__ inline int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+struct SlabCursor {
+    int pid;      // tile being loaded
+    int kt;       // slab inside that tile
+};
+
+__global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
+    // [stage][A|W][256 rows][128 B], then 4 x 8 KB epilogue regions: 160 KB, the whole LDS of a CU
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + 4 * kEpiBytes];
+
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int G = gridDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int KT = p.K / BK;
+
+    // ---- loader: wave w fills rows [64w, 64w+64) of both operand slabs, 8 rows per instruction;
+    // lane l lands at slot (l & 7) of row 64w + 8q + (l >> 3) and fetches the piece the swizzle puts there
+    const int ld_r = lane >> 3, ld_slot = lane & 7;
+    auto issue_slab = [&](const SlabCursor& c, int stage) {
+        int tm, tn;
+        tile_coords(p, c.pid, tm, tn);
+        const int64_t m0 = static_cast<int64_t>(tm) * BM;
+        const int n0 = tn * BN;
+        const int k0 = c.kt * BK;
+        uint8_t* sa = lds + stage * kStageBytes + wave * 64 * 128;
+        uint8_t* sw = sa + kOpBytes;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int row = wave * 64 + q * 8 + ld_r;
+            const int piece = ld_slot ^ ((row >> 1) & 7);
+            int64_t m = m0 + row;
+            if (m >= p.M) m = p.M - 1;  // ragged M: duplicate the last row, never stored
+            int n = n0 + row;
+            if (n >= p.N) n = p.N - 1;
+            __builtin_amdgcn_global_load_lds(p.a + m * p.K + k0 + piece * 8, sa + q * 8 * 128, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(p.w + static_cast<int64_t>(n) * p.K + k0 + piece * 8, sw + q * 8 * 128,
+                                             16, 0, 0);
+        }
+    };
+    auto advance = [&](SlabCursor& c) {
+        if (++c.kt == KT) {
+            c.kt = 0;
+            c.pid += G;
+        }
+    };
+
+    // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
+    const int g = (lane >> 1) & 7;  // swizzle key of the lane's rows (every block starts at a multiple of 16)
+    const int a_row = (wm * 128 + (lane & 31)) * 128;
+    const int w_row = kOpBytes + (wn * 128 + (lane & 31)) * 128;
+    auto read_frags = [&](int stage, int kk, bf16x8* fa, bf16x8* fw) {
+        const uint8_t* base = lds + stage * kStageBytes;
+        const int off = (((2 * kk + (lane >> 5)) ^ g) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * 128 + off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + w_row + j * 32 * 128 + off);
+    };
+
+    int pid = blockIdx.x;
+    if (pid >= tiles) return;
+    SlabCursor ld{pid, 0};
+    const int total_slabs_mine = ((tiles - 1 - pid) / G + 1) * KT;
+    int issued = 0;
+    // prologue: two slabs in flight, wait for the first
+    issue_slab(ld, 0);
+    advance(ld);
+    ++issued;
+    if (issued < total_slabs_mine) {
+        issue_slab(ld, 1);
+        advance(ld);
+        ++issued;
+    }
+    if (issued == 2)
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));  // this wave's 16 loads of the first slab have landed
+    else
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+
+    f32x16 acc[4][4];
+    bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
+    read_frags(0, 0, fa0, fw0);
+    int stage = 0;
+    for (; pid < tiles; pid += G) {
+        int tm, tn;
+        tile_coords(p, pid, tm, tn);
+        zero(acc);
+        for (int kt = 0; kt < KT; ++kt) {
+            read_frags(stage, 1, fa1, fw1);
+            mfma_step(acc, fa0, fw0);
+            interleave_reads();
+            read_frags(stage, 2, fa0, fw0);
+            mfma_step(acc, fa1, fw1);
+            interleave_reads();
+            read_frags(stage, 3, fa1, fw1);
+            mfma_step(acc, fa0, fw0);
+            interleave_reads();
+            // own loads of the next slab have landed (the barrier's fence covers LDS reads only), then the
+            // barrier publishes that slab and frees this stage
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            __syncthreads();
+            if (issued < total_slabs_mine) {
+                issue_slab(ld, stage);  // slab after next into the stage just freed
+                advance(ld);
+                ++issued;
+            }
+            const bool more = kt + 1 < KT || pid + G < tiles;
+            if (more) read_frags(stage ^ 1, 0, fa0, fw0);
+            mfma_step(acc, fa1, fw1);
+            if (more) interleave_reads();
+            stage ^= 1;
+        }
+        store_tile_staged(p, acc, static_cast<int64_t>(tm) * BM, tn * BN, wm, wn, lane,
+                          lds + 2 * kStageBytes + wave * kEpiBytes);
+    }
+}
+
+// ============================================================================
+// register-staged kernel for any K % 8 == 0 (zero-filled K tail)
+// ============================================================================
+constexpr int LDA = BK + 8;               // padded LDS row (elements): 144 bytes
+constexpr int kTileElems = BM * LDA;      // one operand tile in LDS
+
+__global__ __launch_bounds__(kThreads, 1) void wkv_kernel_staged(WkvArgs p) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTileElems];  // [buf][A|W][256][LDA]
 
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, blockIdx.x, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * BM;
     const int n0 = tn * BN;
     const int tid = threadIdx.x;
@@ -75,7 +319,6 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel(WkvArgs p) {
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- global -> register loader: 8 x 16 B of A and of W per lane ----
     const int ld_row = tid >> 3;        // + 32 * i
     const int ld_col = (tid & 7) * 8;   // element offset inside the K slab
     const uint16_t* a_src[8];
@@ -83,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         int64_t m = m0 + ld_row + 32 * i;
-        if (m >= p.M) m = p.M - 1;  // ragged M: duplicate the last row, never stored
+        if (m >= p.M) m = p.M - 1;
         int n = n0 + ld_row + 32 * i;
         if (n >= p.N) n = p.N - 1;
         a_src[i] = p.a + m * p.K + ld_col;
@@ -107,69 +350,44 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel(WkvArgs p) {
             *reinterpret_cast<u32x4*>(lb + (ld_row + 32 * i) * LDA + ld_col) = rw[i];
         }
     };
+    const int frag_off_a = (wm * 128 + (lane & 31)) * LDA + (lane >> 5) * 8;
+    const int frag_off_w = kTileElems + (wn * 128 + (lane & 31)) * LDA + (lane >> 5) * 8;
+    auto read_frags = [&](int buf, int kk, bf16x8* fa, bf16x8* fw) {
+        const uint16_t* base = lds + buf * 2 * kTileElems + kk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + frag_off_a + i * 32 * LDA);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + frag_off_w + j * 32 * LDA);
+    };
 
     f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // fragment addressing: lane holds row (lane % 32), k pieces 8*(lane/32) .. +8
-    const int frag_row = lane & 31;
-    const int frag_k = (lane >> 5) * 8;
-
+    zero(acc);
+    bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
     const int KT = (p.K + BK - 1) / BK;
     load_slab(0);
     store_slab(0);
     __syncthreads();
+    read_frags(0, 0, fa0, fw0);
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) load_slab((kt + 1) * BK);
-        const uint16_t* la = lds + cur * 2 * kTileElems + (wm * 128 + frag_row) * LDA + frag_k;
-        const uint16_t* lb = lds + cur * 2 * kTileElems + kTileElems + (wn * 128 + frag_row) * LDA + frag_k;
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(la + i * 32 * LDA + kk);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(lb + j * 32 * LDA + kk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) store_slab(cur ^ 1);
+        const bool more = kt + 1 < KT;
+        if (more) load_slab((kt + 1) * BK);
+        read_frags(cur, 16, fa1, fw1);
+        mfma_step(acc, fa0, fw0);
+        interleave_reads();
+        read_frags(cur, 32, fa0, fw0);
+        mfma_step(acc, fa1, fw1);
+        interleave_reads();
+        read_frags(cur, 48, fa1, fw1);
+        mfma_step(acc, fa0, fw0);
+        interleave_reads();
+        if (more) store_slab(cur ^ 1);
         __syncthreads();
+        if (more) read_frags(cur ^ 1, 0, fa0, fw0);
+        mfma_step(acc, fa1, fw1);
+        if (more) interleave_reads();
     }
-
-    // ---- epilogue: bf16 through LDS, then row-contiguous 16-byte stores ----
-    uint16_t* ep = lds + wave * 128 * EPI_LD;
-    // accumulator element r of block (i, j): row 32i + 8(r/4) + 4(lane/32) + r%4, column 32j + lane%32
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = 32 * j + (lane & 31);
-                ep[row * EPI_LD + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][r]));
-            }
-    __syncthreads();
-    const int64_t row0 = m0 + wm * 128;
-    const int col0 = n0 + wn * 128;
-#pragma unroll 4
-    for (int q = lane; q < 128 * 16; q += 64) {
-        const int row = q >> 4, c16 = (q & 15) * 8;
-        const int64_t m = row0 + row;
-        const int n = col0 + c16;
-        if (m < p.M && n < p.N)
-            *reinterpret_cast<u32x4*>(p.kv + m * p.N + n) = *reinterpret_cast<const u32x4*>(ep + row * EPI_LD + c16);
-    }
+    store_tile(p, acc, m0, n0, wm, wn, lane);
 }
 
 }  // namespace
@@ -196,7 +414,13 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     p.tiles_n = (Nout + BN - 1) / BN;
     if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv: too many tiles");
     p.tiles_m = static_cast<int>(tiles_m);
-    hipLaunchKernelGGL(wkv_kernel, dim3(static_cast<unsigned>(tiles_m * p.tiles_n)), dim3(kThreads), 0,
-                       as_stream(stream), p);
+    const int64_t tiles = tiles_m * p.tiles_n;
+    if (K % BK == 0) {
+        const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
+        hipLaunchKernelGGL(wkv_kernel_dma, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    } else {
+        hipLaunchKernelGGL(wkv_kernel_staged, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
+                           as_stream(stream), p);
+    }
     return check_launch("engram_wkv");
 }

@@ -18,7 +18,7 @@ def _rand_bf16(rng, shape, std=1.0):
     return torch.from_numpy((rng.normal(size=shape) * std).astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,K,N", [(64, 192, 1280), (1, 8, 8), (300, 200, 264), (257, 1536, 520), (513, 64, 256),
+@pytest.mark.parametrize("T,K,N", [(64, 192, 1280), (1, 8, 8), (300, 200, 264), (257, 1536, 520), (513, 64, 256), (2600, 1536, 6400),
                                    (1000, 1536, 25600)])
 def test_wkv_ragged_shapes(gpu_device, T, K, N):
     import gram_hash_embedding_amd as g
