@@ -56,6 +56,8 @@ constexpr int kSchedDsRead = 0x100;
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkmcnt0 = 0xC07F;  // lgkmcnt == 0 only (vmcnt 63, expcnt 7 left at their maxima)
+// word 3 of a raw buffer resource on gfx9-family targets (32-bit data format, no swizzle)
+constexpr int kBufferWord3 = 0x00020000;
 
 struct WkvArgs {
     const uint16_t* a;
@@ -80,6 +82,18 @@ __device__ inline void tile_coords(const WkvArgs& p, int pid, int& tm, int& tn) 
     tm = first_m + r % gsize;
     tn = r / gsize;
 }
+
+// One accumulator element read out of its AGPR at this point of the program: a volatile asm keeps the
+// read inside its epilogue round (the compiler would otherwise copy all 256 accumulators to VGPRs ahead
+// of the first epilogue barrier and spill).
+__device__ inline float acc_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+// lane id recomputed from the exec mask (two VALU ops) rather than kept live in a VGPR
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -138,89 +152,83 @@ __device__ inline void store_tile(const WkvArgs& p, const f32x16 (&acc)[4][4], i
     }
 }
 
-// Epilogue through an 8 KB LDS region per wave: 4 rounds of 32 tokens x 128 outputs (16-byte pieces
-// XOR-swizzled by row so both the 8-byte writes and the 16-byte reads are bank-conflict free), then
-// 16 lanes per 256-byte output row: every store instruction writes whole 128-byte lines, streamed
-// past the caches (non-temporal) since kv is not read again by this kernel.
-__device__ inline void store_tile_staged(const WkvArgs& p, const f32x16 (&acc)[4][4], int64_t m0, int n0, int wm,
-                                         int wn, int lane, uint8_t* ep) {
-    const int64_t tok_base = m0 + wm * 128;
-    const int col_base = n0 + wn * 128;
-    const int r = lane & 31;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = 32 * j + 8 * g + 4 * (lane >> 5);  // output inside the wave's 128
-                const u32x2 v = {pack_bf16(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
-                                 pack_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-                *reinterpret_cast<u32x2*>(ep + r * 256 + (((col >> 3) ^ (r & 15)) << 4) + ((col >> 2) & 1) * 8) = v;
-            }
-        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // this wave's writes are in LDS before it reads them back
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int rr = q * 4 + (lane >> 4);
-            const int chunk = lane & 15;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rr * 256 + ((chunk ^ (rr & 15)) << 4));
-            const int64_t m = tok_base + 32 * i + rr;
-            const int n = col_base + chunk * 8;
-            if (m < p.M && n < p.N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.kv + m * p.N + n));
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // reads done before the next round overwrites the region
-    }
-}
-
 // ============================================================================
 // main kernel: persistent, direct-to-LDS loads (K % 64 == 0)
 // ============================================================================
 constexpr int kOpBytes = BM * BK * 2;          // one operand slab: 256 rows x 128 B = 32 KB
 constexpr int kStageBytes = 2 * kOpBytes;      // A slab + W slab
-constexpr int kEpiBytes = 8192;                // per-wave epilogue staging region
-
-// byte offset of 16-byte piece c of row r inside an operand slab
-__device__ inline int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+constexpr int kExBytes = 64 * 512;             // epilogue exchange: 64 token rows x 256 outputs (bf16)
 
 struct SlabCursor {
-    int pid;      // tile being loaded
-    int kt;       // slab inside that tile
+    int pid;  // tile being loaded
+    int kt;   // slab inside that tile
 };
 
+// The four waves split the memory traffic: waves 0 and 1 issue every global -> LDS load, waves 2 and 3
+// every global store.  A wave's vmcnt counts its loads and stores together, and the slab barrier must
+// wait for the loads; with the roles split, the loaders never have stores outstanding and the storers
+// never wait on vmcnt, so a tile's output drains while the next tile computes.
 __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
-    // [stage][A|W][256 rows][128 B], then 4 x 8 KB epilogue regions: 160 KB, the whole LDS of a CU
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + 4 * kEpiBytes];
+    // [stage][A|W][256 rows][128 B] + exchange region: 160 KB, the whole LDS of a CU
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
 
     const int tiles = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
     const int wm = wave >> 1, wn = wave & 1;
+    const bool loader = wave < 2;
     const int KT = p.K / BK;
 
-    // ---- loader: wave w fills rows [64w, 64w+64) of both operand slabs, 8 rows per instruction;
-    // lane l lands at slot (l & 7) of row 64w + 8q + (l >> 3) and fetches the piece the swizzle puts there
+    // A barrier that publishes LDS: the loaders' own slab loads have landed (vmcnt), every wave's LDS
+    // accesses are done (lgkmcnt).  The empty asm statements keep the compiler from moving memory
+    // accesses across the barrier; no wave waits for its global stores here.
+    auto sync = [&](bool wait_loads) {
+        if (wait_loads && loader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // epilogue barrier: also a scheduling fence, so each round's accumulator conversions stay in
+    // that round instead of being clustered (and spilled) ahead of the first barrier
+    auto sync_epi = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        sync(false);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- loader waves: wave w fills rows [128w, 128w+128) of both operand slabs, 8 rows per
+    // instruction; lane l lands at slot (l & 7) of row 128w + 8q + (l >> 3) and fetches the 16-byte
+    // piece the swizzle puts there.  Buffer loads: the tile's rows are a buffer resource (SGPRs) whose
+    // size stops at the last valid row, so rows past M or N read as zero instead of faulting, and a lane
+    // needs only two 32-bit offsets (the swizzle key of row 128w + 8q + r is ((r >> 1) | 4(q & 1))).
     const int ld_r = lane >> 3, ld_slot = lane & 7;
+    const int row_bytes = p.K * 2;
+    const uint32_t vo_even = static_cast<uint32_t>((wave * 128 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
+    const uint32_t vo_odd = vo_even ^ (4u << 4);
     auto issue_slab = [&](const SlabCursor& c, int stage) {
+        if (!loader) return;
         int tm, tn;
         tile_coords(p, c.pid, tm, tn);
         const int64_t m0 = static_cast<int64_t>(tm) * BM;
         const int n0 = tn * BN;
-        const int k0 = c.kt * BK;
-        uint8_t* sa = lds + stage * kStageBytes + wave * 64 * 128;
+        const int rows_a = static_cast<int>(min<int64_t>(BM, p.M - m0));
+        const int rows_w = min(BN, p.N - n0);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
+        const uint32_t k0b = static_cast<uint32_t>(c.kt * BK * 2);
+        uint8_t* sa = lds + stage * kStageBytes + wave * 128 * 128;
         uint8_t* sw = sa + kOpBytes;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int row = wave * 64 + q * 8 + ld_r;
-            const int piece = ld_slot ^ ((row >> 1) & 7);
-            int64_t m = m0 + row;
-            if (m >= p.M) m = p.M - 1;  // ragged M: duplicate the last row, never stored
-            int n = n0 + row;
-            if (n >= p.N) n = p.N - 1;
-            __builtin_amdgcn_global_load_lds(p.a + m * p.K + k0 + piece * 8, sa + q * 8 * 128, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(p.w + static_cast<int64_t>(n) * p.K + k0 + piece * 8, sw + q * 8 * 128,
-                                             16, 0, 0);
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t vo = (q & 1) ? vo_odd : vo_even;
+            const uint32_t so = k0b + static_cast<uint32_t>(q * 8 * row_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + q * 8 * 128, 16, vo, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, vo, so, 0, 0);
         }
     };
     auto advance = [&](SlabCursor& c) {
@@ -243,12 +251,55 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + w_row + j * 32 * 128 + off);
     };
 
+    // ---- epilogue: 4 rounds of 32 tokens per wave through the exchange region (64 rows of 512 B,
+    // 16-byte pieces XOR-swizzled by row: conflict-free 8-byte writes and 16-byte reads), then the
+    // storer waves write whole 128-byte lines, non-temporal (kv is not read again here)
+    uint8_t* ex = lds + 2 * kStageBytes;
+    auto epilogue = [&](const f32x16 (&acc)[4][4], int64_t m0, int n0) {
+        // Every lane-derived address below is rebuilt from a freshly computed lane id, so the compiler
+        // cannot hoist the ~80 epilogue addresses out of the tile loop (where they would pin VGPRs for
+        // the whole kernel and spill; a scratch reload would also make a storer wave wait for its
+        // outstanding stores).
+        const int l = lane_id();
+        const int key = (wm * 32 + (l & 31)) & 31;
+        const uint32_t wbase = static_cast<uint32_t>((wm * 32 + (l & 31)) * 512 + (l >> 5) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int chunk = wn * 16 + 4 * j + gq;  // 16-byte piece of the 512-byte row
+                    const u32x2 v = {pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1])),
+                                     pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]))};
+                    *reinterpret_cast<u32x2*>(ex + wbase + ((chunk ^ key) << 4)) = v;
+                }
+            sync_epi();
+            if (!loader) {
+                const int half = wave - 2;  // token half wm = half of the tile
+                const int ls = lane_id();
+                const int chunk = ls & 31, hi = ls >> 5;
+                uint16_t* dst = p.kv + (m0 + half * 128 + 32 * i + hi) * p.N + n0 + chunk * 8;
+                const bool col_ok = n0 + chunk * 8 < p.N;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rr = half * 32 + 2 * q + hi;  // exchange row
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 512 + ((chunk ^ (rr & 31)) << 4));
+                    const int64_t m = m0 + half * 128 + 32 * i + 2 * q + hi;
+                    if (m < p.M && col_ok)
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(2 * q) * p.N));
+                }
+            }
+            sync_epi();
+        }
+    };
+
     int pid = blockIdx.x;
     if (pid >= tiles) return;
     SlabCursor ld{pid, 0};
     const int total_slabs_mine = ((tiles - 1 - pid) / G + 1) * KT;
     int issued = 0;
-    // prologue: two slabs in flight, wait for the first
+    // prologue: two slabs in flight, then wait for all of them (once per kernel)
     issue_slab(ld, 0);
     advance(ld);
     ++issued;
@@ -257,11 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         advance(ld);
         ++issued;
     }
-    if (issued == 2)
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));  // this wave's 16 loads of the first slab have landed
-    else
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    __syncthreads();
+    sync(true);
 
     f32x16 acc[4][4];
     bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
@@ -281,23 +328,22 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
             read_frags(stage, 3, fa1, fw1);
             mfma_step(acc, fa0, fw0);
             interleave_reads();
-            // own loads of the next slab have landed (the barrier's fence covers LDS reads only), then the
-            // barrier publishes that slab and frees this stage
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-            __syncthreads();
+            // the next slab has landed and this stage is no longer read: publish the one, refill the other
+            sync(true);
             if (issued < total_slabs_mine) {
                 issue_slab(ld, stage);  // slab after next into the stage just freed
                 advance(ld);
                 ++issued;
             }
-            const bool more = kt + 1 < KT || pid + G < tiles;
+            // (the next tile's first fragments are read after the epilogue, which needs the registers)
+            const bool more = kt + 1 < KT;
             if (more) read_frags(stage ^ 1, 0, fa0, fw0);
             mfma_step(acc, fa1, fw1);
             if (more) interleave_reads();
             stage ^= 1;
         }
-        store_tile_staged(p, acc, static_cast<int64_t>(tm) * BM, tn * BN, wm, wn, lane,
-                          lds + 2 * kStageBytes + wave * kEpiBytes);
+        epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
+        if (pid + G < tiles) read_frags(stage, 0, fa0, fw0);
     }
 }
 
