@@ -32,6 +32,8 @@
 //   are renumbered so each XCD walks a contiguous run, grouped 8 M-tiles deep,
 //   so the 32 tiles resident on an XCD share A and W panels in its L2.
 // - K not a multiple of 64: a register-staged variant with a zero-filled K tail.
+#include <type_traits>
+
 #include "common.h"
 
 namespace engram {
@@ -51,6 +53,7 @@ constexpr int kCUs = 256;
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedVmem = 0x010;
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -208,14 +211,16 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     const int row_bytes = p.K * 2;
     const uint32_t vo_even = static_cast<uint32_t>((wave * 128 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
     const uint32_t vo_odd = vo_even ^ (4u << 4);
-    auto issue_slab = [&](const SlabCursor& c, int stage) {
-        if (!loader) return;
+    // `live` false (past this workgroup's last slab) still issues the instructions, against an empty
+    // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
+    // block as the MFMAs they are interleaved with.  An empty resource zero-fills a free stage.
+    auto issue_slab = [&](const SlabCursor& c, int stage, bool live) {
         int tm, tn;
-        tile_coords(p, c.pid, tm, tn);
+        tile_coords(p, live ? c.pid : static_cast<int>(blockIdx.x), tm, tn);
         const int64_t m0 = static_cast<int64_t>(tm) * BM;
         const int n0 = tn * BN;
-        const int rows_a = static_cast<int>(min<int64_t>(BM, p.M - m0));
-        const int rows_w = min(BN, p.N - n0);
+        const int rows_a = live ? static_cast<int>(min<int64_t>(BM, p.M - m0)) : 0;
+        const int rows_w = live ? min(BN, p.N - n0) : 0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(p.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -231,11 +236,10 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, vo, so, 0, 0);
         }
     };
-    auto advance = [&](SlabCursor& c) {
-        if (++c.kt == KT) {
-            c.kt = 0;
-            c.pid += G;
-        }
+    auto advance = [&](SlabCursor& c) {  // branch-free: it sits inside the interleaved block
+        const bool wrap = c.kt + 1 == KT;
+        c.kt = wrap ? 0 : c.kt + 1;
+        c.pid += wrap ? G : 0;
     };
 
     // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
@@ -294,57 +298,88 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         }
     };
 
-    int pid = blockIdx.x;
-    if (pid >= tiles) return;
-    SlabCursor ld{pid, 0};
-    const int total_slabs_mine = ((tiles - 1 - pid) / G + 1) * KT;
-    int issued = 0;
-    // prologue: two slabs in flight, then wait for all of them (once per kernel)
-    issue_slab(ld, 0);
-    advance(ld);
-    ++issued;
-    if (issued < total_slabs_mine) {
-        issue_slab(ld, 1);
-        advance(ld);
-        ++issued;
-    }
-    sync(true);
+    if (static_cast<int>(blockIdx.x) >= tiles) return;
+    const int total_slabs_mine = ((tiles - 1 - static_cast<int>(blockIdx.x)) / G + 1) * KT;
 
-    f32x16 acc[4][4];
-    bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
-    read_frags(0, 0, fa0, fw0);
-    int stage = 0;
-    for (; pid < tiles; pid += G) {
-        int tm, tn;
-        tile_coords(p, pid, tm, tn);
-        zero(acc);
-        for (int kt = 0; kt < KT; ++kt) {
-            read_frags(stage, 1, fa1, fw1);
-            mfma_step(acc, fa0, fw0);
-            interleave_reads();
-            read_frags(stage, 2, fa0, fw0);
-            mfma_step(acc, fa1, fw1);
-            interleave_reads();
-            read_frags(stage, 3, fa1, fw1);
-            mfma_step(acc, fa0, fw0);
-            interleave_reads();
-            // the next slab has landed and this stage is no longer read: publish the one, refill the other
-            sync(true);
-            if (issued < total_slabs_mine) {
-                issue_slab(ld, stage);  // slab after next into the stage just freed
-                advance(ld);
-                ++issued;
-            }
-            // (the next tile's first fragments are read after the epilogue, which needs the registers)
-            const bool more = kt + 1 < KT;
-            if (more) read_frags(stage ^ 1, 0, fa0, fw0);
-            mfma_step(acc, fa1, fw1);
-            if (more) interleave_reads();
-            stage ^= 1;
+    // The tile loop, instantiated separately for loader and storer waves (the branch is per wave, the
+    // barrier count per tile is the same in both).  In the loader instance the 32 loads of the slab
+    // after next are spread among the last 16 MFMAs of the current slab.
+    auto run = [&](auto loader_tag) {
+        constexpr bool kLoader = decltype(loader_tag)::value;
+        int pid = blockIdx.x;
+        SlabCursor ld{pid, 0};
+        int issued = 0;
+        if (kLoader) {
+            // prologue: two slabs in flight
+            issue_slab(ld, 0, true);
+            advance(ld);
+            ++issued;
+            issue_slab(ld, 1, issued < total_slabs_mine);
+            advance(ld);
+            ++issued;
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
-        epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
-        if (pid + G < tiles) read_frags(stage, 0, fa0, fw0);
-    }
+        sync(false);
+
+        f32x16 acc[4][4];
+        bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
+        read_frags(0, 0, fa0, fw0);
+        int stage = 0;
+        for (; pid < tiles; pid += G) {
+            int tm, tn;
+            tile_coords(p, pid, tm, tn);
+            zero(acc);
+            for (int kt = 0; kt < KT; ++kt) {
+                read_frags(stage, 1, fa1, fw1);
+                mfma_step(acc, fa0, fw0);
+                interleave_reads();
+                read_frags(stage, 2, fa0, fw0);
+                mfma_step(acc, fa1, fw1);
+                interleave_reads();
+                read_frags(stage, 3, fa1, fw1);
+                mfma_step(acc, fa0, fw0);
+                interleave_reads();
+                // the next slab has landed and this stage is no longer read: publish one, refill the other
+                if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+                sync(false);
+                // The next slab's first fragments (the next tile's, at the end of a tile; harmless
+                // stale reads after the last one) are read under the last 16 MFMAs of this slab.
+                read_frags(stage ^ 1, 0, fa0, fw0);
+                if (kLoader) {
+                    issue_slab(ld, stage, issued < total_slabs_mine);  // slab after next into the freed stage
+                    advance(ld);
+                    ++issued;
+                    mfma_step(acc, fa1, fw1);
+                    // fragment reads first (the compiler keeps them ahead of the LDS-writing loads),
+                    // then the 32 loads three or two at a time between the remaining MFMAs
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+#pragma unroll
+                    for (int s8 = 0; s8 < 8; ++s8) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 3, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+                } else {
+                    mfma_step(acc, fa1, fw1);
+                    interleave_reads();
+                }
+                stage ^= 1;
+            }
+            epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
+        }
+    };
+    if (loader)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 }
 
 // ============================================================================
