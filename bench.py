@@ -148,9 +148,11 @@ def main(argv=None):
     torch.cuda.set_device(dev)
 
     if args.copy_probe_mb:
+        # a plain copy of known size: the reference that rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled by
         n = args.copy_probe_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src = torch.full((n,), 7, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst

@@ -5,12 +5,13 @@
 // the stream copy and of its key (each over `dim`, per copy, not jointly over
 // the copies), and dot = sum(h * w * key) * rstd * dim^-1/2.
 //
-// Design (gfx950): HBM-bound streaming reduction.  One wave per
-// (token, copy): every lane streams 16-byte pieces (8 bf16) of the copy's
-// stream row and key row, widens them to fp32, multiplies by the weight
-// product (q and k are tiny and stay in L2) and keeps three fp32 partial
-// sums.  A wave-wide butterfly over DPP/permute lanes finishes the sums; lane 0
-// applies the two reciprocal square roots and writes one fp32.
+// Design (gfx950): HBM-bound streaming reduction.  One wave per 4 tokens of
+// one copy: every lane streams 16-byte pieces (8 bf16) of the 4 stream rows
+// and 4 key rows (8 loads in flight per lane and step), widens them to fp32,
+// multiplies by the weight product (the copy's q and k pieces are loaded once
+// for the 4 tokens; they stay in L2) and keeps three fp32 partial sums per
+// token.  A wave-wide butterfly finishes the sums; lane 0 applies the two
+// reciprocal square roots and writes one fp32 per token.
 #include "common.h"
 
 namespace engram {
@@ -18,6 +19,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kTok = 4;  // tokens per wave: the copy's q/k chunks are loaded once for all of them
 
 struct GateArgs {
     const uint16_t* x;
@@ -29,7 +31,8 @@ struct GateArgs {
     float inv_dim;       // 1/dim
     float rsqrt_dim;     // dim^-1/2
     float* dot;
-    int64_t pairs;       // T * hc
+    int64_t T;
+    int64_t groups;      // ceil(T / kTok) * hc
     int hc, dim;
 };
 
@@ -42,38 +45,58 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
+// One wave per (group of kTok tokens, copy c).
 __global__ __launch_bounds__(kThreads) void gate_dot_kernel(GateArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t pair = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (pair >= a.pairs) return;
-    const int64_t t = pair / a.hc;
-    const int c = static_cast<int>(pair - t * a.hc);
-    const u32x4* h = reinterpret_cast<const u32x4*>(a.x + pair * a.dim);
-    const u32x4* key = reinterpret_cast<const u32x4*>(a.kv + t * a.ld_kv + static_cast<int64_t>(c) * a.dim);
+    const int64_t group = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (group >= a.groups) return;
+    const int c = static_cast<int>(group % a.hc);
+    const int64_t t0 = (group / a.hc) * kTok;
+    const int ntok = static_cast<int>(min<int64_t>(kTok, a.T - t0));
     const u32x4* q = reinterpret_cast<const u32x4*>(a.q + static_cast<int64_t>(c) * a.dim);
     const u32x4* k = reinterpret_cast<const u32x4*>(a.k + static_cast<int64_t>(c) * a.dim);
+    const u32x4* h[kTok];
+    const u32x4* key[kTok];
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+        const int64_t t = t0 + min(u, ntok - 1);  // ragged tail: repeat the last token, never written
+        h[u] = reinterpret_cast<const u32x4*>(a.x + (t * a.hc + c) * a.dim);
+        key[u] = reinterpret_cast<const u32x4*>(a.kv + t * a.ld_kv + static_cast<int64_t>(c) * a.dim);
+    }
     const int chunks = a.dim / 8;
 
-    float hh = 0.f, kk = 0.f, hwk = 0.f;
+    float hh[kTok], kk[kTok], hwk[kTok];
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) hh[u] = kk[u] = hwk[u] = 0.f;
     for (int j = lane; j < chunks; j += 64) {
-        const u32x4 hv = h[j], kv = key[j], qv = q[j], kw = k[j];
+        const u32x4 qv = q[j], kw = k[j];
+        u32x4 hv[kTok], kv[kTok];
+#pragma unroll
+        for (int u = 0; u < kTok; ++u) {
+            hv[u] = h[u][j];
+            kv[u] = key[u][j];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float h0 = lo_bf16(hv[i]), h1 = hi_bf16(hv[i]);
-            const float k0 = lo_bf16(kv[i]), k1 = hi_bf16(kv[i]);
             const float w0 = lo_bf16(qv[i]) * lo_bf16(kw[i]);  // exact: bf16 * bf16 fits fp32
             const float w1 = hi_bf16(qv[i]) * hi_bf16(kw[i]);
-            hh += h0 * h0 + h1 * h1;
-            kk += k0 * k0 + k1 * k1;
-            hwk += h0 * w0 * k0 + h1 * w1 * k1;
+#pragma unroll
+            for (int u = 0; u < kTok; ++u) {
+                const float h0 = lo_bf16(hv[u][i]), h1 = hi_bf16(hv[u][i]);
+                const float k0 = lo_bf16(kv[u][i]), k1 = hi_bf16(kv[u][i]);
+                hh[u] += h0 * h0 + h1 * h1;
+                kk[u] += k0 * k0 + k1 * k1;
+                hwk[u] += h0 * w0 * k0 + h1 * w1 * k1;
+            }
         }
     }
-    hh = wave_sum(hh);
-    kk = wave_sum(kk);
-    hwk = wave_sum(hwk);
-    if (lane == 0) {
-        const float rstd = rsqrtf(hh * a.inv_dim + a.eps) * rsqrtf(kk * a.inv_dim + a.eps);
-        a.dot[pair] = hwk * rstd * a.rsqrt_dim;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+        const float shh = wave_sum(hh[u]), skk = wave_sum(kk[u]), shwk = wave_sum(hwk[u]);
+        if (lane == 0 && u < ntok) {
+            const float rstd = rsqrtf(shh * a.inv_dim + a.eps) * rsqrtf(skk * a.inv_dim + a.eps);
+            a.dot[(t0 + u) * a.hc + c] = shwk * rstd * a.rsqrt_dim;
+        }
     }
 }
 
@@ -104,10 +127,11 @@ extern "C" int engram_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld
     a.inv_dim = 1.0f / static_cast<float>(dim);
     a.rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
     a.dot = dot;
-    a.pairs = T * hc;
+    a.T = T;
+    a.groups = (T + kTok - 1) / kTok * hc;
     a.hc = hc;
     a.dim = dim;
-    const int64_t blocks = (a.pairs + kWaves - 1) / kWaves;
+    const int64_t blocks = (a.groups + kWaves - 1) / kWaves;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gate_dot: too many tokens");
     hipLaunchKernelGGL(gate_dot_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, as_stream(stream), a);
     return check_launch("engram_gate_dot");
