@@ -5,8 +5,8 @@ Python loader for `liboracle.so` (plain C, `engram_oracle.c`).  Only `tests/`,
 this package; the product (`gram_hash_embedding_amd`) never does.
 
 Every wrapper takes and returns numpy arrays.  bf16 values travel as their
-uint16 bit patterns.  The hash, gather and dequant are exact; the projection
-and gate return float64.
+uint16 bit patterns.  The hash, gather and dequant are exact; the projection,
+gate and output return float64.
 """
 from __future__ import annotations
 
@@ -45,12 +45,13 @@ def lib():
         L.oracle_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p]
         L.oracle_wkv.argtypes = [p, p, p, i64, i32, i32]
         L.oracle_gate_dot.argtypes = [p, p, i64, p, p, ctypes.c_double, p, i64, i32, i32]
+        L.oracle_gate_output.argtypes = [p, p, i64, p, p, p, p, i64, i32, i32]
         L.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3fn_decode.restype = ctypes.c_float
         L.oracle_bf16_rne.argtypes = [ctypes.c_float]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_num_threads.restype = ctypes.c_int
-        for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot):
+        for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot, L.oracle_gate_output):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +138,25 @@ def gate_dot(x_bits, kv_bits, q_bits, k_bits, eps):
                                dim)
     _check(rc, "oracle_gate_dot")
     return out
+
+
+def gate_output(x_bits, kv_bits, dot, token_mask=None):
+    """x [T, hc, dim] and kv [T, >= (hc+1)*dim] (value = columns hc*dim .. (hc+1)*dim) as bf16 bits;
+    dot [T, hc]; token_mask [T] (nonzero = takes part) or None -> (gate float64 [T, hc],
+    out float64 [T, hc, dim])."""
+    x = _c(x_bits, np.uint16)
+    kv = _c(kv_bits, np.uint16)
+    d = _c(dot, np.float64)
+    mask = _c(token_mask, np.uint8)
+    T, hc, dim = x.shape
+    if d.shape != (T, hc) or (mask is not None and mask.size != T):
+        raise ValueError("gate_output: dot must be [T, hc] and token_mask [T]")
+    gate = np.empty((T, hc), dtype=np.float64)
+    out = np.empty((T, hc, dim), dtype=np.float64)
+    rc = lib().oracle_gate_output(_ptr(x), _ptr(kv), kv.shape[1], _ptr(d), _ptr(mask), _ptr(gate), _ptr(out),
+                                  T, hc, dim)
+    _check(rc, "oracle_gate_output")
+    return gate, out
 
 
 def e4m3fn_decode(byte: int) -> float:

@@ -10,6 +10,8 @@
  *   gather+dequant -- ParallelEngramEmbedding.forward
  *   wkv          -- the `wkv` Linear of Engram.forward
  *   gate dot     -- Engram.forward up to the gate pre-activation `dot`
+ *   gate output  -- the rest of Engram.forward: signed-sqrt sigmoid gate,
+ *                   masked positions shut, residual add of the gated value
  *
  * Only tests, the smoke entry point and the benchmark's CPU-baseline leg may
  * load this library.  It shares no code, header, table or constant with the
@@ -22,8 +24,8 @@
  * Parity pins (tests/test_oracle_*.py): the hash against a Python big-int
  * brute force and against invariants the pages state; the decode against
  * torch's float8_e4m3fn for all 256 bytes; bf16 rounding against torch; the
- * projection against numpy's float64 matmul; the gate on hand-built vectors
- * with closed-form results.
+ * projection against numpy's float64 matmul; the gate dot, gate and output on
+ * hand-built vectors with closed-form results.
  */
 #include <math.h>
 #include <stdint.h>
@@ -219,6 +221,41 @@ int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const 
             /* normalised per (token, copy) over dim, not jointly over the copies */
             const double rstd = (1.0 / sqrt(hh / dim + eps)) * (1.0 / sqrt(kk / dim + eps));
             dot[t * hc + c] = hwk * rstd / sqrt((double)dim);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* gate activation, mask and residual                                        */
+/* ------------------------------------------------------------------------ */
+
+/* The end of Engram.forward on the stack-hashes page: the gate is the sigmoid
+ * of the signed square root of the dot, with |dot| clamped from below at 1e-6
+ * first (so a zero dot still gives sigmoid(+-1e-3), its sign taken from the
+ * dot, -0 included); a token whose mask entry is false gets gate 0; the output
+ * adds the gated value, which all hc copies share, to each copy of the stream:
+ *     out[t,c,j] = h[t,c,j] + gate[t,c] * value[t,j],  value = kv[t, hc*dim + j].
+ * dot [T,hc] is an input (the oracle's own, or the device's for a unit check);
+ * token_mask [T] (nonzero = takes part) or NULL; gate [T,hc] and out
+ * [T,hc,dim] are double. */
+int oracle_gate_output(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const double* dot,
+                       const uint8_t* token_mask, double* gate, double* out, int64_t T, int hc, int dim) {
+    if (T < 0 || hc < 1 || dim < 1 || ld_kv < (int64_t)(hc + 1) * dim) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* value = kv + t * ld_kv + (int64_t)hc * dim;
+        for (int c = 0; c < hc; ++c) {
+            const double d = dot[t * hc + c];
+            const double mag = sqrt(fmax(fabs(d), 1e-6));
+            const double z = copysign(mag, d);
+            double g = 1.0 / (1.0 + exp(-z));
+            if (token_mask && !token_mask[t]) g = 0.0;
+            gate[t * hc + c] = g;
+            const uint16_t* h = x + (t * hc + c) * (int64_t)dim;
+            double* o = out + (t * hc + c) * (int64_t)dim;
+            for (int j = 0; j < dim; ++j)
+                o[j] = oracle_bf16_to_double(h[j]) + g * oracle_bf16_to_double(value[j]);
         }
     }
     return ORACLE_OK;

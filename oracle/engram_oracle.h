@@ -41,6 +41,13 @@ int oracle_wkv(const uint16_t* a, const uint16_t* w, double* kv, int64_t T, int 
 int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
                     const uint16_t* k_weight, double eps, double* dot, int64_t T, int hc, int dim);
 
+/* gate activation, mask and residual: gate = sigmoid(copysign(sqrt(max(|dot|,
+ * 1e-6)), dot)), 0 where token_mask [T] (or NULL = all true) is 0; out[t,c,j] =
+ * h[t,c,j] + gate[t,c] * kv[t, hc*dim + j].  dot [T,hc] in; gate [T,hc] and
+ * out [T,hc,dim] double out. */
+int oracle_gate_output(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const double* dot,
+                       const uint8_t* token_mask, double* gate, double* out, int64_t T, int hc, int dim);
+
 float oracle_e4m3fn_decode(uint8_t byte);
 uint16_t oracle_bf16_rne(float f);
 double oracle_bf16_to_double(uint16_t h);
