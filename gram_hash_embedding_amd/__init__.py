@@ -11,6 +11,9 @@ an exception is raised.
     engram_gather_dequant  -- fp8 row gather + block-scale dequant -> bf16
     engram_wkv             -- kv = A @ W^T on bf16 matrix cores
     engram_gate_dot        -- per-(token, copy) RMS-normalised gate pre-activation
+    engram_gate_output     -- the dot, the sigmoid gate, the token mask and the residual add
+    engram_wkv_gate        -- wkv + gate dot fused: value columns and dot out, keys never stored
+    engram_gate_residual   -- gate, token mask and residual add from a given dot
 """
 from __future__ import annotations
 
@@ -44,7 +47,13 @@ def lib() -> ctypes.CDLL:
         L.engram_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p, p]
         L.engram_wkv.argtypes = [p, p, p, i64, i32, i32, p]
         L.engram_gate_dot.argtypes = [p, p, i64, p, p, f32, p, i64, i32, i32, p]
-        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_wkv, L.engram_gate_dot, L.engram_abi_version):
+        L.engram_gate_output.argtypes = [p, p, i64, p, p, f32, p, p, p, i64, i32, i32, p]
+        L.engram_wkv_gate.argtypes = [p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
+        L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
+        L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
+        L.engram_wkv_gate_workspace_bytes.restype = i64
+        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_wkv, L.engram_gate_dot, L.engram_gate_output,
+                  L.engram_wkv_gate, L.engram_gate_residual, L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
         L.engram_status_string.restype = ctypes.c_char_p
@@ -191,5 +200,116 @@ def engram_gate_dot(x, kv, q_weight, k_weight, eps, out=None, stream=None):
     return out
 
 
-__all__ = ["engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "EngramError", "lib",
+def engram_gate_output(x, kv, q_weight, k_weight, eps, token_mask=None, out=None, dot=None, stream=None):
+    """out bf16 [T, hc, dim] (x's shape) = x + gate * value, the gate from the dot of x with the keys in
+    kv [T, >= (hc+1)*dim]; token_mask [T] (or x's leading [B, L]) bool/uint8, False shuts the gate.
+    `dot` (float32 [T, hc]), if given, receives the pre-activation."""
+    import torch
+
+    x3 = x.reshape(-1, x.shape[-2], x.shape[-1])
+    T, hc, dim = x3.shape
+    if kv.dim() != 2 or kv.shape[0] != T:
+        raise ValueError("kv must be [T, ld]")
+    if tuple(q_weight.shape) != (hc, dim) or tuple(k_weight.shape) != (hc, dim):
+        raise ValueError("q_weight and k_weight must be [hc, dim]")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    mask_p = None
+    if token_mask is not None:
+        if token_mask.numel() != T:
+            raise ValueError("token_mask must hold one entry per token")
+        if token_mask.dtype == torch.bool:
+            token_mask = token_mask.view(torch.uint8)
+        mask_p = _dev(token_mask.reshape(T), "token_mask", torch.uint8, 1)
+    dot_p = None
+    if dot is not None:
+        if tuple(dot.shape) != (T, hc):
+            raise ValueError("dot must be [T, hc]")
+        dot_p = _dev(dot, "dot", torch.float32)
+    _check(lib().engram_gate_output(
+        _dev(x3, "x", torch.bfloat16, 3), _dev(kv, "kv", torch.bfloat16, 2), kv.shape[1],
+        _dev(q_weight, "q_weight", torch.bfloat16, 2), _dev(k_weight, "k_weight", torch.bfloat16, 2),
+        float(eps), mask_p, _dev(out, "out", torch.bfloat16), dot_p, T, hc, dim, _stream(stream)))
+    return out
+
+
+def engram_wkv_gate_workspace_bytes(T: int, hc: int, dim: int) -> int:
+    n = lib().engram_wkv_gate_workspace_bytes(int(T), int(hc), int(dim))
+    if n < 0:
+        raise ValueError(f"engram_wkv_gate: hc={hc} dim={dim} outside the limits")
+    return n
+
+
+def engram_wkv_gate(a, w, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None, stream=None):
+    """(value bf16 [T, dim], dot float32 [T, hc]) from a bf16 [T, K], w bf16 [(hc+1)*dim, K] and the stream
+    x bf16 [T, hc, dim] (or [B, L, hc, dim]).  `value` may be a [T, ld >= dim] row-strided view whose first
+    dim columns are written; `workspace` a uint8 device tensor of engram_wkv_gate_workspace_bytes bytes
+    (allocated here if not given)."""
+    import torch
+
+    x3 = x.reshape(-1, x.shape[-2], x.shape[-1])
+    T, hc, dim = x3.shape
+    if a.dim() != 2 or a.shape[0] != T:
+        raise ValueError("a must be [T, K]")
+    K = a.shape[1]
+    if tuple(w.shape) != ((hc + 1) * dim, K):
+        raise ValueError("w must be [(hc+1)*dim, K]")
+    if tuple(q_weight.shape) != (hc, dim) or tuple(k_weight.shape) != (hc, dim):
+        raise ValueError("q_weight and k_weight must be [hc, dim]")
+    if value is None:
+        value = torch.empty((T, dim), dtype=torch.bfloat16, device=a.device)
+    if value.dim() != 2 or value.shape[0] != T or value.shape[1] < dim or value.stride(1) != 1:
+        raise ValueError("value must be [T, >= dim] with unit column stride")
+    if value.dtype != torch.bfloat16 or not value.is_cuda:
+        raise TypeError("value must be a bf16 GPU tensor")
+    if dot is None:
+        dot = torch.empty((T, hc), dtype=torch.float32, device=a.device)
+    if tuple(dot.shape) != (T, hc):
+        raise ValueError("dot must be [T, hc]")
+    need = engram_wkv_gate_workspace_bytes(T, hc, dim)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    _check(lib().engram_wkv_gate(
+        _dev(a, "a", torch.bfloat16, 2), _dev(w, "w", torch.bfloat16, 2), _dev(x3, "x", torch.bfloat16, 3),
+        _dev(q_weight, "q_weight", torch.bfloat16, 2), _dev(k_weight, "k_weight", torch.bfloat16, 2), float(eps),
+        ctypes.c_void_p(value.data_ptr()), value.stride(0), _dev(dot, "dot", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), T, K, hc, dim, _stream(stream)))
+    return value, dot
+
+
+def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
+    """out bf16 (x's shape: [T, hc, dim] or [B, L, hc, dim]) = x + gate(dot) * value, from value bf16
+    [T, >= dim] (row-strided view allowed) and dot float32 [T, hc]; token_mask [T] or [B, L]
+    (False shuts the gate).  `out` may be x itself."""
+    import torch
+
+    x3 = x.reshape(-1, x.shape[-2], x.shape[-1])
+    T, hc, dim = x3.shape
+    if value.dim() != 2 or value.shape[0] != T or value.shape[1] < dim or value.stride(1) != 1:
+        raise ValueError("value must be [T, >= dim] with unit column stride")
+    if value.dtype != torch.bfloat16 or not value.is_cuda:
+        raise TypeError("value must be a bf16 GPU tensor")
+    if tuple(dot.shape) != (T, hc):
+        raise ValueError("dot must be [T, hc]")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    mask_p = None
+    if token_mask is not None:
+        if token_mask.numel() != T:
+            raise ValueError("token_mask must hold one entry per token")
+        if token_mask.dtype == torch.bool:
+            token_mask = token_mask.view(torch.uint8)
+        mask_p = _dev(token_mask.reshape(T), "token_mask", torch.uint8, 1)
+    _check(lib().engram_gate_residual(
+        _dev(x3, "x", torch.bfloat16, 3), ctypes.c_void_p(value.data_ptr()), value.stride(0),
+        _dev(dot, "dot", torch.float32), mask_p, _dev(out, "out", torch.bfloat16), T, hc, dim, _stream(stream)))
+    return out
+
+
+__all__ = ["engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
+           "engram_wkv_gate", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "EngramError", "lib",
            "LIB_PATH"]

@@ -65,10 +65,18 @@ constexpr int kBufferWord3 = 0x00020000;
 struct WkvArgs {
     const uint16_t* a;
     const uint16_t* w;
-    uint16_t* kv;
+    uint16_t* kv;      // stored output rows: columns [out_col0, N) of the product, row stride ld_out
     int64_t M;
     int N, K;
     int tiles_m, tiles_n;
+    int64_t ld_out;
+    int out_col0;
+    // fused gate partial sums (key columns [0, hc*dim) are reduced, not stored)
+    const uint16_t* x;  // [M, hc, dim] bf16
+    const uint16_t* q;  // [hc, dim] bf16
+    const uint16_t* k;  // [hc, dim] bf16
+    float* part;        // [hc][dim/128][3][M] fp32: per 128-column slice sum(h w key), sum(key^2), sum(h^2)
+    int hc, dim;
 };
 
 // pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
@@ -97,6 +105,9 @@ __device__ inline float acc_read(float a) {
 
 // lane id recomputed from the exec mask (two VALU ops) rather than kept live in a VGPR
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -171,6 +182,7 @@ struct SlabCursor {
 // every global store.  A wave's vmcnt counts its loads and stores together, and the slab barrier must
 // wait for the loads; with the roles split, the loaders never have stores outstanding and the storers
 // never wait on vmcnt, so a tile's output drains while the next tile computes.
+template <bool kGate>
 __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     // [stage][A|W][256 rows][128 B] + exchange region: 160 KB, the whole LDS of a CU
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                 const int half = wave - 2;  // token half wm = half of the tile
                 const int ls = lane_id();
                 const int chunk = ls & 31, hi = ls >> 5;
-                uint16_t* dst = p.kv + (m0 + half * 128 + 32 * i + hi) * p.N + n0 + chunk * 8;
+                uint16_t* dst = p.kv + (m0 + half * 128 + 32 * i + hi) * p.ld_out + (n0 - p.out_col0) + chunk * 8;
                 const bool col_ok = n0 + chunk * 8 < p.N;
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
@@ -291,10 +303,122 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                     const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 512 + ((chunk ^ (rr & 31)) << 4));
                     const int64_t m = m0 + half * 128 + 32 * i + 2 * q + hi;
                     if (m < p.M && col_ok)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(2 * q) * p.N));
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 2 * q * p.ld_out));
                 }
             }
             sync_epi();
+        }
+    };
+
+    // ---- fused gate epilogue of a key tile: no stores of the product.  The tile's 256 columns lie in
+    // one copy c; wave (wm, wn) owns the 128-column slice s = 2 * (tile's slice) + wn.  Lane l holds,
+    // per round i, token 32i + l%32 of the wave's 128 tokens and 64 of the slice's columns (4
+    // consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is rounded to bf16
+    // (the product is a bf16 tensor before it is used) and reduced against the stream's matching
+    // element: sum(h w key), sum(key^2), sum(h^2) over the lane's 64 columns, then over the two lane
+    // halves.
+    // The stream rows of a round (32 tokens x 256 B per wave) come in with full-line direct-to-LDS
+    // loads into the wave's own 8 KB quarter of the exchange region (row r, 16-byte piece p at slot
+    // p ^ ((r >> 1) & 15): the lane-layout reads below are conflict-free) -- scattered 8-byte loads
+    // straight into the lane layout touch 32 lines per instruction and measured 0.1 ms slower.  The
+    // next round's rows are in flight while a round is reduced.  The loader waves hand their sums to
+    // the storer waves through LDS (one barrier), so they never have stores outstanding.
+    auto gate_epilogue = [&](const f32x16 (&acc)[4][4], int64_t m0, int n0) {
+        const int l = lane_id();
+        const int c = n0 / p.dim;
+        const int col0 = n0 - c * p.dim + wn * 128;  // the wave's slice, in the copy's columns
+        const int slice = col0 / 128;
+        const int slices = p.dim / 128;
+        const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        float wgt[4][4][4];  // q * k (exact in fp32) for the lane's 64 columns
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + 32 * j + 8 * gq);
+                const u32x2 kv = *reinterpret_cast<const u32x2*>(krow + 32 * j + 8 * gq);
+                wgt[j][gq][0] = lo_bf16(qv[0]) * lo_bf16(kv[0]);
+                wgt[j][gq][1] = hi_bf16(qv[0]) * hi_bf16(kv[0]);
+                wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
+                wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
+            }
+        uint8_t* xl = ex + wave * 8192;
+        const uint16_t* xslice = p.x + static_cast<int64_t>(c) * p.dim + col0;
+        const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
+        auto dma_x = [&](int i) {  // round i's 32 rows: 4 rows of 16 pieces per instruction
+            const int ll = lane_id();
+#pragma unroll
+            for (int ins = 0; ins < 8; ++ins) {
+                const int r = 4 * ins + (ll >> 4);
+                const int piece = (ll & 15) ^ ((r >> 1) & 15);
+                const int64_t t = min<int64_t>(m0 + wm * 128 + 32 * i + r, p.M - 1);  // past M: unused
+                __builtin_amdgcn_global_load_lds(xslice + t * xstride + 8 * piece, xl + ins * 1024, 16, 0, 0);
+            }
+        };
+        float res[4][3];
+        dma_x(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x2 xr[4][4];
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            asm volatile("" ::: "memory");
+            {
+                const int rr = l & 31, h = l >> 5;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq)
+                        xr[j][gq] = *reinterpret_cast<const u32x2*>(
+                            xl + rr * 256 + (((4 * j + gq) ^ ((rr >> 1) & 15)) << 4) + h * 8);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+            asm volatile("" ::: "memory");
+            if (i < 3) dma_x(i + 1);  // the quarter has been read: refill it
+            float hwk = 0.f, kk = 0.f, hh = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const uint32_t k01 = pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1]));
+                    const uint32_t k23 = pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]));
+                    const float key[4] = {lo_bf16(k01), hi_bf16(k01), lo_bf16(k23), hi_bf16(k23)};
+                    const float h[4] = {lo_bf16(xr[j][gq][0]), hi_bf16(xr[j][gq][0]), lo_bf16(xr[j][gq][1]),
+                                        hi_bf16(xr[j][gq][1])};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        hwk += h[r] * wgt[j][gq][r] * key[r];
+                        kk += key[r] * key[r];
+                        hh += h[r] * h[r];
+                    }
+                }
+            res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
+            res[i][1] = kk + __shfl_xor(kk, 32, 64);
+            res[i][2] = hh + __shfl_xor(hh, 32, 64);
+        }
+        // hand-over: a loader wave (tokens 0-127 of the tile) leaves its sums in its own quarter, laid
+        // out [round][sum][token]; the storer wave of the same slice writes them with lanes 32-63
+        if (loader && l < 32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 3; ++q) reinterpret_cast<float*>(xl)[(i * 3 + q) * 32 + l] = res[i][q];
+        }
+        sync_epi();
+        if (!loader) {
+            const int ls = lane_id();
+            const float* partner = reinterpret_cast<const float*>(ex + (wave - 2) * 8192);
+            const int64_t tbase = m0 + (ls < 32 ? 128 : 0) + (ls & 31);
+            float* out = p.part + (static_cast<int64_t>(c) * slices + slice) * 3 * p.M;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = tbase + 32 * i;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const float v = ls < 32 ? res[i][q] : partner[(i * 3 + q) * 32 + (ls & 31)];
+                    if (t < p.M) out[q * p.M + t] = v;
+                }
+            }
         }
     };
 
@@ -373,7 +497,10 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                 }
                 stage ^= 1;
             }
-            epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
+            if (kGate && tn * BN < p.out_col0)
+                gate_epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
+            else
+                epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
         }
     };
     if (loader)
@@ -471,6 +598,26 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_staged(WkvArgs p) {
     store_tile(p, acc, m0, n0, wm, wn, lane);
 }
 
+// ============================================================================
+// gate finalize: the fused kernel's per-slice partial sums -> dot (fixed summation order)
+// ============================================================================
+__global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, float* dot, int64_t M, int hc,
+                                                            int slices, float eps, float inv_dim, float rsqrt_dim) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= M * hc) return;
+    const int c = static_cast<int>(idx / M);  // consecutive threads: consecutive tokens of one copy
+    const int64_t t = idx - static_cast<int64_t>(c) * M;
+    const float* src = part + static_cast<int64_t>(c) * slices * 3 * M + t;
+    float hwk = 0.f, kk = 0.f, hh = 0.f;
+    for (int s = 0; s < slices; ++s) {
+        hwk += src[(3 * s + 0) * M];
+        kk += src[(3 * s + 1) * M];
+        hh += src[(3 * s + 2) * M];
+    }
+    const float rstd = rsqrtf(hh * inv_dim + eps) * rsqrtf(kk * inv_dim + eps);
+    dot[t * hc + c] = hwk * rstd * rsqrt_dim;
+}
+
 }  // namespace
 }  // namespace engram
 
@@ -484,13 +631,15 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     if (T == 0) return ENGRAM_OK;
     if (!a || !w || !kv) return fail(ENGRAM_EINVAL, "engram_wkv: null pointer");
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(kv, 16)) return fail(ENGRAM_EINVAL, "engram_wkv: misaligned pointer");
-    WkvArgs p;
+    WkvArgs p = {};
     p.a = a;
     p.w = w;
     p.kv = kv;
     p.M = T;
     p.N = Nout;
     p.K = K;
+    p.ld_out = Nout;
+    p.out_col0 = 0;
     const int64_t tiles_m = (T + BM - 1) / BM;
     p.tiles_n = (Nout + BN - 1) / BN;
     if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv: too many tiles");
@@ -498,10 +647,70 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     const int64_t tiles = tiles_m * p.tiles_n;
     if (K % BK == 0) {
         const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-        hipLaunchKernelGGL(wkv_kernel_dma, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+        hipLaunchKernelGGL(wkv_kernel_dma<false>, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
     } else {
         hipLaunchKernelGGL(wkv_kernel_staged, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
                            as_stream(stream), p);
     }
     return check_launch("engram_wkv");
+}
+
+extern "C" int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim) {
+    if (T < 0 || hc < 1 || hc > 64 || dim < 256 || dim % 256 != 0) return -1;
+    return static_cast<int64_t>(hc) * (dim / 128) * 3 * T * static_cast<int64_t>(sizeof(float));
+}
+
+extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
+                               const uint16_t* k_weight, float eps, uint16_t* value, int64_t ld_value, float* dot,
+                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc,
+                               int32_t dim, void* stream) {
+    if (T < 0) return fail(ENGRAM_EINVAL, "engram_wkv_gate: T < 0");
+    if (K < BK || K % BK != 0) return fail(ENGRAM_EINVAL, "engram_wkv_gate: K=%d must be a positive multiple of %d", K, BK);
+    if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "engram_wkv_gate: hc=%d outside [1, 64]", hc);
+    if (dim < 256 || dim % 256 != 0)
+        return fail(ENGRAM_EINVAL, "engram_wkv_gate: dim=%d must be a positive multiple of 256", dim);
+    if (ld_value < dim || ld_value % 8 != 0)
+        return fail(ENGRAM_EINVAL, "engram_wkv_gate: ld_value=%lld must be >= dim and a multiple of 8",
+                    (long long)ld_value);
+    const int64_t need = engram_wkv_gate_workspace_bytes(T, hc, dim);
+    if (workspace_bytes < need)
+        return fail(ENGRAM_ERANGE, "engram_wkv_gate: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    if (T == 0) return ENGRAM_OK;
+    if (!a || !w || !x || !q_weight || !k_weight || !value || !dot || !workspace)
+        return fail(ENGRAM_EINVAL, "engram_wkv_gate: null pointer");
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(x, 16) || !aligned(q_weight, 16) || !aligned(k_weight, 16) ||
+        !aligned(value, 16) || !aligned(dot, 4) || !aligned(workspace, 16))
+        return fail(ENGRAM_EINVAL, "engram_wkv_gate: misaligned pointer");
+    const int Nout = (hc + 1) * dim;
+    WkvArgs p = {};
+    p.a = a;
+    p.w = w;
+    p.kv = value;
+    p.M = T;
+    p.N = Nout;
+    p.K = K;
+    p.ld_out = ld_value;
+    p.out_col0 = hc * dim;
+    p.x = x;
+    p.q = q_weight;
+    p.k = k_weight;
+    p.part = static_cast<float*>(workspace);
+    p.hc = hc;
+    p.dim = dim;
+    const int64_t tiles_m = (T + BM - 1) / BM;
+    p.tiles_n = Nout / BN;
+    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tiles");
+    p.tiles_m = static_cast<int>(tiles_m);
+    const int64_t tiles = tiles_m * p.tiles_n;
+    const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
+    hipLaunchKernelGGL(wkv_kernel_dma<true>, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    int rc = check_launch("engram_wkv_gate");
+    if (rc != ENGRAM_OK) return rc;
+    const int64_t blocks = (T * hc + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");
+    hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
+                       p.part, dot, T, hc, dim / 128, eps, 1.0f / static_cast<float>(dim),
+                       static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim))));
+    return check_launch("engram_wkv_gate (finalize)");
 }

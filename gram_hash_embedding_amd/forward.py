@@ -1,17 +1,24 @@
-"""One Engram forward pass over the four entry points, with reusable buffers.
+"""One Engram forward pass over the HIP entry points, with reusable buffers.
 
 The order of the steps is that of the DeepSeek V4.1 "stack-hashes" page: the
 model forward hashes once for all engram layers, then each engram layer
 gathers its rows from its own slice of the ids, projects them with `wkv`
-and forms the gate pre-activation against the residual stream.  This module
-only allocates outputs and calls the HIP entry points in that order.
+and forms the gate pre-activation against the residual stream -- or, with
+`output=True`, the whole of Engram.forward: the gate, the token mask and the
+residual add, which return the layer's new stream.  With `fused=True` the
+projection and the gate pre-activation run as one entry point
+(engram_wkv_gate: the keys are reduced inside the projection and never
+stored) and the output, if asked for, comes from engram_gate_residual.  This
+module only allocates outputs and workspace and calls the HIP entry points in
+that order.
 """
 from __future__ import annotations
 
 import dataclasses
 from typing import List
 
-from . import engram_gate_dot, engram_gather_dequant, engram_hash, engram_wkv
+from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant, engram_hash,
+               engram_wkv, engram_wkv_gate, engram_wkv_gate_workspace_bytes)
 
 
 @dataclasses.dataclass
@@ -41,7 +48,8 @@ class LayerWeights:
 
 
 class EngramForward:
-    """Runs hash -> (gather+dequant -> wkv -> gate dot) per layer on the current stream."""
+    """Runs hash -> (gather+dequant -> wkv -> gate dot | gate output) per layer on the current stream
+    (or gather+dequant -> fused wkv + gate dot [-> gate residual])."""
 
     def __init__(self, state: HashState, layers: List[LayerWeights], eps: float):
         self.state = state
@@ -87,11 +95,14 @@ class EngramForward:
             input_ids, start_pos, token_mask, s.token_map, s.cache, s.multipliers, s.primes, s.offsets, s.pad_id,
             s.dead, out=out))
 
-    def layer(self, e: int, hash_ids, x, events=None):
-        """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim].
+    def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False):
+        """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim]
+        (or [B, L, hc, dim]); with `output`, also the layer's output stream bf16 (x's shape), where
+        token_mask [B, L] (False = pass through) shuts the gate.  With `fused`, the second tensor is
+        the value bf16 [T, dim] alone (the keys are never stored).
 
-        The three tensors are this object's buffers for layer e: the next call for the same
-        layer overwrites them."""
+        The tensors are this object's buffers for layer e: the next call for the same layer
+        overwrites them."""
         import torch
 
         lw = self.layers[e]
@@ -101,23 +112,40 @@ class EngramForward:
         a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
         self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
             hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
-        kv = self._buf(("kv", e), (T, lw.wkv.shape[0]), torch.bfloat16, dev)
-        self._timed(events, "wkv", lambda: engram_wkv(a.view(T, -1), lw.wkv, out=kv))
         x3 = x.reshape(T, x.shape[-2], x.shape[-1])
         dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
+        if fused:
+            hc, dim = x3.shape[1], x3.shape[2]
+            value = self._buf(("value", e), (T, dim), torch.bfloat16, dev)
+            ws = self._buf("workspace", (engram_wkv_gate_workspace_bytes(T, hc, dim),), torch.uint8, dev)
+            self._timed(events, "wkv_gate", lambda: engram_wkv_gate(
+                a.view(T, -1), lw.wkv, x3, lw.q_weight, lw.k_weight, self.eps, value=value, dot=dot, workspace=ws))
+            if output:
+                out = self._buf(("out", e), tuple(x.shape), torch.bfloat16, dev)
+                self._timed(events, "gate_residual", lambda: engram_gate_residual(x, value, dot, token_mask, out=out))
+                return a, value, dot, out
+            return a, value, dot
+        kv = self._buf(("kv", e), (T, lw.wkv.shape[0]), torch.bfloat16, dev)
+        self._timed(events, "wkv", lambda: engram_wkv(a.view(T, -1), lw.wkv, out=kv))
+        if output:
+            out = self._buf(("out", e), tuple(x.shape), torch.bfloat16, dev)
+            self._timed(events, "gate_output", lambda: engram_gate_output(
+                x, kv, lw.q_weight, lw.k_weight, self.eps, token_mask, out=out, dot=dot))
+            return a, kv, dot, out
         self._timed(events, "gate_dot", lambda: engram_gate_dot(x3, kv, lw.q_weight, lw.k_weight, self.eps, out=dot))
         return a, kv, dot
 
-    def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None):
+    def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
-        (or one tensor shared by all layers).  Returns the per-layer gate pre-activations.
+        (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
+        `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
         `events`: optional dict that collects (start, end) timing events per entry point."""
         ids = self.hash(input_ids, start_pos, token_mask, events)
-        dots = []
+        res = []
         for e in range(self.E):
             x = xs[e] if isinstance(xs, (list, tuple)) else xs
-            dots.append(self.layer(e, ids, x, events)[2])
-        return dots
+            res.append(self.layer(e, ids, x, events, token_mask=token_mask, output=output, fused=fused)[-1])
+        return res
 
 
 def _numel(shape) -> int:

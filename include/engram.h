@@ -11,6 +11,13 @@
  *   engram_gather_dequant  -- ParallelEngramEmbedding.forward (one rank)
  *   engram_wkv             -- the `wkv` Linear inside Engram.forward
  *   engram_gate_dot        -- Engram.forward up to the gate pre-activation `dot`
+ *   engram_gate_output     -- the rest of Engram.forward: the dot, the gate,
+ *                             the token mask and the residual add
+ *   engram_wkv_gate        -- engram_wkv and engram_gate_dot in one pass: the
+ *                             keys are reduced where they are computed and
+ *                             never written; only the value columns are stored
+ *   engram_gate_residual   -- the gate, the token mask and the residual add
+ *                             from a given dot (after engram_wkv_gate)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -155,6 +162,97 @@ int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t T, in
 int engram_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
                     const uint16_t* k_weight, float eps, float* dot, int64_t T, int32_t hc, int32_t dim,
                     void* stream);
+
+/*
+ * engram_gate_output -- the end of Engram.forward (stack-hashes page: `dot`,
+ * `gate`, the token mask and the returned sum), one pass over the stream.
+ *
+ *   dot[t,c]   as engram_gate_dot computes it
+ *   gate[t,c]  = sigmoid(copysign(sqrt(max(|dot|, 1e-6)), dot)); 0 if token_mask[t] == 0
+ *   out[t,c,j] = bf16(fp32(h[j] + fp32(gate[t,c] * value[j])))
+ *   with h = x[t,c,:], value = kv[t, hc*dim : (hc+1)*dim] (one value row per token,
+ *   shared by its hc copies).  The product and the sum are rounded separately (no
+ *   fused multiply-add), then the sum is rounded to bf16 to nearest even, so a
+ *   masked token's output equals x bit for bit (x = -0 with value >= +0 gives +0,
+ *   by IEEE addition).
+ *
+ * x          uint16 [T, hc, dim] bf16 bits; 16-byte aligned
+ * kv         uint16 bf16 bits, row stride ld_kv >= (hc+1)*dim: keys in columns
+ *            [0, hc*dim), value in [hc*dim, (hc+1)*dim) (engram_wkv's output,
+ *            ld_kv = Nout); 16-byte aligned, ld_kv % 8 == 0
+ * q_weight, k_weight  uint16 [hc, dim] bf16 bits; 16-byte aligned
+ * eps        the RMS epsilon (norm_eps)
+ * token_mask uint8 [T], nonzero = the token takes part, 0 = its gate is shut;
+ *            NULL = every token takes part
+ * out        uint16 [T, hc, dim] bf16 bits, out; 16-byte aligned; must not
+ *            overlap x or kv
+ * dot        float32 [T, hc], out, optional (NULL = not written); 4-byte aligned
+ * Limits: T >= 0; 1 <= hc <= 64; 8 <= dim <= 8192 and dim % 8 == 0.
+ */
+int engram_gate_output(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
+                       const uint16_t* k_weight, float eps, const uint8_t* token_mask, uint16_t* out,
+                       float* dot, int64_t T, int32_t hc, int32_t dim, void* stream);
+
+/*
+ * engram_wkv_gate -- the `wkv` Linear and the gate pre-activation of
+ * Engram.forward (stack-hashes page: `kv`, its key/value split, `rstd`, `dot`)
+ * fused: the product's key columns are rounded to bf16 and reduced against
+ * the stream inside the projection, so the [T, hc*dim] keys are never
+ * written; only the value columns are stored.
+ *
+ *   kv       = bf16(a * w^T)  (fp32 accumulation), Nout = (hc+1)*dim
+ *   value    = kv[:, hc*dim : (hc+1)*dim]                       -> value
+ *   dot[t,c] = as engram_gate_dot, with key = kv[t, c*dim : (c+1)*dim]  -> dot
+ * The sums of a (token, copy) are formed per 128-column slice (fp32) in the
+ * projection, kept in `workspace`, and added in slice order by a second
+ * kernel on the same stream, so results are deterministic.
+ *
+ * a          uint16 [T, K] bf16 bits; 16-byte aligned
+ * w          uint16 [(hc+1)*dim, K] bf16 bits; 16-byte aligned
+ * x          uint16 [T, hc, dim] bf16 bits (the stream); 16-byte aligned
+ * q_weight, k_weight  uint16 [hc, dim] bf16 bits; 16-byte aligned
+ * eps        the RMS epsilon (norm_eps)
+ * value      uint16 [T, ld_value] bf16 bits, out (first dim columns of each row
+ *            written); ld_value >= dim, ld_value % 8 == 0; 16-byte aligned
+ * dot        float32 [T, hc], out; 4-byte aligned
+ * workspace  device scratch of at least engram_wkv_gate_workspace_bytes(T, hc,
+ *            dim) bytes, 16-byte aligned, owned by the caller; its contents
+ *            are overwritten and need no initialisation.  Two calls in flight
+ *            at once must not share it.
+ * Limits: T >= 0; K >= 64 and K % 64 == 0; 1 <= hc <= 64; dim >= 256 and
+ * dim % 256 == 0 (each 256-column tile of the product lies in one key copy
+ * or in the value).  Too small a workspace -> ENGRAM_ERANGE.
+ */
+int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
+                    const uint16_t* k_weight, float eps, uint16_t* value, int64_t ld_value, float* dot,
+                    void* workspace, int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc, int32_t dim,
+                    void* stream);
+
+/*
+ * engram_gate_residual -- the end of Engram.forward after `dot` (stack-hashes
+ * page: `gate`, the token mask, the returned sum) for a dot computed
+ * elsewhere (engram_wkv_gate's):
+ *
+ *   gate[t,c]  = sigmoid(copysign(sqrt(max(|dot[t,c]|, 1e-6)), dot[t,c])); 0 if token_mask[t] == 0
+ *   out[t,c,j] = bf16(fp32(h[j] + fp32(gate[t,c] * value[t,j]))),  h = x[t,c,:]
+ * with the same rounding as engram_gate_output.
+ *
+ * x          uint16 [T, hc, dim] bf16 bits; 16-byte aligned
+ * value      uint16 [T, ld_value] bf16 bits (first dim columns used); ld_value
+ *            >= dim, ld_value % 8 == 0; 16-byte aligned
+ * dot        float32 [T, hc]; 4-byte aligned
+ * token_mask uint8 [T] (nonzero = takes part) or NULL = every token
+ * out        uint16 [T, hc, dim] bf16 bits, out; 16-byte aligned; may be x itself
+ *            (each element is read before it is written, by the same thread)
+ * Limits: T >= 0; 1 <= hc <= 64; dim >= 8 and dim % 8 == 0.
+ */
+int engram_gate_residual(const uint16_t* x, const uint16_t* value, int64_t ld_value, const float* dot,
+                         const uint8_t* token_mask, uint16_t* out, int64_t T, int32_t hc, int32_t dim,
+                         void* stream);
+
+/* Bytes of workspace engram_wkv_gate needs for T tokens (hc * dim/128 * 3 * T
+ * floats), or -1 if hc or dim is outside the limits above. */
+int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,9 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert set(names) >= {"engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot",
-                          "engram_status_string", "engram_last_error", "engram_abi_version"}
+                          "engram_gate_output", "engram_wkv_gate", "engram_wkv_gate_workspace_bytes",
+                          "engram_gate_residual", "engram_status_string", "engram_last_error",
+                          "engram_abi_version"}
     L = g.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -75,6 +77,9 @@ def test_zero_tokens_is_a_valid_no_op():
     assert L.engram_gather_dequant(None, 0, 24, 24, None, None, 10, 0, 64, 32, None, None, None, None) == 0
     assert L.engram_wkv(None, None, None, 0, 64, 64, None) == 0
     assert L.engram_gate_dot(None, None, 64, None, None, 1e-20, None, 0, 4, 16, None) == 0
+    assert L.engram_gate_output(None, None, 80, None, None, 1e-20, None, None, None, 0, 4, 16, None) == 0
+    assert L.engram_wkv_gate(None, None, None, None, None, 1e-20, None, 256, None, None, 0, 0, 64, 4, 256, None) == 0
+    assert L.engram_gate_residual(None, None, 16, None, None, None, 0, 4, 16, None) == 0
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -107,6 +112,62 @@ def test_wkv_validation(K, N, msg):
 def test_gate_validation(ld, hc, dim, msg):
     assert g.lib().engram_gate_dot(FAKE, FAKE, ld, FAKE, FAKE, 1e-20, FAKE, 10, hc, dim, None) == 1
     assert msg in _err()
+
+
+@pytest.mark.parametrize("ld,hc,dim,msg", [(80, 0, 16, "hc=0"), (80, 65, 16, "hc=65"), (80, 4, 12, "dim=12"),
+                                           (16392, 1, 8200, "dim=8200"), (64, 4, 16, "ld_kv"),
+                                           (84, 4, 16, "ld_kv")])
+def test_gate_output_validation(ld, hc, dim, msg):
+    assert g.lib().engram_gate_output(FAKE, FAKE, ld, FAKE, FAKE, 1e-20, None, FAKE, None, 10, hc, dim, None) == 1
+    assert msg in _err()
+
+
+def test_gate_output_pointer_checks():
+    L = g.lib()
+    assert L.engram_gate_output(FAKE, FAKE, 80, FAKE, FAKE, 1e-20, None, None, None, 10, 4, 16, None) == 1
+    assert "null" in _err()
+    bad = ctypes.c_void_p(0x100008)
+    assert L.engram_gate_output(FAKE, FAKE, 80, FAKE, FAKE, 1e-20, None, bad, None, 10, 4, 16, None) == 1
+    assert "misaligned" in _err()
+    assert L.engram_gate_output(FAKE, FAKE, 80, FAKE, FAKE, 1e-20, None, FAKE, ctypes.c_void_p(0x100002), 10, 4,
+                                16, None) == 1
+    assert "misaligned" in _err()
+
+
+def test_wkv_gate_workspace_bytes():
+    L = g.lib()
+    assert L.engram_wkv_gate_workspace_bytes(65536, 4, 5120) == 4 * 40 * 3 * 65536 * 4
+    assert L.engram_wkv_gate_workspace_bytes(1, 1, 256) == 1 * 2 * 3 * 1 * 4
+    assert L.engram_wkv_gate_workspace_bytes(0, 4, 256) == 0
+    for T, hc, dim in [(-1, 4, 256), (10, 0, 256), (10, 65, 256), (10, 4, 320), (10, 4, 128)]:
+        assert L.engram_wkv_gate_workspace_bytes(T, hc, dim) == -1
+    with pytest.raises(ValueError):
+        g.engram_wkv_gate_workspace_bytes(10, 4, 320)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=96), 1, "K=96"), (dict(K=0), 1, "K=0"), (dict(hc=0), 1, "hc=0"), (dict(dim=320), 1, "dim=320"),
+    (dict(dim=128), 1, "dim=128"), (dict(ld_value=200), 1, "ld_value"), (dict(ld_value=260), 1, "ld_value"),
+    (dict(ws_bytes=10 * 4 * 2 * 3 * 4 - 4), 2, "workspace"), (dict(a=None), 1, "null"), (dict(ws=None), 1, "null"),
+    (dict(value=ctypes.c_void_p(0x100008)), 1, "misaligned"), (dict(ws=ctypes.c_void_p(0x100004)), 1, "misaligned"),
+])
+def test_wkv_gate_validation(kw, status, msg):
+    a = dict(a=FAKE, w=FAKE, x=FAKE, q=FAKE, k=FAKE, value=FAKE, ld_value=256, dot=FAKE, ws=FAKE,
+             ws_bytes=10 * 4 * 2 * 3 * 4, T=10, K=128, hc=4, dim=256)
+    a.update(kw)
+    rc = g.lib().engram_wkv_gate(a["a"], a["w"], a["x"], a["q"], a["k"], 1e-20, a["value"], a["ld_value"], a["dot"],
+                                 a["ws"], a["ws_bytes"], a["T"], a["K"], a["hc"], a["dim"], None)
+    assert rc == status
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("ld,hc,dim,msg", [(16, 0, 16, "hc=0"), (16, 65, 16, "hc=65"), (16, 4, 12, "dim=12"),
+                                           (8, 4, 16, "ld_value"), (20, 4, 16, "ld_value")])
+def test_gate_residual_validation(ld, hc, dim, msg):
+    assert g.lib().engram_gate_residual(FAKE, FAKE, ld, FAKE, None, FAKE, 10, hc, dim, None) == 1
+    assert msg in _err()
+    assert g.lib().engram_gate_residual(FAKE, FAKE, 16, None, None, FAKE, 10, 4, 16, None) == 1
+    assert "null" in _err()
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -1,7 +1,11 @@
 """The whole path at workload sizes, launched exactly as the benchmark launches
 it (gram_hash_embedding_amd.forward.EngramForward), against the oracle's own
 pipeline on sampled tokens: hash ids in full, gathered rows bit-exact, kv and
-the gate pre-activation within tolerance."""
+the gate pre-activation within tolerance; the fused projection + gate dot
+(value columns bit-exact against the unfused kv, dot within tolerance); then
+the whole module (gate, mask, residual) unfused and fused, as the
+benchmark's loops run them, the output stream within tolerance and masked
+tokens bit-exact."""
 import numpy as np
 import pytest
 
@@ -34,9 +38,12 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
     ids = oracle.hash(hi.input_ids, 0, hi.token_mask, hi.token_map, np.zeros((B, L), np.int64), hi.multipliers,
                       hi.primes, hi.offsets, cfg.pad_id, synth.DEAD)
     np.testing.assert_array_equal(wl.fwd._bufs["ids"].view(B, L, cfg.n_layers, C).cpu().numpy(), ids)
-    sample = sample_tokens(T, n_sample, cfg_index, L=L, mask=hi.token_mask)
+    masked = [] if hi.token_mask is None else np.flatnonzero(hi.token_mask.reshape(T) == 0)
+    extra = masked[:: max(1, len(masked) // 16)][:16] if len(masked) else ()
+    sample = sample_tokens(T, n_sample, cfg_index, L=L, mask=hi.token_mask, extra=extra)
     sidx = torch.from_numpy(sample).to(gpu_device)
     x_bits = bits(wl.x[0].view(T, cfg.hc_mult, cfg.dim)[sidx])
+    want = []
     for e in range(cfg.n_layers):
         lw = wl.fwd.layers[e]
         a_gpu, kv_gpu, dot_gpu = wl.fwd._bufs[("a", e)], wl.fwd._bufs[("kv", e)], dots[e]
@@ -57,3 +64,30 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
         dot_unit = oracle.gate_dot(x_bits, kv_got, q_bits, k_bits, cfg.eps)
         assert_close(dot_gpu.view(T, -1)[sidx].cpu().numpy(), dot_unit, rtol=1e-3, atol=1e-4,
                      what=f"dot (gpu kv) layer {e}")
+        want.append((_oracle_kv_bf16(kv_want), dot_want))
+
+    m = None if hi.token_mask is None else hi.token_mask.reshape(T)[sample].astype(np.uint8)
+    hcd = cfg.hc_mult * cfg.dim
+    for fused in (False, True):
+        # the fused projection + gate dot: same dot, value columns only
+        if fused:
+            dots_f = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, fused=True)
+            torch.cuda.synchronize()
+            for e in range(cfg.n_layers):
+                kv_o, dot_o = want[e]
+                assert_close(dots_f[e].view(T, -1)[sidx].cpu().numpy(), dot_o, what=f"dot (fused) layer {e}")
+                v_got = bits(wl.fwd._bufs[("value", e)].view(T, -1)[sidx])
+                np.testing.assert_array_equal(v_got, bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])[:, hcd:],
+                                              err_msg=f"fused value columns, layer {e}")
+        outs = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, output=True, fused=fused)
+        torch.cuda.synchronize()
+        for e in range(cfg.n_layers):
+            kv_o, dot_o = want[e]
+            assert_close(wl.fwd._bufs[("dot", e)].view(T, -1)[sidx].cpu().numpy(), dot_o,
+                         what=f"dot (output, fused={fused}) layer {e}")
+            _, out_want = oracle.gate_output(x_bits, kv_o, dot_o, m)
+            out_got = bits(outs[e].view(T, cfg.hc_mult, cfg.dim)[sidx])
+            assert_close(oracle.bf16_bits_to_float(out_got), out_want, what=f"out (fused={fused}) layer {e}")
+            if m is not None:
+                np.testing.assert_array_equal(out_got[m == 0], x_bits[m == 0],
+                                              err_msg=f"masked tokens (fused={fused}), layer {e}")

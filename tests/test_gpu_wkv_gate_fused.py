@@ -1,0 +1,120 @@
+"""engram_wkv_gate (the projection and the gate pre-activation in one pass,
+keys never stored) and engram_gate_residual on the GPU.
+
+The fused value columns are the same arithmetic as engram_wkv's (bit-exact);
+the fused dot matches engram_gate_dot on engram_wkv's keys up to the order of
+the fp32 sums, and the oracle's pipeline within the gate tolerance; the
+residual from a dot is bit-exact against engram_gate_output's, and within
+bf16 rounding of the oracle's output."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_close, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_bf16(rng, shape, std=1.0, mean=0.0):
+    import torch
+
+    return torch.from_numpy((rng.normal(size=shape) * std + mean).astype(np.float32)).to(torch.bfloat16)
+
+
+def _kv_bf16(kv64):
+    import torch
+
+    return torch.from_numpy(kv64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _inputs(rng, T, K, hc, dim, dev):
+    a = _rand_bf16(rng, (T, K), 0.1).to(dev)
+    w = _rand_bf16(rng, ((hc + 1) * dim, K), 0.02).to(dev)
+    x = _rand_bf16(rng, (T, hc, dim)).to(dev)
+    q = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(dev)
+    k = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(dev)
+    return a, w, x, q, k
+
+
+# (T, K, hc, dim): ragged token counts (tails of 44, 1, 1, 232 rows), one-copy and many-copy layouts,
+# the workload's dim with its 100 column tiles
+SHAPES = [(64, 192, 1, 256), (300, 128, 2, 256), (257, 1536, 4, 512), (513, 64, 3, 768), (1, 64, 1, 256),
+          (1000, 1536, 4, 5120)]
+
+
+@pytest.mark.parametrize("T,K,hc,dim", SHAPES)
+def test_wkv_gate_matches_the_unfused_path_and_the_oracle(gpu_device, T, K, hc, dim):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(T * 7 + K + hc * 1000 + dim)
+    a, w, x, q, k = _inputs(rng, T, K, hc, dim, gpu_device)
+    value, dot = g.engram_wkv_gate(a, w, x, q, k, 1e-20)
+    kv = g.engram_wkv(a, w)
+    dot_unfused = g.engram_gate_dot(x, kv, q, k, 1e-20)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(value), bits(kv)[:, hc * dim:], err_msg="value columns")
+    assert_close(dot.cpu().numpy(), dot_unfused.cpu().numpy(), rtol=1e-3, atol=1e-4, what="dot vs unfused")
+    rows = np.arange(T) if T <= 300 else np.unique(np.r_[0, 255, 256, 511, 512, T - 1, rng.integers(0, T, 60)])
+    kv_want = oracle.wkv(bits(a)[rows], bits(w))
+    assert_close(oracle.bf16_bits_to_float(bits(value)[rows]), kv_want[:, hc * dim:], what="value vs oracle")
+    dot_want = oracle.gate_dot(bits(x)[rows], _kv_bf16(kv_want), bits(q), bits(k), 1e-20)
+    assert_close(dot.cpu().numpy()[rows], dot_want, what="dot vs oracle")
+
+
+def test_wkv_gate_strided_value_deterministic_and_workspace_checked(gpu_device):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(21)
+    T, K, hc, dim = 300, 256, 2, 512
+    a, w, x, q, k = _inputs(rng, T, K, hc, dim, gpu_device)
+    wide = torch.full((T, dim + 64), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    value, dot = g.engram_wkv_gate(a, w, x, q, k, 1e-20, value=wide[:, 32:32 + dim])
+    v2, dot2 = g.engram_wkv_gate(a, w, x, q, k, 1e-20)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(wide[:, 32:32 + dim]), bits(v2))
+    assert (bits(wide[:, :32]) == bits(torch.tensor([7.0], dtype=torch.bfloat16))[0]).all()
+    assert (bits(wide[:, 32 + dim:]) == bits(torch.tensor([7.0], dtype=torch.bfloat16))[0]).all()
+    np.testing.assert_array_equal(dot.cpu().numpy().view(np.uint32), dot2.cpu().numpy().view(np.uint32))
+    small = torch.empty(g.engram_wkv_gate_workspace_bytes(T, hc, dim) - 16, dtype=torch.uint8, device=gpu_device)
+    with pytest.raises(g.EngramError, match="workspace"):
+        g.engram_wkv_gate(a, w, x, q, k, 1e-20, workspace=small)
+
+
+def test_wkv_gate_zero_tokens(gpu_device):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=gpu_device)
+    value, dot = g.engram_wkv_gate(z(0, 64), z(512, 64), z(0, 1, 256), z(1, 256), z(1, 256), 1e-20)
+    assert value.shape == (0, 256) and dot.shape == (0, 1)
+
+
+@pytest.mark.parametrize("T,hc,dim,masked", [(5, 4, 256, False), (33, 4, 5120, True), (7, 3, 520, True),
+                                             (1, 1, 8, False)])
+def test_gate_residual_matches_gate_output_bit_for_bit(gpu_device, T, hc, dim, masked):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(T + hc + dim)
+    x = _rand_bf16(rng, (T, hc, dim)).to(gpu_device)
+    kv = _rand_bf16(rng, (T, (hc + 1) * dim), 0.5).to(gpu_device)
+    q = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(gpu_device)
+    k = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(gpu_device)
+    mask = torch.from_numpy(rng.random(T) < 0.6).to(gpu_device) if masked else None
+    dot = torch.empty((T, hc), dtype=torch.float32, device=gpu_device)
+    want = g.engram_gate_output(x, kv, q, k, 1e-20, mask, dot=dot)
+    got = g.engram_gate_residual(x, kv[:, hc * dim:], dot, mask)
+    np.testing.assert_array_equal(bits(got), bits(want))
+    m = None if mask is None else mask.cpu().numpy().astype(np.uint8)
+    _, out_unit = oracle.gate_output(bits(x), bits(kv), dot.cpu().numpy().astype(np.float64), m)
+    assert_close(oracle.bf16_bits_to_float(bits(got)), out_unit, rtol=2.0 ** -8, atol=1e-6, what="residual")
+    # in place: out is x
+    x2 = x.clone()
+    g.engram_gate_residual(x2, kv[:, hc * dim:], dot, mask, out=x2)
+    np.testing.assert_array_equal(bits(x2), bits(want))
