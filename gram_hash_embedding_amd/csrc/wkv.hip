@@ -59,6 +59,9 @@ constexpr int kSchedVmem = 0x010;
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkmcnt0 = 0xC07F;  // lgkmcnt == 0 only (vmcnt 63, expcnt 7 left at their maxima)
+// cache-policy operand of a global load: non-temporal (the line is streamed through L2 instead of
+// displacing the operand panels that the other tiles of the XCD are re-reading)
+constexpr int kNonTemporal = 2;
 // word 3 of a raw buffer resource on gfx9-family targets (32-bit data format, no swizzle)
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -217,8 +220,9 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     // ---- loader waves: wave w fills rows [128w, 128w+128) of both operand slabs, 8 rows per
     // instruction; lane l lands at slot (l & 7) of row 128w + 8q + (l >> 3) and fetches the 16-byte
     // piece the swizzle puts there.  Buffer loads: the tile's rows are a buffer resource (SGPRs) whose
-    // size stops at the last valid row, so rows past M or N read as zero instead of faulting, and a lane
-    // needs only two 32-bit offsets (the swizzle key of row 128w + 8q + r is ((r >> 1) | 4(q & 1))).
+    // size stops at the last valid row, so rows past M or N read as zero instead of faulting; a lane's
+    // offset is one of two 32-bit bases (the swizzle key of row 128w + 8q + r is ((r >> 1) | 4(q & 1)))
+    // plus the instruction's row offset.
     const int ld_r = lane >> 3, ld_slot = lane & 7;
     const int row_bytes = p.K * 2;
     const uint32_t vo_even = static_cast<uint32_t>((wave * 128 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
@@ -242,10 +246,11 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         uint8_t* sw = sa + kOpBytes;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const uint32_t vo = (q & 1) ? vo_odd : vo_even;
-            const uint32_t so = k0b + static_cast<uint32_t>(q * 8 * row_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + q * 8 * 128, 16, vo, so, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, vo, so, 0, 0);
+            // the row offset goes into the VGPR offset: a raw buffer's range check covers the VGPR and
+            // immediate offsets but not the SGPR offset, which carries only the slab's column
+            const uint32_t vo = ((q & 1) ? vo_odd : vo_even) + static_cast<uint32_t>(q * 8 * row_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + q * 8 * 128, 16, vo, k0b, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, vo, k0b, 0, 0);
         }
     };
     auto advance = [&](SlabCursor& c) {  // branch-free: it sits inside the interleaved block
@@ -317,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     // (the product is a bf16 tensor before it is used) and reduced against the stream's matching
     // element: sum(h w key), sum(key^2), sum(h^2) over the lane's 64 columns, then over the two lane
     // halves.
-    // The stream rows of a round (32 tokens x 256 B per wave) come in with full-line direct-to-LDS
-    // loads into the wave's own 8 KB quarter of the exchange region (row r, 16-byte piece p at slot
+    // The stream rows of a round (32 tokens x 256 B per wave) come in with full-line, non-temporal
+    // direct-to-LDS loads into the wave's own 8 KB quarter of the exchange region (row r, 16-byte piece p at slot
     // p ^ ((r >> 1) & 15): the lane-layout reads below are conflict-free) -- scattered 8-byte loads
     // straight into the lane layout touch 32 lines per instruction and measured 0.1 ms slower.  The
     // next round's rows are in flight while a round is reduced.  The loader waves hand their sums to
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                 const int r = 4 * ins + (ll >> 4);
                 const int piece = (ll & 15) ^ ((r >> 1) & 15);
                 const int64_t t = min<int64_t>(m0 + wm * 128 + 32 * i + r, p.M - 1);  // past M: unused
-                __builtin_amdgcn_global_load_lds(xslice + t * xstride + 8 * piece, xl + ins * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(xslice + t * xstride + 8 * piece, xl + ins * 1024, 16, 0, kNonTemporal);
             }
         };
         float res[4][3];
