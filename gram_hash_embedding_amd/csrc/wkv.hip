@@ -5,33 +5,38 @@
 // keys followed by the shared value), fp32 accumulation, one bf16 rounding.
 //
 // Design (gfx950, dense contraction -> MFMA):
-// - Workgroup tile 256 x 256, four waves in a 2 x 2 grid, each wave a
-//   128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 blocks in 256 fp32 accumulators
-//   (AGPRs); one wave per SIMD, one workgroup per CU.  A 128 x 128 wave tile
-//   is what keeps LDS fragment traffic (64 B/clk/CU at full MFMA rate) inside
-//   the LDS bandwidth.
+// - Workgroup tile 256 x 256 and eight waves, two per SIMD: wave (wm, wn) owns
+//   128 tokens x 64 outputs = 4 x 2 MFMA 32x32x16 blocks in 128 fp32
+//   accumulators (AGPRs).  One workgroup per CU.  With one wave per SIMD,
+//   a wave stalled on issuing its direct-to-LDS loads (the CU's address FIFO
+//   fills) left the matrix core idle; with two, the SIMD partner keeps it busy
+//   (main loop 4.17 -> 3.73 ms on the long-prefill shape).  Fragment reads grow
+//   to 96 B/clk/CU at full MFMA rate, under half of the 256 B/clk the LDS
+//   delivers (measured).
 // - Main kernel (K a multiple of 64): persistent, one workgroup per CU walks
 //   its tiles; A and W slabs of 64 along K go HBM/L2 -> LDS with the gfx950
-//   direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging, no
-//   ds_write instructions), two 64 KB stages.  Rows are 128 B with the 16-byte
-//   pieces XOR-swizzled by (row/2) mod 8, so the fragment reads of 16
-//   consecutive rows hit 16 distinct bank groups.
+//   direct-to-LDS loads (buffer_load_dwordx4 ... lds: no VGPR staging, no
+//   ds_write instructions), two 64 KB stages, issued by the four loader waves
+//   (one per SIMD).  Rows are 128 B with the 16-byte pieces XOR-swizzled by
+//   (row/2) mod 8, so the fragment reads of 16 consecutive rows hit 16
+//   distinct bank groups.
 // - One barrier per slab, placed before the last of its four k-steps: it
 //   publishes the next slab (already landed) and frees the current stage for
 //   the slab after next, whose loads are issued right away; the first
-//   fragments of the next slab are then read while the last 16 MFMAs of this
+//   fragments of the next slab are then read while the last 8 MFMAs of this
 //   one run.  The load stream runs across tile boundaries, so the next tile's
 //   first slabs arrive during the current tile's last ones and its epilogue.
-// - Fragment reads of k-step s+1 are interleaved with the 16 MFMAs of step s.
+// - Fragment reads of k-step s+1 are interleaved with the 8 MFMAs of step s.
 // - The MFMA is issued as W-fragment x A-fragment, so each lane ends up with
-//   4 consecutive output columns of one token.  The persistent kernel's
-//   epilogue turns them into full 128-byte-line, non-temporal 16-byte stores
-//   through a per-wave 8 KB LDS region (the remaining 32 KB of the CU's LDS);
-//   scattered 8-byte stores measured 15% slower here.
+//   4 consecutive output columns of one token.  The epilogue turns them into
+//   full 128-byte-line, non-temporal 16-byte stores through a 32 KB LDS
+//   exchange region (the rest of the CU's LDS), written by the four storer
+//   waves; scattered 8-byte stores measured 15% slower.
 // - Tile order: workgroups are dispatched round-robin over the 8 XCDs; tiles
 //   are renumbered so each XCD walks a contiguous run, grouped 8 M-tiles deep,
 //   so the 32 tiles resident on an XCD share A and W panels in its L2.
-// - K not a multiple of 64: a register-staged variant with a zero-filled K tail.
+// - K not a multiple of 64: a register-staged four-wave variant with a
+//   zero-filled K tail.
 #include <type_traits>
 
 #include "common.h"
@@ -78,7 +83,7 @@ struct WkvArgs {
     const uint16_t* x;  // [M, hc, dim] bf16
     const uint16_t* q;  // [hc, dim] bf16
     const uint16_t* k;  // [hc, dim] bf16
-    float* part;        // [hc][dim/128][3][M] fp32: per 128-column slice sum(h w key), sum(key^2), sum(h^2)
+    float* part;        // [hc][dim/64][3][M] fp32: per 64-column slice sum(h w key), sum(key^2), sum(h^2)
     int hc, dim;
 };
 
@@ -170,23 +175,46 @@ __device__ inline void store_tile(const WkvArgs& p, const f32x16 (&acc)[4][4], i
 }
 
 // ============================================================================
-// main kernel: persistent, direct-to-LDS loads (K % 64 == 0)
+// main kernel: persistent, eight waves, direct-to-LDS loads (K % 64 == 0)
 // ============================================================================
+constexpr int kWaves = 8;                      // two per SIMD
+constexpr int kMainThreads = 64 * kWaves;
 constexpr int kOpBytes = BM * BK * 2;          // one operand slab: 256 rows x 128 B = 32 KB
 constexpr int kStageBytes = 2 * kOpBytes;      // A slab + W slab
 constexpr int kExBytes = 64 * 512;             // epilogue exchange: 64 token rows x 256 outputs (bf16)
+constexpr int kXArea = 32 * 128;               // a wave's stream rows for one round: 32 tokens x 64 bf16
+
+// the eight-wave tile: wave (wm, wn) owns tokens [128 wm, +128) x outputs [64 wn, +64), as 4 x 2 MFMA blocks
+__device__ inline void mfma_step8(f32x16 (&acc)[4][2], const bf16x8* fa, const bf16x8* fw) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// the 6 fragment reads of the next k-step spread among the 8 MFMAs of this one
+__device__ inline void interleave_reads8() {
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+}
 
 struct SlabCursor {
     int pid;  // tile being loaded
     int kt;   // slab inside that tile
 };
 
-// The four waves split the memory traffic: waves 0 and 1 issue every global -> LDS load, waves 2 and 3
-// every global store.  A wave's vmcnt counts its loads and stores together, and the slab barrier must
-// wait for the loads; with the roles split, the loaders never have stores outstanding and the storers
-// never wait on vmcnt, so a tile's output drains while the next tile computes.
+// Eight waves, two per SIMD: wave w runs on SIMD w % 4, so each SIMD hosts one loader wave (0-3) and one
+// storer wave (4-7).  A wave that issues its slab's 16 direct-to-LDS loads stalls while the CU's address
+// FIFO drains; its SIMD partner keeps the matrix core busy meanwhile (with one wave per SIMD that stall
+// was a matrix-core bubble, measured at ~20 % of the main loop).  A wave's vmcnt counts its loads and
+// stores together and the slab barrier must wait for the loads, so the roles stay split: loaders never
+// have stores outstanding, storers never wait for slab loads.
 template <bool kGate>
-__global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
+__global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // [stage][A|W][256 rows][128 B] + exchange region: 160 KB, the whole LDS of a CU
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
 
@@ -195,15 +223,14 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-    const int wm = wave >> 1, wn = wave & 1;
-    const bool loader = wave < 2;
+    const int wm = wave & 1, wn = wave >> 1;
+    const bool loader = wave < 4;
     const int KT = p.K / BK;
 
-    // A barrier that publishes LDS: the loaders' own slab loads have landed (vmcnt), every wave's LDS
-    // accesses are done (lgkmcnt).  The empty asm statements keep the compiler from moving memory
-    // accesses across the barrier; no wave waits for its global stores here.
-    auto sync = [&](bool wait_loads) {
-        if (wait_loads && loader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    // A barrier that publishes LDS: every wave's LDS accesses are done (lgkmcnt); the loaders wait for
+    // their slab loads (vmcnt) right before it.  The empty asm statements keep the compiler from moving
+    // memory accesses across the barrier.
+    auto sync = [&]() {
         __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -213,19 +240,19 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     // that round instead of being clustered (and spilled) ahead of the first barrier
     auto sync_epi = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        sync(false);
+        sync();
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- loader waves: wave w fills rows [128w, 128w+128) of both operand slabs, 8 rows per
-    // instruction; lane l lands at slot (l & 7) of row 128w + 8q + (l >> 3) and fetches the 16-byte
+    // ---- loader waves: wave w fills rows [64w, 64w+64) of both operand slabs, 8 rows per
+    // instruction; lane l lands at slot (l & 7) of row 64w + 8q + (l >> 3) and fetches the 16-byte
     // piece the swizzle puts there.  Buffer loads: the tile's rows are a buffer resource (SGPRs) whose
     // size stops at the last valid row, so rows past M or N read as zero instead of faulting; a lane's
-    // offset is one of two 32-bit bases (the swizzle key of row 128w + 8q + r is ((r >> 1) | 4(q & 1)))
+    // offset is one of two 32-bit bases (the swizzle key of row 64w + 8q + r is ((r >> 1) | 4(q & 1)))
     // plus the instruction's row offset.
     const int ld_r = lane >> 3, ld_slot = lane & 7;
     const int row_bytes = p.K * 2;
-    const uint32_t vo_even = static_cast<uint32_t>((wave * 128 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
+    const uint32_t vo_even = static_cast<uint32_t>((wave * 64 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
     const uint32_t vo_odd = vo_even ^ (4u << 4);
     // `live` false (past this workgroup's last slab) still issues the instructions, against an empty
     // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
@@ -242,10 +269,10 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(p.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
         const uint32_t k0b = static_cast<uint32_t>(c.kt * BK * 2);
-        uint8_t* sa = lds + stage * kStageBytes + wave * 128 * 128;
+        uint8_t* sa = lds + stage * kStageBytes + wave * 64 * 128;
         uint8_t* sw = sa + kOpBytes;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < 8; ++q) {
             // the row offset goes into the VGPR offset: a raw buffer's range check covers the VGPR and
             // immediate offsets but not the SGPR offset, which carries only the slab's column
             const uint32_t vo = ((q & 1) ? vo_odd : vo_even) + static_cast<uint32_t>(q * 8 * row_bytes);
@@ -262,53 +289,53 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
     const int g = (lane >> 1) & 7;  // swizzle key of the lane's rows (every block starts at a multiple of 16)
     const int a_row = (wm * 128 + (lane & 31)) * 128;
-    const int w_row = kOpBytes + (wn * 128 + (lane & 31)) * 128;
+    const int w_row = kOpBytes + (wn * 64 + (lane & 31)) * 128;
     auto read_frags = [&](int stage, int kk, bf16x8* fa, bf16x8* fw) {
         const uint8_t* base = lds + stage * kStageBytes;
         const int off = (((2 * kk + (lane >> 5)) ^ g) << 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * 128 + off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + w_row + j * 32 * 128 + off);
+        for (int j = 0; j < 2; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + w_row + j * 32 * 128 + off);
     };
 
-    // ---- epilogue: 4 rounds of 32 tokens per wave through the exchange region (64 rows of 512 B,
-    // 16-byte pieces XOR-swizzled by row: conflict-free 8-byte writes and 16-byte reads), then the
-    // storer waves write whole 128-byte lines, non-temporal (kv is not read again here)
+    // ---- epilogue: 4 rounds; in round i every wave puts its tokens 32i..32i+31 (64 outputs each) into
+    // the exchange region (64 rows of 512 B: row 32 wm + t, 16-byte pieces XOR-swizzled by row), then the
+    // four storer waves write 16 whole rows each with full-line, non-temporal 16-byte stores (kv is not
+    // read again here)
     uint8_t* ex = lds + 2 * kStageBytes;
-    auto epilogue = [&](const f32x16 (&acc)[4][4], int64_t m0, int n0) {
+    auto epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
         // Every lane-derived address below is rebuilt from a freshly computed lane id, so the compiler
-        // cannot hoist the ~80 epilogue addresses out of the tile loop (where they would pin VGPRs for
-        // the whole kernel and spill; a scratch reload would also make a storer wave wait for its
-        // outstanding stores).
+        // cannot hoist the epilogue addresses out of the tile loop (where they would pin VGPRs for the
+        // whole kernel).
         const int l = lane_id();
-        const int key = (wm * 32 + (l & 31)) & 31;
+        const int key = l & 31;
         const uint32_t wbase = static_cast<uint32_t>((wm * 32 + (l & 31)) * 512 + (l >> 5) * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int chunk = wn * 16 + 4 * j + gq;  // 16-byte piece of the 512-byte row
+                    const int chunk = wn * 8 + 4 * j + gq;  // 16-byte piece of the 512-byte row
                     const u32x2 v = {pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1])),
                                      pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]))};
                     *reinterpret_cast<u32x2*>(ex + wbase + ((chunk ^ key) << 4)) = v;
                 }
             sync_epi();
             if (!loader) {
-                const int half = wave - 2;  // token half wm = half of the tile
+                const int s = wave - 4;  // exchange rows [16s, 16s + 16)
                 const int ls = lane_id();
                 const int chunk = ls & 31, hi = ls >> 5;
-                uint16_t* dst = p.kv + (m0 + half * 128 + 32 * i + hi) * p.ld_out + (n0 - p.out_col0) + chunk * 8;
                 const bool col_ok = n0 + chunk * 8 < p.N;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int rr = half * 32 + 2 * q + hi;  // exchange row
+                for (int q = 0; q < 8; ++q) {
+                    const int rr = 16 * s + 2 * q + hi;  // exchange row: token half rr / 32, token rr % 32
                     const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 512 + ((chunk ^ (rr & 31)) << 4));
-                    const int64_t m = m0 + half * 128 + 32 * i + 2 * q + hi;
+                    const int64_t m = m0 + (rr >> 5) * 128 + 32 * i + (rr & 31);
                     if (m < p.M && col_ok)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 2 * q * p.ld_out));
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + (n0 - p.out_col0) + chunk * 8));
                 }
             }
             sync_epi();
@@ -316,29 +343,29 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
     };
 
     // ---- fused gate epilogue of a key tile: no stores of the product.  The tile's 256 columns lie in
-    // one copy c; wave (wm, wn) owns the 128-column slice s = 2 * (tile's slice) + wn.  Lane l holds,
-    // per round i, token 32i + l%32 of the wave's 128 tokens and 64 of the slice's columns (4
-    // consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is rounded to bf16
-    // (the product is a bf16 tensor before it is used) and reduced against the stream's matching
-    // element: sum(h w key), sum(key^2), sum(h^2) over the lane's 64 columns, then over the two lane
-    // halves.
-    // The stream rows of a round (32 tokens x 256 B per wave) come in with full-line, non-temporal
-    // direct-to-LDS loads into the wave's own 8 KB quarter of the exchange region (row r, 16-byte piece p at slot
-    // p ^ ((r >> 1) & 15): the lane-layout reads below are conflict-free) -- scattered 8-byte loads
-    // straight into the lane layout touch 32 lines per instruction and measured 0.1 ms slower.  The
-    // next round's rows are in flight while a round is reduced.  The loader waves hand their sums to
-    // the storer waves through LDS (one barrier), so they never have stores outstanding.
-    auto gate_epilogue = [&](const f32x16 (&acc)[4][4], int64_t m0, int n0) {
+    // one copy c; wave (wm, wn) owns the 64-column slice s = (n0 - c dim) / 64 + wn of that copy and
+    // tokens 128 wm .. 128 wm + 127.  Lane l holds, per round i, token 32i + l%32 and 32 of the slice's
+    // columns (4 consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is
+    // rounded to bf16 (the product is a bf16 tensor before it is used) and reduced against the stream's
+    // matching element: sum(h w key), sum(key^2), sum(h^2) over the lane's columns, then over the two
+    // lane halves; per (copy, slice, token) the three sums go to the workspace.
+    // Stream rows come in with full-line, non-temporal direct-to-LDS loads issued by the storer waves
+    // (which have no slab loads to wait for), each for its own 4 KB area of the exchange region and for
+    // the area of its SIMD partner (loader wave w - 4: same tokens, the slice 128 columns to the left):
+    // row t of an area is token t's 128 bytes, 16-byte piece p at slot p ^ ((t >> 1) & 7), so the
+    // lane-layout reads below are conflict-free.  Loader waves hand their sums to their partner, which
+    // stores both, so loaders never have stores outstanding.
+    auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
         const int l = lane_id();
         const int c = n0 / p.dim;
-        const int col0 = n0 - c * p.dim + wn * 128;  // the wave's slice, in the copy's columns
-        const int slice = col0 / 128;
-        const int slices = p.dim / 128;
+        const int colw = n0 - c * p.dim;           // the tile's first column in the copy
+        const int col0 = colw + wn * 64;           // this wave's slice
+        const int slices = p.dim / 64;
         const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
         const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
-        float wgt[4][4][4];  // q * k (exact in fp32) for the lane's 64 columns
+        float wgt[2][4][4];  // q * k (exact in fp32) for the lane's 32 columns
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + 32 * j + 8 * gq);
@@ -348,41 +375,45 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                 wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
                 wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
             }
-        uint8_t* xl = ex + wave * 8192;
-        const uint16_t* xslice = p.x + static_cast<int64_t>(c) * p.dim + col0;
+        uint8_t* xl = ex + wave * kXArea;
         const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
-        auto dma_x = [&](int i) {  // round i's 32 rows: 4 rows of 16 pieces per instruction
+        // storer wave: round i's 32 rows of its own area (v = 0) and its partner's (v = 1), 8 rows of
+        // 8 pieces per instruction
+        auto dma_x = [&](int i) {
             const int ll = lane_id();
 #pragma unroll
-            for (int ins = 0; ins < 8; ++ins) {
-                const int r = 4 * ins + (ll >> 4);
-                const int piece = (ll & 15) ^ ((r >> 1) & 15);
-                const int64_t t = min<int64_t>(m0 + wm * 128 + 32 * i + r, p.M - 1);  // past M: unused
-                __builtin_amdgcn_global_load_lds(xslice + t * xstride + 8 * piece, xl + ins * 1024, 16, 0, kNonTemporal);
+            for (int v = 0; v < 2; ++v) {
+                const int ow = wave - 4 * v;  // owner wave of the area
+                const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
+#pragma unroll
+                for (int ins = 0; ins < 4; ++ins) {
+                    const int r = 8 * ins + (ll >> 3);
+                    const int piece = (ll & 7) ^ ((r >> 1) & 7);
+                    const int64_t t = min<int64_t>(m0 + (ow & 1) * 128 + 32 * i + r, p.M - 1);  // past M: unused
+                    __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece, ex + ow * kXArea + ins * 1024, 16,
+                                                     0, kNonTemporal);
+                }
             }
         };
         float res[4][3];
-        dma_x(0);
+        if (!loader) dma_x(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            u32x2 xr[4][4];
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-            asm volatile("" ::: "memory");
+            if (!loader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            sync_epi();  // round i's stream rows are in
+            u32x2 xr[2][4];
             {
                 const int rr = l & 31, h = l >> 5;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq)
                         xr[j][gq] = *reinterpret_cast<const u32x2*>(
-                            xl + rr * 256 + (((4 * j + gq) ^ ((rr >> 1) & 15)) << 4) + h * 8);
+                            xl + rr * 128 + (((4 * j + gq) ^ ((rr >> 1) & 7)) << 4) + h * 8);
             }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-            asm volatile("" ::: "memory");
-            if (i < 3) dma_x(i + 1);  // the quarter has been read: refill it
             float hwk = 0.f, kk = 0.f, hh = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const uint32_t k01 = pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1]));
@@ -400,9 +431,11 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
             res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
             res[i][2] = hh + __shfl_xor(hh, 32, 64);
+            sync_epi();  // every wave has read round i's rows: the areas can be refilled
+            if (!loader && i < 3) dma_x(i + 1);
         }
-        // hand-over: a loader wave (tokens 0-127 of the tile) leaves its sums in its own quarter, laid
-        // out [round][sum][token]; the storer wave of the same slice writes them with lanes 32-63
+        // hand-over: a loader wave leaves its sums in its own area, laid out [round][sum][token]; its
+        // partner writes them with lanes 32-63 and its own with lanes 0-31
         if (loader && l < 32) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -412,8 +445,9 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
         sync_epi();
         if (!loader) {
             const int ls = lane_id();
-            const float* partner = reinterpret_cast<const float*>(ex + (wave - 2) * 8192);
-            const int64_t tbase = m0 + (ls < 32 ? 128 : 0) + (ls & 31);
+            const float* partner = reinterpret_cast<const float*>(ex + (wave - 4) * kXArea);
+            const int64_t tbase = m0 + wm * 128 + (ls & 31);
+            const int slice = (ls < 32 ? col0 : col0 - 128) / 64;
             float* out = p.part + (static_cast<int64_t>(c) * slices + slice) * 3 * p.M;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -425,14 +459,15 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
                 }
             }
         }
+        sync_epi();  // the partner's sums are read before the areas are refilled
     };
 
     if (static_cast<int>(blockIdx.x) >= tiles) return;
     const int total_slabs_mine = ((tiles - 1 - static_cast<int>(blockIdx.x)) / G + 1) * KT;
 
     // The tile loop, instantiated separately for loader and storer waves (the branch is per wave, the
-    // barrier count per tile is the same in both).  In the loader instance the 32 loads of the slab
-    // after next are spread among the last 16 MFMAs of the current slab.
+    // barrier count per tile is the same in both).  In the loader instance the 16 loads of the slab
+    // after next are spread among the last 8 MFMAs of the current slab.
     auto run = [&](auto loader_tag) {
         constexpr bool kLoader = decltype(loader_tag)::value;
         int pid = blockIdx.x;
@@ -448,57 +483,56 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_dma(WkvArgs p) {
             ++issued;
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
-        sync(false);
+        sync();
 
-        f32x16 acc[4][4];
-        bf16x8 fa0[4], fw0[4], fa1[4], fw1[4];
+        f32x16 acc[4][2];
+        bf16x8 fa0[4], fw0[2], fa1[4], fw1[2];
         read_frags(0, 0, fa0, fw0);
         int stage = 0;
         for (; pid < tiles; pid += G) {
             int tm, tn;
             tile_coords(p, pid, tm, tn);
-            zero(acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
             for (int kt = 0; kt < KT; ++kt) {
                 read_frags(stage, 1, fa1, fw1);
-                mfma_step(acc, fa0, fw0);
-                interleave_reads();
+                mfma_step8(acc, fa0, fw0);
+                interleave_reads8();
                 read_frags(stage, 2, fa0, fw0);
-                mfma_step(acc, fa1, fw1);
-                interleave_reads();
+                mfma_step8(acc, fa1, fw1);
+                interleave_reads8();
                 read_frags(stage, 3, fa1, fw1);
-                mfma_step(acc, fa0, fw0);
-                interleave_reads();
+                mfma_step8(acc, fa0, fw0);
+                interleave_reads8();
                 // the next slab has landed and this stage is no longer read: publish one, refill the other
                 if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-                sync(false);
+                sync();
                 // The next slab's first fragments (the next tile's, at the end of a tile; harmless
-                // stale reads after the last one) are read under the last 16 MFMAs of this slab.
+                // stale reads after the last one) are read under the last 8 MFMAs of this slab.
                 read_frags(stage ^ 1, 0, fa0, fw0);
                 if (kLoader) {
                     issue_slab(ld, stage, issued < total_slabs_mine);  // slab after next into the freed stage
                     advance(ld);
                     ++issued;
-                    mfma_step(acc, fa1, fw1);
-                    // fragment reads first (the compiler keeps them ahead of the LDS-writing loads),
-                    // then the 32 loads three or two at a time between the remaining MFMAs
+                    mfma_step8(acc, fa1, fw1);
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+                    for (int s6 = 0; s6 < 6; ++s6) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
                         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     }
 #pragma unroll
-                    for (int s8 = 0; s8 < 8; ++s8) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 3, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    }
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
+                    for (int s2 = 0; s2 < 2; ++s2) {
                         __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
                         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     }
                 } else {
-                    mfma_step(acc, fa1, fw1);
-                    interleave_reads();
+                    mfma_step8(acc, fa1, fw1);
+                    interleave_reads8();
                 }
                 stage ^= 1;
             }
@@ -652,7 +686,7 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     const int64_t tiles = tiles_m * p.tiles_n;
     if (K % BK == 0) {
         const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-        hipLaunchKernelGGL(wkv_kernel_dma<false>, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+        hipLaunchKernelGGL(wkv_kernel<false>, dim3(grid), dim3(kMainThreads), 0, as_stream(stream), p);
     } else {
         hipLaunchKernelGGL(wkv_kernel_staged, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
                            as_stream(stream), p);
@@ -662,7 +696,7 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
 
 extern "C" int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim) {
     if (T < 0 || hc < 1 || hc > 64 || dim < 256 || dim % 256 != 0) return -1;
-    return static_cast<int64_t>(hc) * (dim / 128) * 3 * T * static_cast<int64_t>(sizeof(float));
+    return static_cast<int64_t>(hc) * (dim / 64) * 3 * T * static_cast<int64_t>(sizeof(float));
 }
 
 extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
@@ -709,13 +743,13 @@ extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint1
     p.tiles_m = static_cast<int>(tiles_m);
     const int64_t tiles = tiles_m * p.tiles_n;
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-    hipLaunchKernelGGL(wkv_kernel_dma<true>, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    hipLaunchKernelGGL(wkv_kernel<true>, dim3(grid), dim3(kMainThreads), 0, as_stream(stream), p);
     int rc = check_launch("engram_wkv_gate");
     if (rc != ENGRAM_OK) return rc;
     const int64_t blocks = (T * hc + 255) / 256;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");
     hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
-                       p.part, dot, T, hc, dim / 128, eps, 1.0f / static_cast<float>(dim),
+                       p.part, dot, T, hc, dim / 64, eps, 1.0f / static_cast<float>(dim),
                        static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim))));
     return check_launch("engram_wkv_gate (finalize)");
 }
