@@ -350,16 +350,43 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // matching element: sum(h w key), sum(key^2), sum(h^2) over the lane's columns, then over the two
     // lane halves; per (copy, slice, token) the three sums go to the workspace.
     // Stream rows come in with full-line, non-temporal direct-to-LDS loads issued by the storer waves
-    // (which have no slab loads to wait for), each for its own 4 KB area of the exchange region and for
-    // the area of its SIMD partner (loader wave w - 4: same tokens, the slice 128 columns to the left):
-    // row t of an area is token t's 128 bytes, 16-byte piece p at slot p ^ ((t >> 1) & 7), so the
-    // lane-layout reads below are conflict-free.  Loader waves hand their sums to their partner, which
-    // stores both, so loaders never have stores outstanding.
-    auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
+    // (which have no slab loads to wait for), each for its own 4 KB area of a round's 32 KB region and
+    // for the area of its SIMD partner (loader wave w - 4: same tokens, the slice 128 columns to the
+    // left): row t of an area is token t's 128 bytes, 16-byte piece p at slot p ^ ((t >> 1) & 7), so
+    // the lane-layout reads below are conflict-free.  The rows are fetched ahead so that the epilogue
+    // rarely waits for HBM: round 0 into the exchange region while the tile's main loop runs, rounds 1
+    // and 2 into the stage the tile's last slab frees (the next tile's second slab is loaded into it
+    // only after the epilogue), round 3 into the exchange region once round 0 is reduced.  Loader waves
+    // hand their sums to their partner, which stores both, so loaders never have stores outstanding.
+    auto round_region = [&](int i, int free_stage) -> uint8_t* {
+        return (i == 1 || i == 2) ? lds + free_stage * kStageBytes + (i - 1) * kExBytes : ex;
+    };
+    // storer wave: round i's 32 rows of its own area (v = 0) and its partner's (v = 1) into `region`,
+    // 8 rows of 8 pieces per instruction (8 loads)
+    auto dma_x = [&](int64_t m0, int n0, int i, uint8_t* region) {
+        const int ll = lane_id();
+        const int c = n0 / p.dim;
+        const int colw = n0 - c * p.dim;
+        const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int ow = wave - 4 * v;  // owner wave of the area
+            const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
+#pragma unroll
+            for (int ins = 0; ins < 4; ++ins) {
+                const int r = 8 * ins + (ll >> 3);
+                const int piece = (ll & 7) ^ ((r >> 1) & 7);
+                const int64_t t = min<int64_t>(m0 + (ow & 1) * 128 + 32 * i + r, p.M - 1);  // past M: unused
+                __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece, region + ow * kXArea + ins * 1024, 16,
+                                                 0, kNonTemporal);
+            }
+        }
+    };
+    // On entry the storers have rounds 0, 1, 2 in flight, in that order, 8 loads each.
+    auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0, int free_stage) {
         const int l = lane_id();
         const int c = n0 / p.dim;
-        const int colw = n0 - c * p.dim;           // the tile's first column in the copy
-        const int col0 = colw + wn * 64;           // this wave's slice
+        const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice
         const int slices = p.dim / 64;
         const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
         const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
@@ -375,32 +402,20 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
                 wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
             }
-        uint8_t* xl = ex + wave * kXArea;
-        const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
-        // storer wave: round i's 32 rows of its own area (v = 0) and its partner's (v = 1), 8 rows of
-        // 8 pieces per instruction
-        auto dma_x = [&](int i) {
-            const int ll = lane_id();
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const int ow = wave - 4 * v;  // owner wave of the area
-                const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
-#pragma unroll
-                for (int ins = 0; ins < 4; ++ins) {
-                    const int r = 8 * ins + (ll >> 3);
-                    const int piece = (ll & 7) ^ ((r >> 1) & 7);
-                    const int64_t t = min<int64_t>(m0 + (ow & 1) * 128 + 32 * i + r, p.M - 1);  // past M: unused
-                    __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece, ex + ow * kXArea + ins * 1024, 16,
-                                                     0, kNonTemporal);
-                }
-            }
-        };
         float res[4][3];
-        if (!loader) dma_x(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (!loader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            // loads issued after round i's: rounds 1 and 2 (before round 0 is reduced), round 3 after it
+            if (!loader) {
+                if (i < 2)
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+                else if (i == 2)
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+                else
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            }
             sync_epi();  // round i's stream rows are in
+            const uint8_t* xl = round_region(i, free_stage) + wave * kXArea;
             u32x2 xr[2][4];
             {
                 const int rr = l & 31, h = l >> 5;
@@ -431,11 +446,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
             res[i][2] = hh + __shfl_xor(hh, 32, 64);
-            sync_epi();  // every wave has read round i's rows: the areas can be refilled
-            if (!loader && i < 3) dma_x(i + 1);
+            if (i == 0) {
+                sync_epi();  // every wave has read round 0's rows: the exchange region takes round 3
+                if (!loader) dma_x(m0, n0, 3, ex);
+            }
         }
-        // hand-over: a loader wave leaves its sums in its own area, laid out [round][sum][token]; its
-        // partner writes them with lanes 32-63 and its own with lanes 0-31
+        // hand-over: a loader wave leaves its sums in its own area of the exchange region (round 3 has
+        // been read by every wave once the barrier below has passed... so the sums go in after it)
+        sync_epi();
+        uint8_t* xl = ex + wave * kXArea;
         if (loader && l < 32) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -459,7 +478,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 }
             }
         }
-        sync_epi();  // the partner's sums are read before the areas are refilled
+        sync_epi();  // the partner's sums are read before the region is reused
     };
 
     if (static_cast<int>(blockIdx.x) >= tiles) return;
@@ -489,57 +508,95 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         bf16x8 fa0[4], fw0[2], fa1[4], fw1[2];
         read_frags(0, 0, fa0, fw0);
         int stage = 0;
+        // One slab: four k-steps of 8 MFMAs, one barrier before the last.  kDefer (the last slab of a
+        // fused key tile): the freed stage is kept for the epilogue's stream rows -- the loaders skip the
+        // slab after next (issued after the epilogue) and the storers fetch rounds 1 and 2 into it.
+        auto slab = [&](auto defer_tag, int64_t m0, int n0) {
+            constexpr bool kDefer = decltype(defer_tag)::value;
+            read_frags(stage, 1, fa1, fw1);
+            mfma_step8(acc, fa0, fw0);
+            interleave_reads8();
+            read_frags(stage, 2, fa0, fw0);
+            mfma_step8(acc, fa1, fw1);
+            interleave_reads8();
+            read_frags(stage, 3, fa1, fw1);
+            mfma_step8(acc, fa0, fw0);
+            interleave_reads8();
+            // the next slab has landed and this stage is no longer read: publish one, refill the other
+            if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            sync();
+            // The next slab's first fragments (the next tile's, at the end of a tile; harmless stale
+            // reads after the last one) are read under the last 8 MFMAs of this slab.
+            read_frags(stage ^ 1, 0, fa0, fw0);
+            if (kLoader && !kDefer) {
+                issue_slab(ld, stage, issued < total_slabs_mine);  // slab after next into the freed stage
+                advance(ld);
+                ++issued;
+                mfma_step8(acc, fa1, fw1);
+#pragma unroll
+                for (int s6 = 0; s6 < 6; ++s6) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                }
+            } else if (!kLoader && kDefer) {
+                dma_x(m0, n0, 1, round_region(1, stage));
+                dma_x(m0, n0, 2, round_region(2, stage));
+                mfma_step8(acc, fa1, fw1);
+#pragma unroll
+                for (int s6 = 0; s6 < 6; ++s6) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                }
+            } else {
+                mfma_step8(acc, fa1, fw1);
+                interleave_reads8();
+            }
+            stage ^= 1;
+        };
         for (; pid < tiles; pid += G) {
             int tm, tn;
             tile_coords(p, pid, tm, tn);
+            const int64_t m0 = static_cast<int64_t>(tm) * BM;
+            const int n0 = tn * BN;
+            const bool key_tile = kGate && n0 < p.out_col0;
+            auto zero_acc = [&]() {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-            for (int kt = 0; kt < KT; ++kt) {
-                read_frags(stage, 1, fa1, fw1);
-                mfma_step8(acc, fa0, fw0);
-                interleave_reads8();
-                read_frags(stage, 2, fa0, fw0);
-                mfma_step8(acc, fa1, fw1);
-                interleave_reads8();
-                read_frags(stage, 3, fa1, fw1);
-                mfma_step8(acc, fa0, fw0);
-                interleave_reads8();
-                // the next slab has landed and this stage is no longer read: publish one, refill the other
-                if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-                sync();
-                // The next slab's first fragments (the next tile's, at the end of a tile; harmless
-                // stale reads after the last one) are read under the last 8 MFMAs of this slab.
-                read_frags(stage ^ 1, 0, fa0, fw0);
-                if (kLoader) {
-                    issue_slab(ld, stage, issued < total_slabs_mine);  // slab after next into the freed stage
+                        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            };
+            if (key_tile) {
+                // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
+                if (!kLoader) dma_x(m0, n0, 0, ex);
+                zero_acc();
+                for (int kt = 0; kt < KT - 1; ++kt) slab(std::false_type{}, m0, n0);
+                const int free_stage = stage;
+                slab(std::true_type{}, m0, n0);
+                gate_epilogue(acc, m0, n0, free_stage);
+                if (kLoader) {  // the slab after next, held back while the epilogue used its stage
+                    issue_slab(ld, free_stage, issued < total_slabs_mine);
                     advance(ld);
                     ++issued;
-                    mfma_step8(acc, fa1, fw1);
-#pragma unroll
-                    for (int s6 = 0; s6 < 6; ++s6) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    }
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    }
-                } else {
-                    mfma_step8(acc, fa1, fw1);
-                    interleave_reads8();
                 }
-                stage ^= 1;
+            } else {
+                zero_acc();
+                for (int kt = 0; kt < KT; ++kt) slab(std::false_type{}, m0, n0);
+                epilogue(acc, m0, n0);
             }
-            if (kGate && tn * BN < p.out_col0)
-                gate_epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
-            else
-                epilogue(acc, static_cast<int64_t>(tm) * BM, tn * BN);
         }
     };
     if (loader)
