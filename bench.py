@@ -139,7 +139,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload (1..5); 3 = long prefill")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the CPU oracle baseline sample")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a counter reference for rocprofv3)")
