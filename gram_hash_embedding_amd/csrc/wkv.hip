@@ -83,7 +83,7 @@ struct WkvArgs {
     const uint16_t* x;  // [M, hc, dim] bf16
     const uint16_t* q;  // [hc, dim] bf16
     const uint16_t* k;  // [hc, dim] bf16
-    float* part;        // [hc][dim/64][3][M] fp32: per 64-column slice sum(h w key), sum(key^2), sum(h^2)
+    float* part;        // [hc][dim/128][3][M] fp32: per 128-column slice pair sum(h w key), sum(key^2), sum(h^2)
     int hc, dim;
 };
 
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // columns (4 consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is
     // rounded to bf16 (the product is a bf16 tensor before it is used) and reduced against the stream's
     // matching element: sum(h w key), sum(key^2), sum(h^2) over the lane's columns, then over the two
-    // lane halves; per (copy, slice, token) the three sums go to the workspace.
+    // lane halves; per (copy, pair of slices, token) the three sums go to the workspace.
     // Stream rows come in with full-line, non-temporal direct-to-LDS loads issued by the storer waves
     // (which have no slab loads to wait for), each for its own 4 KB area of a round's 32 KB region and
     // for the area of its SIMD partner (loader wave w - 4: same tokens, the slice 128 columns to the
@@ -387,7 +387,6 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         const int l = lane_id();
         const int c = n0 / p.dim;
         const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice
-        const int slices = p.dim / 64;
         const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
         const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
         float wgt[2][4][4];  // q * k (exact in fp32) for the lane's 32 columns
@@ -463,18 +462,22 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         }
         sync_epi();
         if (!loader) {
+            // the storer adds its partner's sums (slice 64 (wn - 2) of the tile) to its own (slice 64 wn):
+            // one value per (copy, 128-column slice pair, token), always summed in this order
             const int ls = lane_id();
-            const float* partner = reinterpret_cast<const float*>(ex + (wave - 4) * kXArea);
-            const int64_t tbase = m0 + wm * 128 + (ls & 31);
-            const int slice = (ls < 32 ? col0 : col0 - 128) / 64;
-            float* out = p.part + (static_cast<int64_t>(c) * slices + slice) * 3 * p.M;
+            if (ls < 32) {
+                const float* partner = reinterpret_cast<const float*>(ex + (wave - 4) * kXArea);
+                const int64_t tbase = m0 + wm * 128 + ls;
+                const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
+                float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = tbase + 32 * i;
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t t = tbase + 32 * i;
 #pragma unroll
-                for (int q = 0; q < 3; ++q) {
-                    const float v = ls < 32 ? res[i][q] : partner[(i * 3 + q) * 32 + (ls & 31)];
-                    if (t < p.M) out[q * p.M + t] = v;
+                    for (int q = 0; q < 3; ++q) {
+                        const float v = res[i][q] + partner[(i * 3 + q) * 32 + ls];
+                        if (t < p.M) out[q * p.M + t] = v;
+                    }
                 }
             }
         }
@@ -753,7 +756,7 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
 
 extern "C" int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim) {
     if (T < 0 || hc < 1 || hc > 64 || dim < 256 || dim % 256 != 0) return -1;
-    return static_cast<int64_t>(hc) * (dim / 64) * 3 * T * static_cast<int64_t>(sizeof(float));
+    return static_cast<int64_t>(hc) * (dim / 128) * 3 * T * static_cast<int64_t>(sizeof(float));
 }
 
 extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
@@ -806,7 +809,7 @@ extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint1
     const int64_t blocks = (T * hc + 255) / 256;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");
     hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
-                       p.part, dot, T, hc, dim / 64, eps, 1.0f / static_cast<float>(dim),
+                       p.part, dot, T, hc, dim / 128, eps, 1.0f / static_cast<float>(dim),
                        static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim))));
     return check_launch("engram_wkv_gate (finalize)");
 }

@@ -203,7 +203,7 @@ int engram_gate_output(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, con
  *   kv       = bf16(a * w^T)  (fp32 accumulation), Nout = (hc+1)*dim
  *   value    = kv[:, hc*dim : (hc+1)*dim]                       -> value
  *   dot[t,c] = as engram_gate_dot, with key = kv[t, c*dim : (c+1)*dim]  -> dot
- * The sums of a (token, copy) are formed per 64-column slice (fp32) in the
+ * The sums of a (token, copy) are formed per 128 columns (fp32) in the
  * projection, kept in `workspace`, and added in slice order by a second
  * kernel on the same stream, so results are deterministic.
  *
@@ -250,7 +250,7 @@ int engram_gate_residual(const uint16_t* x, const uint16_t* value, int64_t ld_va
                          const uint8_t* token_mask, uint16_t* out, int64_t T, int32_t hc, int32_t dim,
                          void* stream);
 
-/* Bytes of workspace engram_wkv_gate needs for T tokens (hc * dim/64 * 3 * T
+/* Bytes of workspace engram_wkv_gate needs for T tokens (hc * dim/128 * 3 * T
  * floats), or -1 if hc or dim is outside the limits above. */
 int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim);
 

@@ -136,8 +136,8 @@ def test_gate_output_pointer_checks():
 
 def test_wkv_gate_workspace_bytes():
     L = g.lib()
-    assert L.engram_wkv_gate_workspace_bytes(65536, 4, 5120) == 4 * 80 * 3 * 65536 * 4
-    assert L.engram_wkv_gate_workspace_bytes(1, 1, 256) == 1 * 4 * 3 * 1 * 4
+    assert L.engram_wkv_gate_workspace_bytes(65536, 4, 5120) == 4 * 40 * 3 * 65536 * 4
+    assert L.engram_wkv_gate_workspace_bytes(1, 1, 256) == 1 * 2 * 3 * 1 * 4
     assert L.engram_wkv_gate_workspace_bytes(0, 4, 256) == 0
     for T, hc, dim in [(-1, 4, 256), (10, 0, 256), (10, 65, 256), (10, 4, 320), (10, 4, 128)]:
         assert L.engram_wkv_gate_workspace_bytes(T, hc, dim) == -1
@@ -148,12 +148,12 @@ def test_wkv_gate_workspace_bytes():
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(K=96), 1, "K=96"), (dict(K=0), 1, "K=0"), (dict(hc=0), 1, "hc=0"), (dict(dim=320), 1, "dim=320"),
     (dict(dim=128), 1, "dim=128"), (dict(ld_value=200), 1, "ld_value"), (dict(ld_value=260), 1, "ld_value"),
-    (dict(ws_bytes=10 * 4 * 4 * 3 * 4 - 4), 2, "workspace"), (dict(a=None), 1, "null"), (dict(ws=None), 1, "null"),
+    (dict(ws_bytes=10 * 4 * 2 * 3 * 4 - 4), 2, "workspace"), (dict(a=None), 1, "null"), (dict(ws=None), 1, "null"),
     (dict(value=ctypes.c_void_p(0x100008)), 1, "misaligned"), (dict(ws=ctypes.c_void_p(0x100004)), 1, "misaligned"),
 ])
 def test_wkv_gate_validation(kw, status, msg):
     a = dict(a=FAKE, w=FAKE, x=FAKE, q=FAKE, k=FAKE, value=FAKE, ld_value=256, dot=FAKE, ws=FAKE,
-             ws_bytes=10 * 4 * 4 * 3 * 4, T=10, K=128, hc=4, dim=256)
+             ws_bytes=10 * 4 * 2 * 3 * 4, T=10, K=128, hc=4, dim=256)
     a.update(kw)
     rc = g.lib().engram_wkv_gate(a["a"], a["w"], a["x"], a["q"], a["k"], 1e-20, a["value"], a["ld_value"], a["dot"],
                                  a["ws"], a["ws_bytes"], a["T"], a["K"], a["hc"], a["dim"], None)
