@@ -9,10 +9,16 @@ The default workload is the long prefill: one sequence of 65,536 tokens, one
 engram layer with the released 384,006,168-row fp8 table (24.6 GB, D = 64,
 8 hash heads, n-grams up to 4), dim 5120, hc_mult 4.
 
-One step is timed four ways, each its own loop of `--steps` steps:
+The table is resident twice: in the pages' layout (fp8 rows and fp32 scales in
+two tensors) and packed (engram_pack_table: one 2*D-byte record per row, the
+row's scales in its own line).  The gathered values are identical; `--table`
+picks which layout the `value` path reads (default: packed).
+
+One step is timed five ways, each its own loop of `--steps` steps:
   fused           the path with the projection and the gate pre-activation in
                   one entry point (keys reduced in the projection, never
                   stored) -- this is `value` and `ms_per_step`
+  fused_*_table   the same on the other table layout
   unfused         the same path as four entry points (kv written, then read)
   module_fused    the whole module: fused path + gate, mask and residual
   module_unfused  the whole module: unfused projection + fused dot/gate/residual
@@ -141,6 +147,9 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=3, help="workload (1..5); 3 = long prefill")
     ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--table", choices=("packed", "pages"), default="packed",
+                    help="table layout of the `value` path: one record per row (engram_pack_table) or the pages' "
+                         "two tensors; the other is timed beside it")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a counter reference for rocprofv3)")
     args = ap.parse_args(argv)
@@ -178,16 +187,17 @@ def main(argv=None):
         return 2
     log(f"building workload {cfg.name} ...")
     t_build = time.perf_counter()
-    wl = sw.build(cfg, device=dev)
+    wl = sw.build(cfg, device=dev, packed=True)
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
     fwd = wl.fwd
     T = cfg.tokens
 
-    def loop(fused, output):
+    def loop(fused, output, packed):
         """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
         def step(events=None):
-            fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output, fused=fused)
+            fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output, fused=fused,
+                     packed=packed)
 
         for _ in range(args.warmup):
             step()
@@ -200,14 +210,21 @@ def main(argv=None):
         return (time.perf_counter() - t0) / args.steps, events
 
     # The path itself (hash -> per layer gather+dequant -> projection -> gate pre-activation), fused
-    # (engram_wkv_gate: keys reduced in the projection) -- the `value` -- and as four separate entry
-    # points; then the whole module (gate, mask, residual -> output stream) both ways.
+    # (engram_wkv_gate: keys reduced in the projection) on the table layout `--table` picks -- the
+    # `value` -- and on the other layout; as four separate entry points; then the whole module (gate,
+    # mask, residual -> output stream) both ways.
+    main_packed = args.table == "packed"
     paths = {}
     kern_events = {}
-    for name, fused, output in (("fused", True, False), ("unfused", False, False),
-                                ("module_fused", True, True), ("module_unfused", False, True)):
-        sec, ev = loop(fused, output)
-        paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1)}
+    for name, fused, output, packed in (("fused", True, False, main_packed),
+                                        ("fused_" + ("pages_table" if main_packed else "packed_table"), True, False,
+                                         not main_packed),
+                                        ("unfused", False, False, main_packed),
+                                        ("module_fused", True, True, main_packed),
+                                        ("module_unfused", False, True, main_packed)):
+        sec, ev = loop(fused, output, packed)
+        paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
+                       "table": "packed" if packed else "pages"}
         for k, v in ev.items():
             kern_events.setdefault(k, v)  # the first loop that runs a kernel times it
     sec_main = paths["fused"]["ms_per_step"] / 1e3
@@ -221,9 +238,10 @@ def main(argv=None):
     E = cfg.n_layers
     W_bytes = 2 * cfg.K * cfg.n_out
     kern["hash"]["GB/s"] = round(T * algo["hash_bytes"] / (kern["hash"]["avg_us"] * 1e3), 1)
-    g = kern["gather_dequant"]
-    g["GB/s"] = round(T * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
-    g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
+    for name in ("gather_dequant", "gather_dequant_packed"):
+        g = kern[name]
+        g["GB/s"] = round(T * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
+        g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
     for name in ("wkv", "wkv_gate"):
         w = kern[name]
         w["TFLOP/s"] = round(T * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
@@ -272,6 +290,7 @@ def main(argv=None):
             "n_hash_cols": cfg.n_hash_cols,
             "dim": cfg.dim,
             "hc_mult": cfg.hc_mult,
+            "table_layout": args.table,
             "parallelism": "single GPU",
         },
         "roofline": roofline,

@@ -9,6 +9,8 @@ an exception is raised.
 
     engram_hash            -- n-gram hash ids (+ compressed-id cache update)
     engram_gather_dequant  -- fp8 row gather + block-scale dequant -> bf16
+    engram_pack_table      -- the table's rows and scales in one record per row (one-off layout conversion)
+    engram_gather_dequant_packed -- engram_gather_dequant on a packed table (same output, fewer lines fetched)
     engram_wkv             -- kv = A @ W^T on bf16 matrix cores
     engram_gate_dot        -- per-(token, copy) RMS-normalised gate pre-activation
     engram_gate_output     -- the dot, the sigmoid gate, the token mask and the residual add
@@ -45,6 +47,8 @@ def lib() -> ctypes.CDLL:
         i64, i32, p, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         L.engram_hash.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p, p]
         L.engram_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p, p]
+        L.engram_gather_dequant_packed.argtypes = [p, i64, i64, i32, p, i64, i64, i32, i32, p, p, p, p]
+        L.engram_pack_table.argtypes = [p, p, i64, i32, i32, p, p]
         L.engram_wkv.argtypes = [p, p, p, i64, i32, i32, p]
         L.engram_gate_dot.argtypes = [p, p, i64, p, p, f32, p, i64, i32, i32, p]
         L.engram_gate_output.argtypes = [p, p, i64, p, p, f32, p, p, p, i64, i32, i32, p]
@@ -52,8 +56,9 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
-        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_wkv, L.engram_gate_dot, L.engram_gate_output,
-                  L.engram_wkv_gate, L.engram_gate_residual, L.engram_abi_version):
+        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
+                  L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
+                  L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
         L.engram_status_string.restype = ctypes.c_char_p
@@ -123,14 +128,8 @@ def engram_hash(input_ids, start_pos, token_mask, token_map, cache, multipliers,
     return out
 
 
-def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n_cols=None, layer=0,
-                          out=None, out_fp8=None, out_scale=None, stream=None):
-    """bf16 [T, C, D] rows for one layer's ids.
-
-    hash_ids: int64 [B, L, E, C] (engram_hash's output; `layer` picks e) or [T, C].
-    weight: float8_e4m3fn or uint8 [R, D]; scale: float32 [R, D/block_size].
-    Optional out_fp8 (uint8 [T, C, D]) and out_scale (float32 [T, C, D/blk]) receive the raw gathered bytes/scales.
-    """
+def _gather_ids(hash_ids, n_cols, layer):
+    """(T, C, id stride, pointer to the layer's first id) of [B, L, E, C] or [T, C] ids."""
     import torch
 
     if hash_ids.dim() == 4:
@@ -145,7 +144,58 @@ def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n
         C = n_cols
     if not hash_ids.is_contiguous() or hash_ids.dtype != torch.int64 or not hash_ids.is_cuda:
         raise ValueError("hash_ids must be a contiguous int64 GPU tensor")
-    ids_ptr = ctypes.c_void_p(hash_ids.data_ptr() + 8 * base)
+    return T, C, stride, ctypes.c_void_p(hash_ids.data_ptr() + 8 * base)
+
+
+def engram_pack_table(weight, scale, block_size=32, out=None, stream=None):
+    """uint8 [R, 2*D]: record r = weight[r] (D fp8 bytes), then scale[r] (fp32), then zeros."""
+    import torch
+
+    if weight.dtype == torch.float8_e4m3fn:
+        weight = weight.view(torch.uint8)
+    R, D = weight.shape
+    if tuple(scale.shape) != (R, D // block_size):
+        raise ValueError("scale must be [R, D/block_size]")
+    if out is None:
+        out = torch.empty((R, 2 * D), dtype=torch.uint8, device=weight.device)
+    if tuple(out.shape) != (R, 2 * D):
+        raise ValueError("out must be [R, 2*D]")
+    _check(lib().engram_pack_table(_dev(weight, "weight", torch.uint8, 2), _dev(scale, "scale", torch.float32, 2),
+                                   R, D, int(block_size), _dev(out, "out", torch.uint8, 2), _stream(stream)))
+    return out
+
+
+def engram_gather_dequant_packed(hash_ids, table, block_size=32, row_start=0, n_cols=None, layer=0, out=None,
+                                 out_fp8=None, out_scale=None, stream=None):
+    """engram_gather_dequant on a packed table (uint8 [R, 2*D], engram_pack_table's layout)."""
+    import torch
+
+    T, C, stride, ids_ptr = _gather_ids(hash_ids, n_cols, layer)
+    R, D2 = table.shape
+    D = D2 // 2
+    if out is None:
+        out = torch.empty((T, C, D), dtype=torch.bfloat16, device=hash_ids.device)
+    if out.numel() != T * C * D:
+        raise ValueError("out has the wrong size")
+    p8 = None if out_fp8 is None else _dev(out_fp8, "out_fp8", torch.uint8)
+    ps = None if out_scale is None else _dev(out_scale, "out_scale", torch.float32)
+    _check(lib().engram_gather_dequant_packed(
+        ids_ptr, T, stride, C, _dev(table, "table", torch.uint8, 2), R, int(row_start), D, int(block_size),
+        _dev(out, "out", torch.bfloat16), p8, ps, _stream(stream)))
+    return out
+
+
+def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n_cols=None, layer=0,
+                          out=None, out_fp8=None, out_scale=None, stream=None):
+    """bf16 [T, C, D] rows for one layer's ids.
+
+    hash_ids: int64 [B, L, E, C] (engram_hash's output; `layer` picks e) or [T, C].
+    weight: float8_e4m3fn or uint8 [R, D]; scale: float32 [R, D/block_size].
+    Optional out_fp8 (uint8 [T, C, D]) and out_scale (float32 [T, C, D/blk]) receive the raw gathered bytes/scales.
+    """
+    import torch
+
+    T, C, stride, ids_ptr = _gather_ids(hash_ids, n_cols, layer)
     if weight.dtype == torch.float8_e4m3fn:
         weight = weight.view(torch.uint8)
     R, D = weight.shape
@@ -311,5 +361,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 
 __all__ = ["engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
-           "engram_wkv_gate", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "EngramError", "lib",
+           "engram_wkv_gate", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

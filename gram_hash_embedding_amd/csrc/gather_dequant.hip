@@ -19,6 +19,12 @@
 //   to nearest even): the same two roundings as the page.
 // - Output rows (t, c) are laid out consecutively, so a wave's stores for
 //   one u cover 64/(D/16) whole rows: 2 KB contiguous at D = 64.
+// - Packed tables (engram_pack_table): the pages keep a row's D fp8 bytes and
+//   its D/blk fp32 scales in two tensors, so a random lookup of a 64-byte row
+//   costs two 128-byte lines (the row's and the scale's) -- 256 bytes fetched
+//   for 72 used.  A packed record of 2*D bytes holds the row and then its
+//   scales (zero padded), aligned to its size: at D <= 64 a lookup touches one
+//   line.  The dequant is the same code, so the outputs are bit-identical.
 #include "common.h"
 
 namespace engram {
@@ -34,8 +40,8 @@ struct GatherArgs {
     int64_t stride;
     int64_t W;  // rows to produce = T * C
     int C;
-    const uint8_t* weight;
-    const float* scale;
+    const uint8_t* weight;  // [R, D] fp8, or the packed table [R, 2D]
+    const float* scale;     // [R, D/blk] fp32 (unused for a packed table)
     int64_t R, row_start;
     int blk;
     uint16_t* out;
@@ -62,7 +68,7 @@ __device__ inline void dequant16(const u32x4& v, float s, u32x4& o0, u32x4& o1) 
     o1 = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-template <int D, int U>
+template <int D, int U, bool kPacked>
 __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) {
     constexpr int LPR = D / 16;              // lanes per row
     constexpr int RPS = kThreads / LPR;      // rows per step of the block
@@ -101,8 +107,14 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        v[u] = *reinterpret_cast<const u32x4*>(a.weight + row[u] * D + lane_in_row * 16);
-        sc[u] = a.scale[row[u] * S + sidx];
+        if (kPacked) {
+            const uint8_t* rec = a.weight + row[u] * (2 * D);
+            v[u] = *reinterpret_cast<const u32x4*>(rec + lane_in_row * 16);
+            sc[u] = reinterpret_cast<const float*>(rec + D)[sidx];
+        } else {
+            v[u] = *reinterpret_cast<const u32x4*>(a.weight + row[u] * D + lane_in_row * 16);
+            sc[u] = a.scale[row[u] * S + sidx];
+        }
     }
 
 #pragma unroll
@@ -124,14 +136,39 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
     }
 }
 
-template <int D>
+template <int D, bool kPacked>
 int launch(const GatherArgs& a, hipStream_t stream) {
     constexpr int U = 8;
     constexpr int rows_per_block = (kThreads / (D / 16)) * U;
     const int64_t blocks = (a.W + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gather_dequant: too many rows");
-    hipLaunchKernelGGL((gather_dequant_kernel<D, U>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
-    return check_launch("engram_gather_dequant");
+    hipLaunchKernelGGL((gather_dequant_kernel<D, U, kPacked>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, a);
+    return check_launch(kPacked ? "engram_gather_dequant_packed" : "engram_gather_dequant");
+}
+
+// One thread per 16-byte piece of the packed table: pieces [0, D/16) of a record are the row, the rest its
+// scales followed by zeros.
+__global__ __launch_bounds__(kThreads) void pack_table_kernel(const uint8_t* weight, const float* scale, int64_t R,
+                                                              int D, int S, uint8_t* packed) {
+    const int64_t pieces = R * (2 * D / 16);
+    const int per_rec = 2 * D / 16;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < pieces;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t r = i / per_rec;
+        const int pc = static_cast<int>(i - r * per_rec);
+        u32x4 v = {0, 0, 0, 0};
+        if (pc < D / 16) {
+            v = *reinterpret_cast<const u32x4*>(weight + r * D + pc * 16);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int sidx = (pc - D / 16) * 4 + k;
+                if (sidx < S) v[k] = __float_as_uint(scale[r * S + sidx]);
+            }
+        }
+        *reinterpret_cast<u32x4*>(packed + i * 16) = v;
+    }
 }
 
 }  // namespace
@@ -139,23 +176,23 @@ int launch(const GatherArgs& a, hipStream_t stream) {
 
 using namespace engram;
 
-extern "C" int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
-                                     const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
-                                     int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
-                                     float* out_scale, void* stream) {
-    if (T < 0) return fail(ENGRAM_EINVAL, "engram_gather_dequant: T < 0");
-    if (C < 1 || C > 1024) return fail(ENGRAM_EINVAL, "engram_gather_dequant: C=%d outside [1, 1024]", C);
-    if (id_token_stride < C) return fail(ENGRAM_EINVAL, "engram_gather_dequant: id_token_stride < C");
+namespace {
+int gather_entry(const char* name, bool packed, const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                 const uint8_t* weight, const float* scale, int64_t R, int64_t row_start, int32_t D, int32_t blk,
+                 uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale, void* stream) {
+    if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", name);
+    if (C < 1 || C > 1024) return fail(ENGRAM_EINVAL, "%s: C=%d outside [1, 1024]", name, C);
+    if (id_token_stride < C) return fail(ENGRAM_EINVAL, "%s: id_token_stride < C", name);
     if (D != 32 && D != 64 && D != 128 && D != 256)
-        return fail(ENGRAM_EINVAL, "engram_gather_dequant: D=%d not in {32, 64, 128, 256}", D);
+        return fail(ENGRAM_EINVAL, "%s: D=%d not in {32, 64, 128, 256}", name, D);
     if (blk < 16 || blk % 16 != 0 || D % blk != 0)
-        return fail(ENGRAM_EINVAL, "engram_gather_dequant: blk=%d must be a multiple of 16 dividing D=%d", blk, D);
-    if (R < 1) return fail(ENGRAM_EINVAL, "engram_gather_dequant: R < 1");
+        return fail(ENGRAM_EINVAL, "%s: blk=%d must be a multiple of 16 dividing D=%d", name, blk, D);
+    if (R < 1) return fail(ENGRAM_EINVAL, "%s: R < 1", name);
     if (T == 0) return ENGRAM_OK;
-    if (!hash_ids || !weight || !scale || !out_bf16) return fail(ENGRAM_EINVAL, "engram_gather_dequant: null pointer");
-    if (!aligned(hash_ids, 8) || !aligned(weight, 16) || !aligned(scale, 4) || !aligned(out_bf16, 16) ||
-        (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, 4)))
-        return fail(ENGRAM_EINVAL, "engram_gather_dequant: misaligned pointer");
+    if (!hash_ids || !weight || (!packed && !scale) || !out_bf16) return fail(ENGRAM_EINVAL, "%s: null pointer", name);
+    if (!aligned(hash_ids, 8) || !aligned(weight, packed ? 2 * D : 16) || (!packed && !aligned(scale, 4)) ||
+        !aligned(out_bf16, 16) || (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, 4)))
+        return fail(ENGRAM_EINVAL, "%s: misaligned pointer", name);
 
     GatherArgs a;
     a.ids = hash_ids;
@@ -172,9 +209,45 @@ extern "C" int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t
     a.out_scale = out_scale;
     hipStream_t s = as_stream(stream);
     switch (D) {
-        case 32: return launch<32>(a, s);
-        case 64: return launch<64>(a, s);
-        case 128: return launch<128>(a, s);
-        default: return launch<256>(a, s);
+        case 32: return packed ? launch<32, true>(a, s) : launch<32, false>(a, s);
+        case 64: return packed ? launch<64, true>(a, s) : launch<64, false>(a, s);
+        case 128: return packed ? launch<128, true>(a, s) : launch<128, false>(a, s);
+        default: return packed ? launch<256, true>(a, s) : launch<256, false>(a, s);
     }
+}
+}  // namespace
+
+extern "C" int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                     const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
+                                     int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                                     float* out_scale, void* stream) {
+    return gather_entry("engram_gather_dequant", false, hash_ids, T, id_token_stride, C, weight, scale, R, row_start,
+                        D, blk, out_bf16, out_fp8, out_scale, stream);
+}
+
+extern "C" int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                            const uint8_t* table, int64_t R, int64_t row_start, int32_t D,
+                                            int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale,
+                                            void* stream) {
+    return gather_entry("engram_gather_dequant_packed", true, hash_ids, T, id_token_stride, C, table, nullptr, R,
+                        row_start, D, blk, out_bf16, out_fp8, out_scale, stream);
+}
+
+extern "C" int engram_pack_table(const uint8_t* weight, const float* scale, int64_t R, int32_t D, int32_t blk,
+                                 uint8_t* packed, void* stream) {
+    if (D != 32 && D != 64 && D != 128 && D != 256)
+        return fail(ENGRAM_EINVAL, "engram_pack_table: D=%d not in {32, 64, 128, 256}", D);
+    if (blk < 16 || blk % 16 != 0 || D % blk != 0)
+        return fail(ENGRAM_EINVAL, "engram_pack_table: blk=%d must be a multiple of 16 dividing D=%d", blk, D);
+    if (R < 0) return fail(ENGRAM_EINVAL, "engram_pack_table: R < 0");
+    if (R == 0) return ENGRAM_OK;
+    if (!weight || !scale || !packed) return fail(ENGRAM_EINVAL, "engram_pack_table: null pointer");
+    if (!aligned(weight, 16) || !aligned(scale, 4) || !aligned(packed, 2 * D))
+        return fail(ENGRAM_EINVAL, "engram_pack_table: misaligned pointer");
+    const int64_t pieces = R * (2 * D / 16);
+    const int64_t need = (pieces + kThreads - 1) / kThreads;
+    const int64_t blocks = need < (1 << 20) ? need : (1 << 20);
+    hipLaunchKernelGGL(pack_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, as_stream(stream),
+                       weight, scale, R, D, D / blk, packed);
+    return check_launch("engram_pack_table");
 }

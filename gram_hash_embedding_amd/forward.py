@@ -15,10 +15,10 @@ that order.
 from __future__ import annotations
 
 import dataclasses
-from typing import List
+from typing import List, Optional
 
-from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant, engram_hash,
-               engram_wkv, engram_wkv_gate, engram_wkv_gate_workspace_bytes)
+from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
+               engram_gather_dequant_packed, engram_hash, engram_wkv, engram_wkv_gate, engram_wkv_gate_workspace_bytes)
 
 
 @dataclasses.dataclass
@@ -45,6 +45,7 @@ class LayerWeights:
     k_weight: "torch.Tensor"       # bf16 [hc, dim]
     block_size: int
     row_start: int = 0
+    packed: "Optional[torch.Tensor]" = None  # uint8 [R, 2*D]: the same table as one record per row (engram_pack_table)
 
 
 class EngramForward:
@@ -95,11 +96,12 @@ class EngramForward:
             input_ids, start_pos, token_mask, s.token_map, s.cache, s.multipliers, s.primes, s.offsets, s.pad_id,
             s.dead, out=out))
 
-    def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False):
+    def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False, packed=False):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim]
         (or [B, L, hc, dim]); with `output`, also the layer's output stream bf16 (x's shape), where
         token_mask [B, L] (False = pass through) shuts the gate.  With `fused`, the second tensor is
-        the value bf16 [T, dim] alone (the keys are never stored).
+        the value bf16 [T, dim] alone (the keys are never stored).  With `packed`, the rows come from
+        the layer's packed table (same values, one record per row).
 
         The tensors are this object's buffers for layer e: the next call for the same layer
         overwrites them."""
@@ -110,8 +112,14 @@ class EngramForward:
         D = lw.weight.shape[1]
         dev = hash_ids.device
         a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
-        self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
-            hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
+        if packed:
+            if lw.packed is None:
+                raise ValueError(f"layer {e} has no packed table")
+            self._timed(events, "gather_dequant_packed", lambda: engram_gather_dequant_packed(
+                hash_ids, lw.packed, lw.block_size, lw.row_start, layer=e, out=a))
+        else:
+            self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
+                hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
         x3 = x.reshape(T, x.shape[-2], x.shape[-1])
         dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
         if fused:
@@ -135,7 +143,8 @@ class EngramForward:
         self._timed(events, "gate_dot", lambda: engram_gate_dot(x3, kv, lw.q_weight, lw.k_weight, self.eps, out=dot))
         return a, kv, dot
 
-    def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False):
+    def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False,
+             packed=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
         (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
@@ -144,7 +153,8 @@ class EngramForward:
         res = []
         for e in range(self.E):
             x = xs[e] if isinstance(xs, (list, tuple)) else xs
-            res.append(self.layer(e, ids, x, events, token_mask=token_mask, output=output, fused=fused)[-1])
+            res.append(self.layer(e, ids, x, events, token_mask=token_mask, output=output, fused=fused,
+                                  packed=packed)[-1])
         return res
 
 

@@ -130,6 +130,37 @@ int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_s
                           float* out_scale, void* stream);
 
 /*
+ * engram_pack_table -- copy one layer's table (the pages' two tensors: the
+ * fp8 rows `weight` [R, D] and their fp32 block scales `scale` [R, D/blk]) into
+ * one packed table of R records of 2*D bytes:
+ *   packed[r, 0 : D)               = weight[r, :]
+ *   packed[r, D : D + 4*(D/blk))   = scale[r, :] (little-endian fp32)
+ *   packed[r, D + 4*(D/blk) : 2*D) = 0
+ * A record is aligned to its size, so at D <= 64 a row and its scales share one
+ * 128-byte line and a random lookup reads one line instead of two.  A one-off
+ * layout conversion (at table load), not a step of the forward.
+ *
+ * weight  uint8 [R, D]; 16-byte aligned
+ * scale   float32 [R, D/blk]; 4-byte aligned
+ * packed  uint8 [R, 2*D], out; aligned to 2*D bytes; caller-owned
+ * Limits: D in {32, 64, 128, 256}; blk a multiple of 16 that divides D; R >= 0.
+ */
+int engram_pack_table(const uint8_t* weight, const float* scale, int64_t R, int32_t D, int32_t blk,
+                      uint8_t* packed, void* stream);
+
+/*
+ * engram_gather_dequant_packed -- engram_gather_dequant on a packed table
+ * (engram_pack_table's layout): the same outputs, bit for bit, with
+ * weight[row, j] = table[row, j] and scale[row, s] = fp32 at table[row, D + 4s].
+ *
+ * table  uint8 [R, 2*D]; aligned to 2*D bytes.  Other arguments, outputs,
+ *        limits and errors as engram_gather_dequant.
+ */
+int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                 const uint8_t* table, int64_t R, int64_t row_start, int32_t D, int32_t blk,
+                                 uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale, void* stream);
+
+/*
  * engram_wkv -- the projection kv = A * W^T (stack-hashes page: Engram's
  * `wkv` Linear, n_hash_cols*head_dim -> dim*(hc_mult+1), no bias).
  *

@@ -20,7 +20,8 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert set(names) >= {"engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot",
+    assert set(names) >= {"engram_hash", "engram_gather_dequant", "engram_gather_dequant_packed",
+                          "engram_pack_table", "engram_wkv", "engram_gate_dot",
                           "engram_gate_output", "engram_wkv_gate", "engram_wkv_gate_workspace_bytes",
                           "engram_gate_residual", "engram_status_string", "engram_last_error",
                           "engram_abi_version"}
@@ -75,6 +76,8 @@ def test_zero_tokens_is_a_valid_no_op():
     L = g.lib()
     assert L.engram_hash(None, 0, 5, 0, None, None, 10, None, 0, 5, None, None, None, 1, 4, 2, 2, -1, None, None) == 0
     assert L.engram_gather_dequant(None, 0, 24, 24, None, None, 10, 0, 64, 32, None, None, None, None) == 0
+    assert L.engram_gather_dequant_packed(None, 0, 24, 24, None, 10, 0, 64, 32, None, None, None, None) == 0
+    assert L.engram_pack_table(None, None, 0, 64, 32, None, None) == 0
     assert L.engram_wkv(None, None, None, 0, 64, 64, None) == 0
     assert L.engram_gate_dot(None, None, 64, None, None, 1e-20, None, 0, 4, 16, None) == 0
     assert L.engram_gate_output(None, None, 80, None, None, 1e-20, None, None, None, 0, 4, 16, None) == 0
@@ -98,6 +101,33 @@ def test_gather_validation(kw, msg):
     rc = g.lib().engram_gather_dequant(a["ids"], a["T"], a["stride"], a["C"], a["weight"], a["scale"], a["R"],
                                        a["row_start"], a["D"], a["blk"], a["out"], None, None, None)
     assert rc == 1
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(D=48), "D=48"),
+    (dict(blk=8), "blk=8"),
+    (dict(C=0), "C=0"),
+    (dict(R=0), "R < 1"),
+    (dict(table=None), "null"),
+    (dict(table=ctypes.c_void_p(0x100040)), "misaligned"),  # 64-byte aligned, a 128-byte record needs 128
+])
+def test_gather_packed_validation(kw, msg):
+    a = dict(ids=FAKE, T=10, stride=24, C=24, table=FAKE, R=100, row_start=0, D=64, blk=32, out=FAKE)
+    a.update(kw)
+    rc = g.lib().engram_gather_dequant_packed(a["ids"], a["T"], a["stride"], a["C"], a["table"], a["R"],
+                                              a["row_start"], a["D"], a["blk"], a["out"], None, None, None)
+    assert rc == 1
+    assert msg in _err()
+    assert "engram_gather_dequant_packed" in _err()
+
+
+@pytest.mark.parametrize("kw,msg", [(dict(D=40), "D=40"), (dict(blk=24), "blk=24"), (dict(R=-1), "R < 0"),
+                                    (dict(packed=None), "null"), (dict(packed=ctypes.c_void_p(0x100040)), "misaligned")])
+def test_pack_table_validation(kw, msg):
+    a = dict(weight=FAKE, scale=FAKE, R=100, D=64, blk=32, packed=FAKE)
+    a.update(kw)
+    assert g.lib().engram_pack_table(a["weight"], a["scale"], a["R"], a["D"], a["blk"], a["packed"], None) == 1
     assert msg in _err()
 
 

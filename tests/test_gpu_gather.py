@@ -107,3 +107,72 @@ def test_gather_config(gpu_device, cfg_index):
         np.testing.assert_array_equal(got, want, err_msg=f"layer {e}")
         del w_dev, s_dev, out
         torch.cuda.empty_cache()
+
+
+def _pack_on_host(w, s, D):
+    """The packed layout written out on the host: row bytes, then the scales' bytes, then zeros."""
+    R = w.shape[0]
+    rec = np.zeros((R, 2 * D), dtype=np.uint8)
+    rec[:, :D] = w
+    sb = np.ascontiguousarray(s.astype("<f4")).view(np.uint8)
+    rec[:, D:D + sb.shape[1]] = sb
+    return rec
+
+
+@pytest.mark.parametrize("D,blk", [(32, 32), (32, 16), (64, 32), (64, 16), (128, 32), (256, 32), (256, 256)])
+def test_packed_table_and_gather(gpu_device, D, blk):
+    """engram_pack_table writes the documented record layout; the packed gather equals the oracle bit for bit."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    R, row_start = 2999, 300
+    w, s = synth.table_rows(D * 11 + blk, np.arange(R), D, blk)
+    w_t = torch.from_numpy(w).to(gpu_device)
+    s_t = torch.from_numpy(s).to(gpu_device)
+    packed = g.engram_pack_table(w_t, s_t, blk)
+    np.testing.assert_array_equal(packed.cpu().numpy(), _pack_on_host(w, s, D))
+    rng = np.random.default_rng(D * 3 + blk)
+    T, stride, C = 257, 11, 9
+    ids = rng.integers(row_start - 30, row_start + R + 30, size=(T, stride), dtype=np.int64)
+    ids[0, :3] = [-(2**62), 2**62, row_start + R]
+    ids_t = torch.from_numpy(ids).to(gpu_device)
+    f8 = torch.empty((T, C, D), dtype=torch.uint8, device=gpu_device)
+    sc = torch.empty((T, C, D // blk), dtype=torch.float32, device=gpu_device)
+    out = g.engram_gather_dequant_packed(ids_t, packed, blk, row_start, n_cols=C, out_fp8=f8, out_scale=sc)
+    want = oracle.gather_dequant(ids, w, s, row_start=row_start, block_size=blk, n_cols=C, want_raw=True)
+    _check((bits(out), f8.cpu().numpy(), sc.cpu().numpy()), want)
+    unpacked = g.engram_gather_dequant(ids_t, w_t, s_t, blk, row_start, n_cols=C)
+    np.testing.assert_array_equal(bits(out), bits(unpacked))
+
+
+@pytest.mark.parametrize("cfg_index", [2, 3])
+def test_packed_gather_config(gpu_device, cfg_index):
+    """The packed gather of a workload's full-size table on sampled tokens, against the oracle."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+    import synth.device as sd
+
+    cfg = synth.CONFIGS[cfg_index]
+    hi = synth.hash_inputs(cfg)
+    B, L = hi.input_ids.shape
+    ids = oracle.hash(hi.input_ids, 0, hi.token_mask, hi.token_map, np.zeros((B, L), np.int64), hi.multipliers,
+                      hi.primes, hi.offsets, cfg.pad_id, synth.DEAD)
+    ids_dev = torch.from_numpy(ids).to(gpu_device)
+    T, C, D, blk = cfg.tokens, cfg.n_hash_cols, cfg.head_dim, cfg.block_size
+    sample = np.sort(np.random.default_rng(cfg_index + 10).choice(T, min(T, 4096), replace=False))
+    e = cfg.n_layers - 1
+    R = cfg.rows_alloc[e]
+    w_dev, s_dev = sd.device_table(synth.table_seed(cfg, e), R, D, blk, gpu_device)
+    packed = g.engram_pack_table(w_dev, s_dev, blk)
+    del w_dev, s_dev
+    torch.cuda.empty_cache()
+    out = g.engram_gather_dequant_packed(ids_dev, packed, blk, layer=e)
+    got = bits(out.view(T, C, D)[torch.from_numpy(sample).to(gpu_device)])
+    lid = ids.reshape(T, cfg.n_layers, C)[sample, e]
+    cw, cs, remap = compact_rows(lid, R, synth.table_seed(cfg, e), D, blk)
+    want = oracle.gather_dequant(remap, cw, cs, block_size=blk)
+    np.testing.assert_array_equal(got, want)
+    del packed, out
+    torch.cuda.empty_cache()
