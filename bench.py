@@ -5,6 +5,8 @@
 One step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: the hash of all tokens, then per engram layer the
 fp8 gather + dequant, the wkv projection and the gate pre-activation dot.
+(The decode workload, --config 4: one step is its 64 forward calls of one
+token per sequence, after an untimed hash of the 4,096-token history.)
 The default workload is the long prefill: one sequence of 65,536 tokens, one
 engram layer with the released 384,006,168-row fp8 table (24.6 GB, D = 64,
 8 hash heads, n-grams up to 4), dim 5120, hc_mult 4.
@@ -182,22 +184,32 @@ def main(argv=None):
         log(f"copy probe: {args.copy_probe_mb} MiB device-to-device")
 
     cfg = synth.CONFIGS[args.config]
-    if cfg.decode_steps:
-        print("bench.py: the decode workload is a parity case, not a bench line", file=sys.stderr)
-        return 2
     log(f"building workload {cfg.name} ...")
     t_build = time.perf_counter()
-    wl = sw.build(cfg, device=dev, packed=True)
+    wl = sw.build(cfg, device=dev, packed=True, x_steps=max(1, cfg.decode_steps))
+    fwd = wl.fwd
+    if cfg.decode_steps:
+        # decode: the compressed-id cache holds the first start_pos tokens of every sequence (untimed); one
+        # bench step is then `decode_steps` forward calls of one token per sequence, each with its own stream
+        fwd.hash(wl.input_ids[:, :cfg.start_pos].contiguous(), 0)
+        P = cfg.start_pos
+        step_ids = [wl.input_ids[:, P + s:P + s + 1].contiguous() for s in range(cfg.decode_steps)]
+        T = cfg.batch * cfg.decode_steps
+    else:
+        T = cfg.tokens
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
-    fwd = wl.fwd
-    T = cfg.tokens
 
     def loop(fused, output, packed):
         """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
         def step(events=None):
-            fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output, fused=fused,
-                     packed=packed)
+            if cfg.decode_steps:
+                for s in range(cfg.decode_steps):
+                    fwd.step(step_ids[s], cfg.start_pos + s, wl.x[s], None, events=events, output=output,
+                             fused=fused, packed=packed)
+            else:
+                fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output,
+                         fused=fused, packed=packed)
 
         for _ in range(args.warmup):
             step()
@@ -235,21 +247,22 @@ def main(argv=None):
     for name, pairs in kern_events.items():
         ms = [s.elapsed_time(e) for s, e in pairs]
         kern[name] = {"launches": len(ms), "avg_us": round(1e3 * sum(ms) / len(ms), 2)}
+    T_launch = cfg.batch if cfg.decode_steps else T  # tokens one launch processes
     E = cfg.n_layers
     W_bytes = 2 * cfg.K * cfg.n_out
-    kern["hash"]["GB/s"] = round(T * algo["hash_bytes"] / (kern["hash"]["avg_us"] * 1e3), 1)
+    kern["hash"]["GB/s"] = round(T_launch * algo["hash_bytes"] / (kern["hash"]["avg_us"] * 1e3), 1)
     for name in ("gather_dequant", "gather_dequant_packed"):
         g = kern[name]
-        g["GB/s"] = round(T * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
+        g["GB/s"] = round(T_launch * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
         g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
     for name in ("wkv", "wkv_gate"):
         w = kern[name]
-        w["TFLOP/s"] = round(T * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
+        w["TFLOP/s"] = round(T_launch * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
         w["frac_mfma"] = round(w["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
     for name, key in (("gate_dot", "gate_bytes"), ("gate_output", "gate_output_bytes"),
                       ("gate_residual", "gate_residual_bytes")):
         k = kern[name]
-        k["GB/s"] = round(T * algo[key] / (k["avg_us"] * 1e3), 1)
+        k["GB/s"] = round(T_launch * algo[key] / (k["avg_us"] * 1e3), 1)
         k["frac_hbm"] = round(k["GB/s"] / PEAK_HBM_GBS, 4)
 
     workload = cfg.name
@@ -262,7 +275,7 @@ def main(argv=None):
         "unit": "TFLOP/s",
         "frac": wg["frac_mfma"],
         "traffic": load_traffic("wkv.hip", "wkv_gate", workload),
-        "algorithmic_bytes_per_launch": T * algo["wkv_gate_bytes"] + W_bytes,
+        "algorithmic_bytes_per_launch": T_launch * algo["wkv_gate_bytes"] + W_bytes,
     }
     result = {
         "metric": METRIC,
@@ -284,6 +297,7 @@ def main(argv=None):
             "global_batch": cfg.batch,
             "seq_len": cfg.seqlen,
             "tokens_per_step": T,
+            "decode_steps": cfg.decode_steps,
             "engram_layers": E,
             "table_rows": list(cfg.rows_alloc[:E]),
             "head_dim": cfg.head_dim,
