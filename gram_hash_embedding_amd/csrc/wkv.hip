@@ -601,6 +601,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 epilogue(acc, m0, n0);
             }
         }
+        // the slabs issued past this workgroup's last one (empty resources) still write LDS: let them land
+        // before the workgroup ends
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     };
     if (loader)
         run(std::true_type{});
