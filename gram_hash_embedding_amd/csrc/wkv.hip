@@ -7,7 +7,8 @@
 // Design (gfx950, dense contraction -> MFMA):
 // - Workgroup tile 256 x 256 and eight waves, two per SIMD: wave (wm, wn) owns
 //   128 tokens x 64 outputs = 4 x 2 MFMA 32x32x16 blocks in 128 fp32
-//   accumulators (AGPRs).  One workgroup per CU.  With one wave per SIMD,
+//   accumulators (VGPRs; the first k-step of a tile takes a zero C operand,
+//   so they are never cleared separately).  One workgroup per CU.  With one wave per SIMD,
 //   a wave stalled on issuing its direct-to-LDS loads (the CU's address FIFO
 //   fills) left the matrix core idle; with two, the SIMD partner keeps it busy
 //   (main loop 4.17 -> 3.73 ms on the long-prefill shape).  Fragment reads grow
@@ -102,20 +103,27 @@ __device__ inline void tile_coords(const WkvArgs& p, int pid, int& tm, int& tn) 
     tn = r / gsize;
 }
 
-// One accumulator element read out of its AGPR at this point of the program: a volatile asm keeps the
-// read inside its epilogue round (the compiler would otherwise copy all 256 accumulators to VGPRs ahead
-// of the first epilogue barrier and spill).
-__device__ inline float acc_read(float a) {
-    float v;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-    return v;
-}
+// One accumulator element.  The accumulators are VGPRs (the library builds this file with LLVM's VGPR form
+// of the MFMA), so the epilogues read them in place, without a v_accvgpr_read per element.
+__device__ inline float acc_read(float a) { return a; }
 
 // lane id recomputed from the exec mask (two VALU ops) rather than kept live in a VGPR
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 (RNE) in one instruction, opaque to the compiler so that it keeps the pair
+__device__ inline uint32_t cvt_pk_bf16(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+
+// c + a.lo * b.lo + a.hi * b.hi over packed bf16 pairs, fp32 accumulation
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -191,6 +199,15 @@ __device__ inline void mfma_step8(f32x16 (&acc)[4][2], const bf16x8* fa, const b
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// the first k-step of a tile: C = 0 (no separate zeroing of the 128 accumulators)
+__device__ inline void mfma_step8_zero(f32x16 (&acc)[4][2], const bf16x8* fa, const bf16x8* fw) {
+    const f32x16 z = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], z, 0, 0, 0);
 }
 
 // the 6 fragment reads of the next k-step spread among the 8 MFMAs of this one
@@ -430,17 +447,17 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const uint32_t k01 = pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1]));
-                    const uint32_t k23 = pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]));
+                    const uint32_t k01 = cvt_pk_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1]));
+                    const uint32_t k23 = cvt_pk_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]));
                     const float key[4] = {lo_bf16(k01), hi_bf16(k01), lo_bf16(k23), hi_bf16(k23)};
                     const float h[4] = {lo_bf16(xr[j][gq][0]), hi_bf16(xr[j][gq][0]), lo_bf16(xr[j][gq][1]),
                                         hi_bf16(xr[j][gq][1])};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        hwk += h[r] * wgt[j][gq][r] * key[r];
-                        kk += key[r] * key[r];
-                        hh += h[r] * h[r];
-                    }
+                    for (int r = 0; r < 4; ++r) hwk += h[r] * wgt[j][gq][r] * key[r];
+                    kk = dot2_bf16(k01, k01, kk);
+                    kk = dot2_bf16(k23, k23, kk);
+                    hh = dot2_bf16(xr[j][gq][0], xr[j][gq][0], hh);
+                    hh = dot2_bf16(xr[j][gq][1], xr[j][gq][1], hh);
                 }
             res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
@@ -514,10 +531,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         // One slab: four k-steps of 8 MFMAs, one barrier before the last.  kDefer (the last slab of a
         // fused key tile): the freed stage is kept for the epilogue's stream rows -- the loaders skip the
         // slab after next (issued after the epilogue) and the storers fetch rounds 1 and 2 into it.
-        auto slab = [&](auto defer_tag, int64_t m0, int n0) {
+        auto slab = [&](auto defer_tag, auto first_tag, int64_t m0, int n0) {
             constexpr bool kDefer = decltype(defer_tag)::value;
+            constexpr bool kFirst = decltype(first_tag)::value;
             read_frags(stage, 1, fa1, fw1);
-            mfma_step8(acc, fa0, fw0);
+            if (kFirst)
+                mfma_step8_zero(acc, fa0, fw0);
+            else
+                mfma_step8(acc, fa0, fw0);
             interleave_reads8();
             read_frags(stage, 2, fa0, fw0);
             mfma_step8(acc, fa1, fw1);
@@ -574,21 +595,18 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             const int64_t m0 = static_cast<int64_t>(tm) * BM;
             const int n0 = tn * BN;
             const bool key_tile = kGate && n0 < p.out_col0;
-            auto zero_acc = [&]() {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-            };
             if (key_tile) {
                 // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
                 if (!kLoader) dma_x(m0, n0, 0, ex);
-                zero_acc();
-                for (int kt = 0; kt < KT - 1; ++kt) slab(std::false_type{}, m0, n0);
-                const int free_stage = stage;
-                slab(std::true_type{}, m0, n0);
+                int free_stage = stage;
+                if (KT == 1) {
+                    slab(std::true_type{}, std::true_type{}, m0, n0);
+                } else {
+                    slab(std::false_type{}, std::true_type{}, m0, n0);
+                    for (int kt = 1; kt < KT - 1; ++kt) slab(std::false_type{}, std::false_type{}, m0, n0);
+                    free_stage = stage;
+                    slab(std::true_type{}, std::false_type{}, m0, n0);
+                }
                 gate_epilogue(acc, m0, n0, free_stage);
                 if (kLoader) {  // the slab after next, held back while the epilogue used its stage
                     issue_slab(ld, free_stage, issued < total_slabs_mine);
@@ -596,8 +614,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     ++issued;
                 }
             } else {
-                zero_acc();
-                for (int kt = 0; kt < KT; ++kt) slab(std::false_type{}, m0, n0);
+                slab(std::false_type{}, std::true_type{}, m0, n0);
+                for (int kt = 1; kt < KT; ++kt) slab(std::false_type{}, std::false_type{}, m0, n0);
                 epilogue(acc, m0, n0);
             }
         }
