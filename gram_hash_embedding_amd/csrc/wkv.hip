@@ -366,27 +366,29 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // rounded to bf16 (the product is a bf16 tensor before it is used) and reduced against the stream's
     // matching element: sum(h w key), sum(key^2), sum(h^2) over the lane's columns, then over the two
     // lane halves; per (copy, pair of slices, token) the three sums go to the workspace.
-    // Stream rows come in with full-line, non-temporal direct-to-LDS loads issued by the storer waves
-    // (which have no slab loads to wait for), each for its own 4 KB area of a round's 32 KB region and
-    // for the area of its SIMD partner (loader wave w - 4: same tokens, the slice 128 columns to the
-    // left): row t of an area is token t's 128 bytes, 16-byte piece p at slot p ^ ((t >> 1) & 7), so
-    // the lane-layout reads below are conflict-free.  The rows are fetched ahead so that the epilogue
-    // rarely waits for HBM: round 0 into the exchange region while the tile's main loop runs, rounds 1
-    // and 2 into the stage the tile's last slab frees (the next tile's second slab is loaded into it
-    // only after the epilogue), round 3 into the exchange region once round 0 is reduced.  Loader waves
-    // hand their sums to their partner, which stores both, so loaders never have stores outstanding.
+    // Stream rows come in with full-line, non-temporal direct-to-LDS loads into a 4 KB area per wave and
+    // round (row t of an area is token t's 128 bytes, 16-byte piece p at slot p ^ ((t >> 1) & 7), so the
+    // lane-layout reads below are conflict-free).  Round 0 goes into the exchange region while the
+    // tile's main loop runs, loaded by the storer waves (which have no slab loads to wait for) for
+    // their own area and for their SIMD partner's (loader wave w - 4: same tokens, the slice 128
+    // columns to the left).  Rounds 1 and 2 go into the stage the tile's last slab frees (the next
+    // tile's second slab is loaded into it only after the epilogue) and round 3 into the exchange
+    // region once round 0 is reduced; each wave loads these for its own area and waits only for its
+    // own loads, so the rounds need no workgroup barrier.  Loader waves hand their sums to their
+    // partner, which stores both, so loaders never have stores outstanding at a slab barrier.
     auto round_region = [&](int i, int free_stage) -> uint8_t* {
         return (i == 1 || i == 2) ? lds + free_stage * kStageBytes + (i - 1) * kExBytes : ex;
     };
     // storer wave: round i's 32 rows of its own area (v = 0) and its partner's (v = 1) into `region`,
     // 8 rows of 8 pieces per instruction (8 loads)
-    auto dma_x = [&](int64_t m0, int n0, int i, uint8_t* region) {
+    auto dma_x = [&](int64_t m0, int n0, int i, uint8_t* region, auto both_tag) {
+        constexpr int kAreas = decltype(both_tag)::value ? 2 : 1;
         const int ll = lane_id();
         const int c = n0 / p.dim;
         const int colw = n0 - c * p.dim;
         const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
+        for (int v = 0; v < kAreas; ++v) {
             const int ow = wave - 4 * v;  // owner wave of the area
             const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
 #pragma unroll
@@ -399,7 +401,22 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             }
         }
     };
-    // On entry the storers have rounds 0, 1, 2 in flight, in that order, 8 loads each.
+    // wait for this wave's own loads down to n outstanding, and keep LDS accesses after the wait
+    auto own_wait = [&](auto n_tag) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(decltype(n_tag)::value));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto lds_fence = [&]() {  // this wave's LDS reads are done (before a load or write into the same area)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // On entry the storers have round 0 of both their areas (8 loads) and rounds 1 and 2 of their own area
+    // (4 loads each) in flight, the loaders rounds 1 and 2 of their own area.  Round 0 reaches the loaders
+    // through the one barrier; every later round is the wave's own loads, so it only waits for them.
     auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0, int free_stage) {
         const int l = lane_id();
         const int c = n0 / p.dim;
@@ -418,19 +435,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
                 wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
             }
+        if (!loader) own_wait(std::integral_constant<int, 8>{});
+        sync_epi();  // round 0's stream rows are in, for every wave
         float res[4][3];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // loads issued after round i's: rounds 1 and 2 (before round 0 is reduced), round 3 after it
-            if (!loader) {
-                if (i < 2)
-                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
-                else if (i == 2)
-                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
-                else
-                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-            }
-            sync_epi();  // round i's stream rows are in
+            if (i == 1) own_wait(std::integral_constant<int, 8>{});  // rounds 2 and 3 may still be in flight
+            if (i == 2) own_wait(std::integral_constant<int, 4>{});
+            if (i == 3) own_wait(std::integral_constant<int, 0>{});
             const uint8_t* xl = round_region(i, free_stage) + wave * kXArea;
             u32x2 xr[2][4];
             {
@@ -441,6 +453,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     for (int gq = 0; gq < 4; ++gq)
                         xr[j][gq] = *reinterpret_cast<const u32x2*>(
                             xl + rr * 128 + (((4 * j + gq) ^ ((rr >> 1) & 7)) << 4) + h * 8);
+            }
+            if (i == 0) {
+                lds_fence();  // round 0 is read out of this wave's area: round 3 goes there
+                dma_x(m0, n0, 3, ex, std::false_type{});
             }
             float hwk = 0.f, kk = 0.f, hh = 0.f;
 #pragma unroll
@@ -462,20 +478,18 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
             res[i][2] = hh + __shfl_xor(hh, 32, 64);
-            if (i == 0) {
-                sync_epi();  // every wave has read round 0's rows: the exchange region takes round 3
-                if (!loader) dma_x(m0, n0, 3, ex);
-            }
         }
-        // hand-over: a loader wave leaves its sums in its own area of the exchange region (round 3 has
-        // been read by every wave once the barrier below has passed... so the sums go in after it)
-        sync_epi();
+        // hand-over: a loader wave leaves its sums in its own area of the exchange region (it has read its
+        // round 3 there); its SIMD partner adds them to its own and stores both
         uint8_t* xl = ex + wave * kXArea;
-        if (loader && l < 32) {
+        if (loader) {
+            lds_fence();
+            if (l < 32) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int q = 0; q < 3; ++q) reinterpret_cast<float*>(xl)[(i * 3 + q) * 32 + l] = res[i][q];
+                    for (int q = 0; q < 3; ++q) reinterpret_cast<float*>(xl)[(i * 3 + q) * 32 + l] = res[i][q];
+            }
         }
         sync_epi();
         if (!loader) {
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 }
             }
         }
-        sync_epi();  // the partner's sums are read before the region is reused
+        sync_epi();  // the partner's sums and the stream rows in the freed stage are read before reuse
     };
 
     if (static_cast<int>(blockIdx.x) >= tiles) return;
@@ -530,7 +544,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         int stage = 0;
         // One slab: four k-steps of 8 MFMAs, one barrier before the last.  kDefer (the last slab of a
         // fused key tile): the freed stage is kept for the epilogue's stream rows -- the loaders skip the
-        // slab after next (issued after the epilogue) and the storers fetch rounds 1 and 2 into it.
+        // slab after next (issued after the epilogue) and every wave fetches its rounds 1 and 2 into it.
         auto slab = [&](auto defer_tag, auto first_tag, int64_t m0, int n0) {
             constexpr bool kDefer = decltype(defer_tag)::value;
             constexpr bool kFirst = decltype(first_tag)::value;
@@ -568,19 +582,19 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 }
-            } else if (!kLoader && kDefer) {
-                dma_x(m0, n0, 1, round_region(1, stage));
-                dma_x(m0, n0, 2, round_region(2, stage));
+            } else if (kDefer) {
+                dma_x(m0, n0, 1, round_region(1, stage), std::false_type{});
+                dma_x(m0, n0, 2, round_region(2, stage), std::false_type{});
                 mfma_step8(acc, fa1, fw1);
 #pragma unroll
                 for (int s6 = 0; s6 < 6; ++s6) {
                     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 }
             } else {
@@ -597,7 +611,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             const bool key_tile = kGate && n0 < p.out_col0;
             if (key_tile) {
                 // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
-                if (!kLoader) dma_x(m0, n0, 0, ex);
+                if (!kLoader) dma_x(m0, n0, 0, ex, std::true_type{});
                 int free_stage = stage;
                 if (KT == 1) {
                     slab(std::true_type{}, std::true_type{}, m0, n0);
