@@ -36,6 +36,10 @@
 // - Tile order: workgroups are dispatched round-robin over the 8 XCDs; tiles
 //   are renumbered so each XCD walks a contiguous run, grouped 8 M-tiles deep,
 //   so the 32 tiles resident on an XCD share A and W panels in its L2.
+// - Launches whose 256-token tiles would leave CUs idle (a decode step of a
+//   few hundred tokens: 100 tiles for 256 CUs) use 128 x 256 tiles instead
+//   (NI = 2 token blocks per wave, 64 x 64 per wave, 48 KB stages), as long
+//   as those still fit the CUs in one pass: twice the CUs at work.
 // - K not a multiple of 64: a register-staged four-wave variant with a
 //   zero-filled K tail.
 #include <type_traits>
@@ -187,35 +191,50 @@ __device__ inline void store_tile(const WkvArgs& p, const f32x16 (&acc)[4][4], i
 // ============================================================================
 constexpr int kWaves = 8;                      // two per SIMD
 constexpr int kMainThreads = 64 * kWaves;
-constexpr int kOpBytes = BM * BK * 2;          // one operand slab: 256 rows x 128 B = 32 KB
-constexpr int kStageBytes = 2 * kOpBytes;      // A slab + W slab
+constexpr int kOpBytes = BN * BK * 2;          // the W slab: 256 rows x 128 B = 32 KB
 constexpr int kExBytes = 64 * 512;             // epilogue exchange: 64 token rows x 256 outputs (bf16)
 constexpr int kXArea = 32 * 128;               // a wave's stream rows for one round: 32 tokens x 64 bf16
 
-// the eight-wave tile: wave (wm, wn) owns tokens [128 wm, +128) x outputs [64 wn, +64), as 4 x 2 MFMA blocks
-__device__ inline void mfma_step8(f32x16 (&acc)[4][2], const bf16x8* fa, const bf16x8* fw) {
+// the eight-wave tile: wave (wm, wn) owns tokens [32 NI wm, +32 NI) x outputs [64 wn, +64), as NI x 2 MFMA
+// blocks (NI = 4: a 256 x 256 workgroup tile; NI = 2: 128 x 256, for launches too small to fill the CUs)
+template <int NI>
+__device__ inline void mfma_step8(f32x16 (&acc)[NI][2], const bf16x8* fa, const bf16x8* fw) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-// the first k-step of a tile: C = 0 (no separate zeroing of the 128 accumulators)
-__device__ inline void mfma_step8_zero(f32x16 (&acc)[4][2], const bf16x8* fa, const bf16x8* fw) {
+// the first k-step of a tile: C = 0 (no separate zeroing of the accumulators)
+template <int NI>
+__device__ inline void mfma_step8_zero(f32x16 (&acc)[NI][2], const bf16x8* fa, const bf16x8* fw) {
     const f32x16 z = {};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], z, 0, 0, 0);
 }
 
-// the 6 fragment reads of the next k-step spread among the 8 MFMAs of this one
-__device__ inline void interleave_reads8() {
+// The NI + 2 fragment reads of the next k-step spread among the 2 NI MFMAs of this one, and with them
+// V global loads (V / (2 NI) per MFMA).
+template <int NI, int V>
+__device__ inline void interleave8() {
+    constexpr int kReads = NI + 2, kMfmas = 2 * NI;
+    if (V == 0) {
 #pragma unroll
-    for (int s = 0; s < 6; ++s) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        for (int s = 0; s < kReads; ++s) {
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        }
+    } else {
+        static_assert(V % kMfmas == 0, "loads spread evenly over the MFMAs");
+#pragma unroll
+        for (int s = 0; s < kMfmas; ++s) {
+            if (s < kReads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmem, V / kMfmas, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        }
     }
 }
 
@@ -230,9 +249,13 @@ struct SlabCursor {
 // was a matrix-core bubble, measured at ~20 % of the main loop).  A wave's vmcnt counts its loads and
 // stores together and the slab barrier must wait for the loads, so the roles stay split: loaders never
 // have stores outstanding, storers never wait for slab loads.
-template <bool kGate>
+template <bool kGate, int NI>
 __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
-    // [stage][A|W][256 rows][128 B] + exchange region: 160 KB, the whole LDS of a CU
+    constexpr int kBM = 64 * NI;               // tokens per tile
+    constexpr int kABytes = kBM * BK * 2;      // the A slab: kBM rows x 128 B
+    constexpr int kStageBytes = kABytes + kOpBytes;
+    constexpr int kSlabLoads = 2 * NI + 8;     // direct-to-LDS loads per loader wave and slab
+    // [stage][A (kBM rows) | W (256 rows)][128 B] + exchange region: 160 KB at NI = 4, the whole LDS of a CU
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
 
     const int tiles = p.tiles_m * p.tiles_n;
@@ -261,40 +284,44 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- loader waves: wave w fills rows [64w, 64w+64) of both operand slabs, 8 rows per
-    // instruction; lane l lands at slot (l & 7) of row 64w + 8q + (l >> 3) and fetches the 16-byte
-    // piece the swizzle puts there.  Buffer loads: the tile's rows are a buffer resource (SGPRs) whose
-    // size stops at the last valid row, so rows past M or N read as zero instead of faulting; a lane's
-    // offset is one of two 32-bit bases (the swizzle key of row 64w + 8q + r is ((r >> 1) | 4(q & 1)))
-    // plus the instruction's row offset.
+    // ---- loader waves: wave w fills rows [16 NI w, +16 NI) of the A slab and [64w, 64w+64) of the W
+    // slab, 8 rows per instruction; lane l lands at slot (l & 7) of row base + 8q + (l >> 3) and fetches
+    // the 16-byte piece the swizzle puts there.  Buffer loads: the tile's rows are a buffer resource
+    // (SGPRs) whose size stops at the last valid row, so rows past M or N read as zero instead of
+    // faulting; a lane's offset is one of two 32-bit bases (every base is a multiple of 16 rows, so the
+    // swizzle key of row base + 8q + r is ((r >> 1) | 4(q & 1))) plus the instruction's row offset.
     const int ld_r = lane >> 3, ld_slot = lane & 7;
     const int row_bytes = p.K * 2;
-    const uint32_t vo_even = static_cast<uint32_t>((wave * 64 + ld_r) * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
-    const uint32_t vo_odd = vo_even ^ (4u << 4);
+    const uint32_t vo_piece = static_cast<uint32_t>(ld_r * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
+    const uint32_t vo_a = vo_piece + static_cast<uint32_t>(wave * 16 * NI * row_bytes);
+    const uint32_t vo_w = vo_piece + static_cast<uint32_t>(wave * 64 * row_bytes);
     // `live` false (past this workgroup's last slab) still issues the instructions, against an empty
     // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
     // block as the MFMAs they are interleaved with.  An empty resource zero-fills a free stage.
     auto issue_slab = [&](const SlabCursor& c, int stage, bool live) {
         int tm, tn;
         tile_coords(p, live ? c.pid : static_cast<int>(blockIdx.x), tm, tn);
-        const int64_t m0 = static_cast<int64_t>(tm) * BM;
+        const int64_t m0 = static_cast<int64_t>(tm) * kBM;
         const int n0 = tn * BN;
-        const int rows_a = live ? static_cast<int>(min<int64_t>(BM, p.M - m0)) : 0;
+        const int rows_a = live ? static_cast<int>(min<int64_t>(kBM, p.M - m0)) : 0;
         const int rows_w = live ? min(BN, p.N - n0) : 0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(p.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(p.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
         const uint32_t k0b = static_cast<uint32_t>(c.kt * BK * 2);
-        uint8_t* sa = lds + stage * kStageBytes + wave * 64 * 128;
-        uint8_t* sw = sa + kOpBytes;
+        uint8_t* sa = lds + stage * kStageBytes + wave * 16 * NI * 128;
+        uint8_t* sw = lds + stage * kStageBytes + kABytes + wave * 64 * 128;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             // the row offset goes into the VGPR offset: a raw buffer's range check covers the VGPR and
             // immediate offsets but not the SGPR offset, which carries only the slab's column
-            const uint32_t vo = ((q & 1) ? vo_odd : vo_even) + static_cast<uint32_t>(q * 8 * row_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + q * 8 * 128, 16, vo, k0b, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, vo, k0b, 0, 0);
+            // (row bases are multiples of 128 bytes: the XOR flips the piece's swizzle bit only)
+            const uint32_t flip = (q & 1) ? (4u << 4) : 0u;
+            const uint32_t qrows = static_cast<uint32_t>(q * 8 * row_bytes);
+            if (q < 2 * NI)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + q * 8 * 128, 16, (vo_a ^ flip) + qrows, k0b, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, sw + q * 8 * 128, 16, (vo_w ^ flip) + qrows, k0b, 0, 0);
         }
     };
     auto advance = [&](SlabCursor& c) {  // branch-free: it sits inside the interleaved block
@@ -305,23 +332,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 
     // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
     const int g = (lane >> 1) & 7;  // swizzle key of the lane's rows (every block starts at a multiple of 16)
-    const int a_row = (wm * 128 + (lane & 31)) * 128;
-    const int w_row = kOpBytes + (wn * 64 + (lane & 31)) * 128;
+    const int a_row = (wm * 32 * NI + (lane & 31)) * 128;
+    const int w_row = kABytes + (wn * 64 + (lane & 31)) * 128;
     auto read_frags = [&](int stage, int kk, bf16x8* fa, bf16x8* fw) {
         const uint8_t* base = lds + stage * kStageBytes;
         const int off = (((2 * kk + (lane >> 5)) ^ g) << 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * 128 + off);
+        for (int i = 0; i < NI; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * 128 + off);
 #pragma unroll
         for (int j = 0; j < 2; ++j) fw[j] = *reinterpret_cast<const bf16x8*>(base + w_row + j * 32 * 128 + off);
     };
 
-    // ---- epilogue: 4 rounds; in round i every wave puts its tokens 32i..32i+31 (64 outputs each) into
+    // ---- epilogue: NI rounds; in round i every wave puts its tokens 32i..32i+31 (64 outputs each) into
     // the exchange region (64 rows of 512 B: row 32 wm + t, 16-byte pieces XOR-swizzled by row), then the
     // four storer waves write 16 whole rows each with full-line, non-temporal 16-byte stores (kv is not
     // read again here)
     uint8_t* ex = lds + 2 * kStageBytes;
-    auto epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
+    auto epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0) {
         // Every lane-derived address below is rebuilt from a freshly computed lane id, so the compiler
         // cannot hoist the epilogue addresses out of the tile loop (where they would pin VGPRs for the
         // whole kernel).
@@ -329,7 +356,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         const int key = l & 31;
         const uint32_t wbase = static_cast<uint32_t>((wm * 32 + (l & 31)) * 512 + (l >> 5) * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -349,7 +376,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 for (int q = 0; q < 8; ++q) {
                     const int rr = 16 * s + 2 * q + hi;  // exchange row: token half rr / 32, token rr % 32
                     const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 512 + ((chunk ^ (rr & 31)) << 4));
-                    const int64_t m = m0 + (rr >> 5) * 128 + 32 * i + (rr & 31);
+                    const int64_t m = m0 + (rr >> 5) * 32 * NI + 32 * i + (rr & 31);
                     if (m < p.M && col_ok)
                         __builtin_nontemporal_store(
                             v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + (n0 - p.out_col0) + chunk * 8));
@@ -361,8 +388,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 
     // ---- fused gate epilogue of a key tile: no stores of the product.  The tile's 256 columns lie in
     // one copy c; wave (wm, wn) owns the 64-column slice s = (n0 - c dim) / 64 + wn of that copy and
-    // tokens 128 wm .. 128 wm + 127.  Lane l holds, per round i, token 32i + l%32 and 32 of the slice's
-    // columns (4 consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is
+    // tokens [32 NI wm, 32 NI (wm + 1)).  Lane l holds, per round i < NI, token 32i + l%32 and 32 of the
+    // slice's columns (4 consecutive columns per (j, gq), as the MFMA leaves them).  Each accumulator is
     // rounded to bf16 (the product is a bf16 tensor before it is used) and reduced against the stream's
     // matching element: sum(h w key), sum(key^2), sum(h^2) over the lane's columns, then over the two
     // lane halves; per (copy, pair of slices, token) the three sums go to the workspace.
@@ -373,7 +400,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // their own area and for their SIMD partner's (loader wave w - 4: same tokens, the slice 128
     // columns to the left).  Rounds 1 and 2 go into the stage the tile's last slab frees (the next
     // tile's second slab is loaded into it only after the epilogue) and round 3 into the exchange
-    // region once round 0 is reduced; each wave loads these for its own area and waits only for its
+    // region once round 0 is reduced (NI = 2: rounds 0 and 1 only); each wave loads these for its own area and waits only for its
     // own loads, so the rounds need no workgroup barrier.  Loader waves hand their sums to their
     // partner, which stores both, so loaders never have stores outstanding at a slab barrier.
     auto round_region = [&](int i, int free_stage) -> uint8_t* {
@@ -395,7 +422,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             for (int ins = 0; ins < 4; ++ins) {
                 const int r = 8 * ins + (ll >> 3);
                 const int piece = (ll & 7) ^ ((r >> 1) & 7);
-                const int64_t t = min<int64_t>(m0 + (ow & 1) * 128 + 32 * i + r, p.M - 1);  // past M: unused
+                const int64_t t = min<int64_t>(m0 + (ow & 1) * 32 * NI + 32 * i + r, p.M - 1);  // past M: unused
                 __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece, region + ow * kXArea + ins * 1024, 16,
                                                  0, kNonTemporal);
             }
@@ -414,10 +441,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
-    // On entry the storers have round 0 of both their areas (8 loads) and rounds 1 and 2 of their own area
-    // (4 loads each) in flight, the loaders rounds 1 and 2 of their own area.  Round 0 reaches the loaders
+    // On entry the storers have round 0 of both their areas (8 loads) and rounds 1 and 2 (NI = 2: round 1)
+    // of their own area (4 loads each) in flight, the loaders rounds 1 and 2 of their own area.  Round 0 reaches the loaders
     // through the one barrier; every later round is the wave's own loads, so it only waits for them.
-    auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0, int free_stage) {
+    auto gate_epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0, int free_stage) {
         const int l = lane_id();
         const int c = n0 / p.dim;
         const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice
@@ -435,13 +462,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
                 wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
             }
-        if (!loader) own_wait(std::integral_constant<int, 8>{});
+        // own loads in flight after round r has landed: rounds r+1 .. NI-1, 4 loads each
+        if (!loader) own_wait(std::integral_constant<int, 4 * (NI == 4 ? 2 : NI - 1)>{});
         sync_epi();  // round 0's stream rows are in, for every wave
-        float res[4][3];
+        float res[NI][3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i == 1) own_wait(std::integral_constant<int, 8>{});  // rounds 2 and 3 may still be in flight
-            if (i == 2) own_wait(std::integral_constant<int, 4>{});
+        for (int i = 0; i < NI; ++i) {
+            if (i == 1) own_wait(std::integral_constant<int, 4 * (NI - 2)>{});  // rounds 2 .. NI-1 may still be in flight
+            if (i == 2) own_wait(std::integral_constant<int, 4 * (NI > 3 ? NI - 3 : 0)>{});
             if (i == 3) own_wait(std::integral_constant<int, 0>{});
             const uint8_t* xl = round_region(i, free_stage) + wave * kXArea;
             u32x2 xr[2][4];
@@ -454,7 +482,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                         xr[j][gq] = *reinterpret_cast<const u32x2*>(
                             xl + rr * 128 + (((4 * j + gq) ^ ((rr >> 1) & 7)) << 4) + h * 8);
             }
-            if (i == 0) {
+            if (i == 0 && NI == 4) {
                 lds_fence();  // round 0 is read out of this wave's area: round 3 goes there
                 dma_x(m0, n0, 3, ex, std::false_type{});
             }
@@ -486,7 +514,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             lds_fence();
             if (l < 32) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
                     for (int q = 0; q < 3; ++q) reinterpret_cast<float*>(xl)[(i * 3 + q) * 32 + l] = res[i][q];
             }
@@ -498,11 +526,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             const int ls = lane_id();
             if (ls < 32) {
                 const float* partner = reinterpret_cast<const float*>(ex + (wave - 4) * kXArea);
-                const int64_t tbase = m0 + wm * 128 + ls;
+                const int64_t tbase = m0 + wm * 32 * NI + ls;
                 const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
                 float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < NI; ++i) {
                     const int64_t t = tbase + 32 * i;
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
@@ -538,8 +566,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         }
         sync();
 
-        f32x16 acc[4][2];
-        bf16x8 fa0[4], fw0[2], fa1[4], fw1[2];
+        f32x16 acc[NI][2];
+        bf16x8 fa0[NI], fw0[2], fa1[NI], fw1[2];
         read_frags(0, 0, fa0, fw0);
         int stage = 0;
         // One slab: four k-steps of 8 MFMAs, one barrier before the last.  kDefer (the last slab of a
@@ -553,60 +581,41 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 mfma_step8_zero(acc, fa0, fw0);
             else
                 mfma_step8(acc, fa0, fw0);
-            interleave_reads8();
+            interleave8<NI, 0>();
             read_frags(stage, 2, fa0, fw0);
             mfma_step8(acc, fa1, fw1);
-            interleave_reads8();
+            interleave8<NI, 0>();
             read_frags(stage, 3, fa1, fw1);
             mfma_step8(acc, fa0, fw0);
-            interleave_reads8();
+            interleave8<NI, 0>();
             // the next slab has landed and this stage is no longer read: publish one, refill the other
             if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
             sync();
             // The next slab's first fragments (the next tile's, at the end of a tile; harmless stale
-            // reads after the last one) are read under the last 8 MFMAs of this slab.
+            // reads after the last one) are read under the last 2 NI MFMAs of this slab.
             read_frags(stage ^ 1, 0, fa0, fw0);
             if (kLoader && !kDefer) {
                 issue_slab(ld, stage, issued < total_slabs_mine);  // slab after next into the freed stage
                 advance(ld);
                 ++issued;
                 mfma_step8(acc, fa1, fw1);
-#pragma unroll
-                for (int s6 = 0; s6 < 6; ++s6) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                }
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                }
+                interleave8<NI, kSlabLoads>();
             } else if (kDefer) {
+                // rounds 1 and 2 (NI = 4) or round 1 (NI = 2) of this wave's stream rows: 4 loads a round
                 dma_x(m0, n0, 1, round_region(1, stage), std::false_type{});
-                dma_x(m0, n0, 2, round_region(2, stage), std::false_type{});
+                if (NI == 4) dma_x(m0, n0, 2, round_region(2, stage), std::false_type{});
                 mfma_step8(acc, fa1, fw1);
-#pragma unroll
-                for (int s6 = 0; s6 < 6; ++s6) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                }
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                }
+                interleave8<NI, 4 * (NI == 4 ? 2 : 1)>();
             } else {
                 mfma_step8(acc, fa1, fw1);
-                interleave_reads8();
+                interleave8<NI, 0>();
             }
             stage ^= 1;
         };
         for (; pid < tiles; pid += G) {
             int tm, tn;
             tile_coords(p, pid, tm, tn);
-            const int64_t m0 = static_cast<int64_t>(tm) * BM;
+            const int64_t m0 = static_cast<int64_t>(tm) * kBM;
             const int n0 = tn * BN;
             const bool key_tile = kGate && n0 < p.out_col0;
             if (key_tile) {
@@ -757,6 +766,31 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
 
 using namespace engram;
 
+namespace {
+
+// Tokens per tile of the main kernel: 256 (NI = 4), or 128 (NI = 2) when 128-token tiles still fit the CUs
+// in one pass -- small launches (a decode step) then use twice the CUs.
+int tile_ni(int64_t T, int tiles_n) { return ((T + 127) / 128) * tiles_n <= kCUs ? 2 : 4; }
+
+// Launch the persistent main kernel over all tiles of p (p.tiles_n set; p.tiles_m filled in here).
+template <bool kGate>
+int launch_main(WkvArgs& p, int64_t T, hipStream_t stream, const char* what) {
+    const int ni = tile_ni(T, p.tiles_n);
+    const int64_t bm = 64 * ni;
+    const int64_t tiles_m = (T + bm - 1) / bm;
+    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
+    p.tiles_m = static_cast<int>(tiles_m);
+    const int64_t tiles = tiles_m * p.tiles_n;
+    const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
+    if (ni == 2)
+        hipLaunchKernelGGL((wkv_kernel<kGate, 2>), dim3(grid), dim3(kMainThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((wkv_kernel<kGate, 4>), dim3(grid), dim3(kMainThreads), 0, stream, p);
+    return check_launch(what);
+}
+
+}  // namespace
+
 extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t T, int32_t K, int32_t Nout,
                           void* stream) {
     if (T < 0) return fail(ENGRAM_EINVAL, "engram_wkv: T < 0");
@@ -774,15 +808,13 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     p.K = K;
     p.ld_out = Nout;
     p.out_col0 = 0;
-    const int64_t tiles_m = (T + BM - 1) / BM;
     p.tiles_n = (Nout + BN - 1) / BN;
-    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv: too many tiles");
-    p.tiles_m = static_cast<int>(tiles_m);
-    const int64_t tiles = tiles_m * p.tiles_n;
-    if (K % BK == 0) {
-        const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-        hipLaunchKernelGGL(wkv_kernel<false>, dim3(grid), dim3(kMainThreads), 0, as_stream(stream), p);
-    } else {
+    if (K % BK == 0) return launch_main<false>(p, T, as_stream(stream), "engram_wkv");
+    {
+        const int64_t tiles_m = (T + BM - 1) / BM;
+        if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv: too many tiles");
+        p.tiles_m = static_cast<int>(tiles_m);
+        const int64_t tiles = tiles_m * p.tiles_n;
         hipLaunchKernelGGL(wkv_kernel_staged, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
                            as_stream(stream), p);
     }
@@ -832,14 +864,8 @@ extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint1
     p.part = static_cast<float*>(workspace);
     p.hc = hc;
     p.dim = dim;
-    const int64_t tiles_m = (T + BM - 1) / BM;
     p.tiles_n = Nout / BN;
-    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tiles");
-    p.tiles_m = static_cast<int>(tiles_m);
-    const int64_t tiles = tiles_m * p.tiles_n;
-    const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-    hipLaunchKernelGGL(wkv_kernel<true>, dim3(grid), dim3(kMainThreads), 0, as_stream(stream), p);
-    int rc = check_launch("engram_wkv_gate");
+    int rc = launch_main<true>(p, T, as_stream(stream), "engram_wkv_gate");
     if (rc != ENGRAM_OK) return rc;
     const int64_t blocks = (T * hc + 255) / 256;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");

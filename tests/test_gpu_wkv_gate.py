@@ -18,8 +18,10 @@ def _rand_bf16(rng, shape, std=1.0):
     return torch.from_numpy((rng.normal(size=shape) * std).astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,K,N", [(64, 192, 1280), (1, 8, 8), (300, 200, 264), (257, 1536, 520), (513, 64, 256), (2600, 1536, 6400),
-                                   (1000, 1536, 25600)])
+# 128-token tiles where they fit the CUs in one pass (64, 257, 513, 256 and 130 tokens here; 130 leaves a
+# 2-row second tile), 256-token tiles above (2600, 1000); K not a multiple of 64 takes the staged kernel
+@pytest.mark.parametrize("T,K,N", [(64, 192, 1280), (1, 8, 8), (300, 200, 264), (257, 1536, 520), (513, 64, 256),
+                                   (256, 1536, 25600), (130, 1536, 25600), (2600, 1536, 6400), (1000, 1536, 25600)])
 def test_wkv_ragged_shapes(gpu_device, T, K, N):
     import gram_hash_embedding_amd as g
 

@@ -38,8 +38,12 @@ def _inputs(rng, T, K, hc, dim, dev):
 
 # (T, K, hc, dim): ragged token counts (tails of 44, 1, 1, 232 rows), one-copy and many-copy layouts,
 # the workload's dim with its 100 column tiles, and grids of 288 and 720 tiles, so that CUs run several
-# tiles back to back (key after key, key after value, value after key)
+# tiles back to back (key after key, key after value, value after key).  Launches whose 128-token tiles
+# fit the 256 CUs in one pass use those (all but the last three here); the decode step's 256 tokens
+# (200 tiles of 128 x 256) and a ragged 200 are on that side, 300 tokens of the same layer (3 x 100
+# tiles would not fit) on the other.
 SHAPES = [(64, 192, 1, 256), (300, 128, 2, 256), (257, 1536, 4, 512), (513, 64, 3, 768), (1, 64, 1, 256),
+          (256, 1536, 4, 5120), (200, 1536, 4, 5120), (300, 1536, 4, 5120),
           (1000, 1536, 4, 5120), (6000, 192, 3, 768), (9000, 64, 4, 1024)]
 
 
