@@ -118,6 +118,11 @@ CONFIGS = {
             compressed_vocab_size=99092, n_heads=8, n_layers=2, head_dim=64, dim=5120,
             prime_base=16000000, rows_alloc=(384006168, 384016682), token_dist="uniform",
             mask_frac=0.05),
+    # The released model's row width (engram_head_dim = 256, so K = 24 * 256 = 6144) on a table of the
+    # mid-prefill size: the path at the D the config block of the pages gives, beside the D = 64 above.
+    6: _cfg(name="released_head_dim", index=6, batch=2, seqlen=4096, start_pos=0, vocab_size=129280,
+            compressed_vocab_size=99092, n_heads=8, n_layers=1, head_dim=256, dim=5120,
+            prime_base=166000, rows_alloc=(3988006,), token_dist="zipf", mask_frac=0.05),
 }
 
 

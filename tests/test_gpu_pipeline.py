@@ -22,7 +22,7 @@ def _oracle_kv_bf16(kv64):
     return torch.from_numpy(kv64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("cfg_index,n_sample", [(1, 64), (2, 192), (3, 128), (5, 96)])
+@pytest.mark.parametrize("cfg_index,n_sample", [(1, 64), (2, 192), (3, 128), (5, 96), (6, 96)])
 def test_forward_pipeline(gpu_device, cfg_index, n_sample):
     import torch
 
