@@ -91,3 +91,52 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
             if m is not None:
                 np.testing.assert_array_equal(out_got[m == 0], x_bits[m == 0],
                                               err_msg=f"masked tokens (fused={fused}), layer {e}")
+
+
+def test_decode_pipeline(gpu_device):
+    """The decode workload as the benchmark runs it: the hash of the 4,096-token history, then 64 calls of
+    one token per sequence through the whole path (through the residual), each with its own stream, the
+    fused and the four-entry-point projection in turn.  Steps 0, 1, 62 and 63 are checked against the
+    oracle: hash ids of all 256 sequences, and on sampled sequences the gathered rows (bit-exact), the gate
+    pre-activation and the output stream (within tolerance)."""
+    import torch
+
+    import synth.workload as sw
+
+    cfg = synth.CONFIGS[4]
+    wl = sw.build(cfg, device=gpu_device, packed=True, x_steps=cfg.decode_steps)
+    hi = wl.host
+    B, Ltot = hi.input_ids.shape
+    P, E, C, D, blk = cfg.start_pos, cfg.n_layers, cfg.n_hash_cols, cfg.head_dim, cfg.block_size
+    hc, dim = cfg.hc_mult, cfg.dim
+    ids_all = oracle.hash(hi.input_ids, 0, None, hi.token_map, np.zeros((B, Ltot), np.int64), hi.multipliers,
+                          hi.primes, hi.offsets, cfg.pad_id, synth.DEAD)
+    wl.fwd.hash(wl.input_ids[:, :P].contiguous(), 0)
+    rng = np.random.default_rng(4)
+    seqs = np.unique(np.r_[0, 1, B - 1, rng.integers(0, B, 29)])
+    sidx = torch.from_numpy(seqs).to(gpu_device)
+    checked = {0, 1, cfg.decode_steps - 2, cfg.decode_steps - 1}
+    for s in range(cfg.decode_steps):
+        fused = s % 2 == 0
+        outs = wl.fwd.step(wl.input_ids[:, P + s:P + s + 1].contiguous(), P + s, wl.x[s], None, output=True,
+                           fused=fused, packed=True)
+        if s not in checked:
+            continue
+        torch.cuda.synchronize()
+        ids_got = wl.fwd._bufs["ids"][:B * E * C].view(B, E, C).cpu().numpy()  # (the buffer held the prefill)
+        np.testing.assert_array_equal(ids_got, ids_all[:, P + s], err_msg=f"hash ids, step {s}")
+        x_bits = bits(wl.x[s].view(B, hc, dim)[sidx])
+        for e in range(E):
+            lw = wl.fwd.layers[e]
+            cw, cs, remap = compact_rows(ids_all[seqs, P + s, e], cfg.rows_alloc[e], synth.table_seed(cfg, e), D,
+                                         blk)
+            a_want = oracle.gather_dequant(remap, cw, cs, block_size=blk).reshape(len(seqs), C * D)
+            a_got = bits(wl.fwd._bufs[("a", e)][:B * C * D].view(B, C * D)[sidx])
+            np.testing.assert_array_equal(a_got, a_want, err_msg=f"gathered rows, step {s}, layer {e}")
+            kv_want = _oracle_kv_bf16(oracle.wkv(a_want, bits(lw.wkv)))
+            dot_want = oracle.gate_dot(x_bits, kv_want, bits(lw.q_weight), bits(lw.k_weight), cfg.eps)
+            dot_got = wl.fwd._bufs[("dot", e)][:B * hc].view(B, hc)[sidx].cpu().numpy()
+            assert_close(dot_got, dot_want, what=f"dot, step {s}, layer {e}, fused={fused}")
+            _, out_want = oracle.gate_output(x_bits, kv_want, dot_want, None)
+            out_got = bits(outs[e].view(B, hc, dim)[sidx])
+            assert_close(oracle.bf16_bits_to_float(out_got), out_want, what=f"out, step {s}, layer {e}, fused={fused}")
