@@ -751,11 +751,28 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
     const int c = static_cast<int>(idx / M);  // consecutive threads: consecutive tokens of one copy
     const int64_t t = idx - static_cast<int64_t>(c) * M;
     const float* src = part + static_cast<int64_t>(c) * slices * 3 * M + t;
+    // The slices' loads go out in batches of kBatch (3 kBatch independent loads in flight per thread), so a
+    // small launch pays a few memory latencies rather than one per slice; the sums still run in slice order.
+    constexpr int kBatch = 8;
     float hwk = 0.f, kk = 0.f, hh = 0.f;
-    for (int s = 0; s < slices; ++s) {
-        hwk += src[(3 * s + 0) * M];
-        kk += src[(3 * s + 1) * M];
-        hh += src[(3 * s + 2) * M];
+    int s0 = 0;
+    for (; s0 + kBatch <= slices; s0 += kBatch) {
+        float v[kBatch][3];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) v[b][q] = src[(3 * (s0 + b) + q) * M];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            hwk += v[b][0];
+            kk += v[b][1];
+            hh += v[b][2];
+        }
+    }
+    for (; s0 < slices; ++s0) {
+        hwk += src[(3 * s0 + 0) * M];
+        kk += src[(3 * s0 + 1) * M];
+        hh += src[(3 * s0 + 2) * M];
     }
     const float rstd = rsqrtf(hh * inv_dim + eps) * rsqrtf(kk * inv_dim + eps);
     dot[t * hc + c] = hwk * rstd * rsqrt_dim;
