@@ -24,6 +24,10 @@ One step is timed five ways, each its own loop of `--steps` steps:
   unfused         the same path as four entry points (kv written, then read)
   module_fused    the whole module: fused path + gate, mask and residual
   module_unfused  the whole module: unfused projection + fused dot/gate/residual
+The decode workload (64 one-token calls per step) also replays the fused and
+unfused steps as HIP graphs (`fused_graph`, `unfused_graph`): launched one by
+one from Python the GPU waits on the host between kernels, so there `value`
+comes from the graph replay of the fused step (`config.launch`).
 Prints one JSON line: whole-job tokens/s, every path's time, per-kernel
 timings from HIP events on the launch stream, the roofline of the dominant
 kernel (the fused projection, bf16 MFMA), and the CPU oracle's throughput on
@@ -200,8 +204,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
 
-    def loop(fused, output, packed):
-        """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
+    def make_step(fused, output, packed):
         def step(events=None):
             if cfg.decode_steps:
                 for s in range(cfg.decode_steps):
@@ -210,6 +213,11 @@ def main(argv=None):
             else:
                 fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output,
                          fused=fused, packed=packed)
+        return step
+
+    def loop(fused, output, packed):
+        """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
+        step = make_step(fused, output, packed)
 
         for _ in range(args.warmup):
             step()
@@ -240,6 +248,34 @@ def main(argv=None):
         for k, v in ev.items():
             kern_events.setdefault(k, v)  # the first loop that runs a kernel times it
     sec_main = paths["fused"]["ms_per_step"] / 1e3
+    value_mode = "eager"
+    if cfg.decode_steps:
+        # A decode step is 64 small calls: launched one by one from Python, the GPU waits on the host between
+        # kernels.  The same step captured once as a HIP graph (the library's launches on torch's capture
+        # stream; every buffer already allocated) and replayed measures the path itself; that is `value`.
+        for name, fused, output in (("fused", True, False), ("unfused", False, False)):
+            step = make_step(fused, output, main_packed)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                graph.replay()
+            torch.cuda.synchronize()
+            sec = (time.perf_counter() - t0) / args.steps
+            paths[name + "_graph"] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
+                                      "table": "packed" if main_packed else "pages"}
+            del graph
+        sec_main = paths["fused_graph"]["ms_per_step"] / 1e3
+        value_mode = "hip_graph"
     value = T / sec_main
 
     algo = algorithmic(cfg, wl.token_mask is not None)
@@ -298,6 +334,7 @@ def main(argv=None):
             "seq_len": cfg.seqlen,
             "tokens_per_step": T,
             "decode_steps": cfg.decode_steps,
+            "launch": value_mode,
             "engram_layers": E,
             "table_rows": list(cfg.rows_alloc[:E]),
             "head_dim": cfg.head_dim,

@@ -19,7 +19,10 @@
 //   each layer in LDS.
 // - Phase 2, all 256 lanes: one output id per lane and step, so the int64
 //   stores of the tile ([64 tokens, E, C] contiguous) are fully coalesced.
-//   Each id costs one 64-bit floor modulo.
+//   Each id costs one 64-bit floor modulo, done as a Barrett reduction
+//   (a 64 x 64 -> high-64 multiply by floor((2^64 - 1) / p), at most two
+//   corrections) with the E * C reciprocals computed once per workgroup
+//   into LDS: exact integer arithmetic, without a 64-bit division per id.
 #include "common.h"
 
 namespace engram {
@@ -46,13 +49,22 @@ struct HashArgs {
     int64_t* out;
 };
 
+// x mod p for x < 2^64 and p >= 1, given m = floor((2^64 - 1) / p): q = floor(x m / 2^64) is at most 2 below
+// floor(x / p) (x m / 2^64 > x / p - x / (p 2^64) - x / 2^64 > x / p - 2), so x - q p lies in [0, 3p).
+__device__ inline uint64_t mod_barrett(uint64_t x, uint64_t p, uint64_t m) {
+    uint64_t r = x - __umul64hi(x, m) * p;
+    if (r >= p) r -= p;
+    if (r >= p) r -= p;
+    return r;
+}
+
 // floor modulo by a positive divisor: the result takes the divisor's sign.
-__device__ inline int64_t floor_mod_pos(int64_t r, int64_t p) {
+__device__ inline int64_t floor_mod_pos(int64_t r, int64_t p, uint64_t m) {
     const uint64_t up = static_cast<uint64_t>(p);
-    if (r >= 0) return static_cast<int64_t>(static_cast<uint64_t>(r) % up);
+    if (r >= 0) return static_cast<int64_t>(mod_barrett(static_cast<uint64_t>(r), up, m));
     // r < 0:  r = -(a + 1) with a = ~r >= 0, and floormod(r, p) = p - 1 - (a mod p)
     const uint64_t a = ~static_cast<uint64_t>(r);
-    return static_cast<int64_t>(up - 1 - a % up);
+    return static_cast<int64_t>(up - 1 - mod_barrett(a, up, m));
 }
 
 __device__ inline int64_t compressed_id(const HashArgs& a, int64_t flat) {
@@ -63,11 +75,17 @@ __device__ inline int64_t compressed_id(const HashArgs& a, int64_t flat) {
 }
 
 __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
-    extern __shared__ int64_t roll[];  // [kTileTokens][E][N-1]
+    extern __shared__ int64_t roll[];  // [kTileTokens][E][N-1], then the reciprocals [E][C]
     const int NR = a.N - 1;
     const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kTileTokens;
     const int ntok = static_cast<int>(min<int64_t>(kTileTokens, a.T - tile0));
     const int tid = threadIdx.x;
+    const int EC = a.E * a.C;
+    uint64_t* recip = reinterpret_cast<uint64_t*>(roll + kTileTokens * a.E * NR);
+    for (int i = tid; i < EC; i += kThreads) {
+        const uint64_t p = static_cast<uint64_t>(a.primes[i]);  // [E, N-1, H] flat = [E, C] in column order
+        recip[i] = p != 0 ? ~0ull / p : 0;
+    }
 
     if (tid < ntok) {
         const int64_t t = tile0 + tid;
@@ -110,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
     }
     __syncthreads();
 
-    const int EC = a.E * a.C;
     const int total = ntok * EC;
     int64_t* out = a.out + tile0 * EC;
     for (int idx = tid; idx < total; idx += kThreads) {
@@ -121,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
         const int n1 = col / a.H;  // n-gram size minus 2
         const int h = col - n1 * a.H;
         const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
-        const int64_t prime = a.primes[(static_cast<int64_t>(e) * NR + n1) * a.H + h];
-        out[idx] = floor_mod_pos(r, prime) + a.offsets[static_cast<int64_t>(e) * a.C + col];
+        const int pc = e * a.C + col;  // = (e * (N-1) + n1) * H + h
+        out[idx] = floor_mod_pos(r, a.primes[pc], recip[pc]) + a.offsets[pc];
     }
 }
 
@@ -178,7 +195,7 @@ extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64
     a.out = hash_ids;
     const int64_t blocks = (T + kTileTokens - 1) / kTileTokens;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_hash: too many tokens");
-    const size_t smem = sizeof(int64_t) * kTileTokens * E * (N - 1);
+    const size_t smem = sizeof(int64_t) * (kTileTokens * E * (N - 1) + static_cast<size_t>(E) * (N - 1) * H);
     hipLaunchKernelGGL(hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, as_stream(stream), a);
     return check_launch("engram_hash");
 }

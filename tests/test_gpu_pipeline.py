@@ -140,3 +140,55 @@ def test_decode_pipeline(gpu_device):
             _, out_want = oracle.gate_output(x_bits, kv_want, dot_want, None)
             out_got = bits(outs[e].view(B, hc, dim)[sidx])
             assert_close(oracle.bf16_bits_to_float(out_got), out_want, what=f"out, step {s}, layer {e}, fused={fused}")
+
+
+def test_decode_step_graph_replays_match_eager(gpu_device):
+    """The benchmark replays the decode step as a HIP graph: a graph of 8 one-token calls (fused and
+    four-entry-point projections alternating) replayed three times, with eager work and synchronisations in
+    between, gives every call's dot and output bit for bit as the eager calls do, and leaves the same cache."""
+    import torch
+
+    import synth.workload as sw
+
+    cfg = synth.CONFIGS[4]
+    steps = 8
+    wl = sw.build(cfg, device=gpu_device, packed=True, x_steps=steps)
+    P, E, hc = cfg.start_pos, cfg.n_layers, cfg.hc_mult
+    B = cfg.batch
+    wl.fwd.hash(wl.input_ids[:, :P].contiguous(), 0)
+    step_ids = [wl.input_ids[:, P + s:P + s + 1].contiguous() for s in range(steps)]
+    hist = torch.zeros((steps, E, B, hc), dtype=torch.float32, device=gpu_device)
+    outs_hist = torch.zeros((steps, E) + tuple(wl.x[0].shape), dtype=torch.bfloat16, device=gpu_device)
+
+    def run():
+        for s in range(steps):
+            outs = wl.fwd.step(step_ids[s], P + s, wl.x[s], None, output=True, fused=s % 2 == 0, packed=True)
+            for e in range(E):
+                hist[s, e].copy_(wl.fwd._bufs[("dot", e)][:B * hc].view(B, hc))
+                outs_hist[s, e].copy_(outs[e])
+
+    run()  # eager (also allocates every buffer the step uses)
+    torch.cuda.synchronize()
+    want_dot, want_out = hist.clone(), outs_hist.clone()
+    want_cache = wl.fwd.state.cache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for r in range(3):
+        hist.zero_()
+        outs_hist.zero_()
+        wl.fwd.state.cache[:, P:P + steps].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hist, want_dot), f"replay {r}: dots"
+        assert torch.equal(outs_hist.view(torch.int16), want_out.view(torch.int16)), f"replay {r}: outputs"
+        assert torch.equal(wl.fwd.state.cache, want_cache), f"replay {r}: cache"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(hist, want_dot), f"eager after replay {r}"
