@@ -21,8 +21,9 @@
 //   stores of the tile ([64 tokens, E, C] contiguous) are fully coalesced.
 //   Each id costs one 64-bit floor modulo, done as a Barrett reduction
 //   (a 64 x 64 -> high-64 multiply by floor((2^64 - 1) / p), at most two
-//   corrections) with the E * C reciprocals computed once per workgroup
-//   into LDS: exact integer arithmetic, without a 64-bit division per id.
+//   corrections): exact integer arithmetic, without a 64-bit division per
+//   id.  A lane keeps one (layer, column) for the whole tile, so its prime,
+//   offset and reciprocal are fetched and computed once.
 #include "common.h"
 
 namespace engram {
@@ -67,32 +68,43 @@ __device__ inline int64_t floor_mod_pos(int64_t r, int64_t p, uint64_t m) {
     return static_cast<int64_t>(up - 1 - mod_barrett(a, up, m));
 }
 
-__device__ inline int64_t compressed_id(const HashArgs& a, int64_t flat) {
-    const int64_t id = a.input_ids[flat];
-    int64_t v = (id >= 0 && id < a.vocab) ? a.token_map[id] : a.dead;
-    if (a.mask != nullptr && a.mask[flat] == 0) v = a.dead;
-    return v;
-}
-
 __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
-    extern __shared__ int64_t roll[];  // [kTileTokens][E][N-1], then the reciprocals [E][C]
+    extern __shared__ int64_t roll[];  // [kTileTokens][E][N-1]
     const int NR = a.N - 1;
     const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kTileTokens;
     const int ntok = static_cast<int>(min<int64_t>(kTileTokens, a.T - tile0));
     const int tid = threadIdx.x;
     const int EC = a.E * a.C;
-    uint64_t* recip = reinterpret_cast<uint64_t*>(roll + kTileTokens * a.E * NR);
-    for (int i = tid; i < EC; i += kThreads) {
-        const uint64_t p = static_cast<uint64_t>(a.primes[i]);  // [E, N-1, H] flat = [E, C] in column order
-        recip[i] = p != 0 ? ~0ull / p : 0;
-    }
 
     if (tid < ntok) {
         const int64_t t = tile0 + tid;
         const int64_t b = t / a.L;
         const int64_t l = t - b * a.L;
         const int64_t p = a.start_pos + l;
+        // Every slot's loads go out together (indices clamped into range, results selected afterwards), so
+        // the window costs two memory round trips (ids, then token_map) rather than one per slot.
+        int64_t raw[kMaxN], cached[kMaxN];
+        uint8_t mk[kMaxN];
+#pragma unroll
+        for (int s = 0; s < kMaxN; ++s) {
+            if (s < a.N) {
+                const int64_t flat = b * a.L + (l >= s ? l - s : 0);
+                const int64_t cpos = b * a.cache_L + (p >= s ? p - s : 0);
+                raw[s] = a.input_ids[flat];
+                mk[s] = a.mask != nullptr ? a.mask[flat] : 1;
+                cached[s] = a.cache[cpos];  // written by an earlier call
+            }
+        }
         int64_t slot[kMaxN];
+#pragma unroll
+        for (int s = 0; s < kMaxN; ++s) {
+            if (s < a.N) {
+                const int64_t id = raw[s];
+                const bool in_vocab = id >= 0 && id < a.vocab;
+                const int64_t mapped = a.token_map[in_vocab ? id : 0];
+                slot[s] = (in_vocab && mk[s] != 0) ? mapped : a.dead;
+            }
+        }
         bool blocked = false;
 #pragma unroll
         for (int s = 0; s < kMaxN; ++s) {
@@ -100,13 +112,8 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
                 if (p < s) {
                     blocked = true;  // before the start of the sequence
                 } else {
-                    int64_t v;
-                    if (l - s >= 0) {
-                        v = compressed_id(a, b * a.L + (l - s));
-                        if (s == 0) a.cache[b * a.cache_L + p] = v;
-                    } else {
-                        v = a.cache[b * a.cache_L + (p - s)];  // written by an earlier call
-                    }
+                    const int64_t v = l - s >= 0 ? slot[s] : cached[s];
+                    if (s == 0) a.cache[b * a.cache_L + p] = v;
                     if (v == a.dead) blocked = true;
                     slot[s] = v;
                 }
@@ -130,16 +137,32 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
 
     const int total = ntok * EC;
     int64_t* out = a.out + tile0 * EC;
-    for (int idx = tid; idx < total; idx += kThreads) {
+    if (EC <= kThreads) {
+        // Lane l keeps one (layer, column) pc = l % EC for the whole tile: its prime, offset and Barrett
+        // reciprocal are fetched once, then it walks tokens l / EC, + G, + 2G, ... (G = 256 / EC); the
+        // lanes of one step write G consecutive token rows, so the stores stay coalesced.
+        const int G = kThreads / EC;
+        if (tid >= G * EC) return;
+        const int pc = tid % EC;  // = e * C + (n - 2) * H + h: primes [E, N-1, H] flat is [E, C] in column order
+        const int e = pc / a.C;
+        const int n1 = (pc - e * a.C) / a.H;  // n-gram size minus 2
+        const int64_t prime = a.primes[pc];
+        const int64_t off = a.offsets[pc];
+        const uint64_t m = prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0;
+        for (int i = tid / EC; i < ntok; i += G) {
+            const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
+            out[i * EC + pc] = floor_mod_pos(r, prime, m) + off;
+        }
+        return;
+    }
+    for (int idx = tid; idx < total; idx += kThreads) {  // more than 256 ids per token: one id per lane and step
         const int i = idx / EC;
-        const int rem = idx - i * EC;
-        const int e = rem / a.C;
-        const int col = rem - e * a.C;
-        const int n1 = col / a.H;  // n-gram size minus 2
-        const int h = col - n1 * a.H;
+        const int pc = idx - i * EC;
+        const int e = pc / a.C;
+        const int n1 = (pc - e * a.C) / a.H;
+        const int64_t prime = a.primes[pc];
         const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
-        const int pc = e * a.C + col;  // = (e * (N-1) + n1) * H + h
-        out[idx] = floor_mod_pos(r, a.primes[pc], recip[pc]) + a.offsets[pc];
+        out[idx] = floor_mod_pos(r, prime, prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0) + a.offsets[pc];
     }
 }
 
@@ -195,7 +218,7 @@ extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64
     a.out = hash_ids;
     const int64_t blocks = (T + kTileTokens - 1) / kTileTokens;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_hash: too many tokens");
-    const size_t smem = sizeof(int64_t) * (kTileTokens * E * (N - 1) + static_cast<size_t>(E) * (N - 1) * H);
+    const size_t smem = sizeof(int64_t) * kTileTokens * E * (N - 1);
     hipLaunchKernelGGL(hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, as_stream(stream), a);
     return check_launch("engram_hash");
 }

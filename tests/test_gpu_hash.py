@@ -20,8 +20,10 @@ def _gpu_hash(dev, ids, start_pos, mask, tmap, cache, mult, primes, offs, pad=2,
 
 
 @pytest.mark.parametrize("full_range", [False, True])
+# ids per token E*(N-1)*H from 1 to 1008: up to 256 a lane keeps one column for the tile (256: one token
+# row per step), above that one id per lane and step
 @pytest.mark.parametrize("B,L,E,N,H", [(3, 77, 2, 4, 2), (1, 1, 1, 2, 1), (2, 130, 3, 5, 3), (4, 64, 1, 8, 2),
-                                       (5, 33, 2, 3, 8)])
+                                       (5, 33, 2, 3, 8), (2, 70, 2, 5, 32), (2, 70, 2, 4, 64), (1, 70, 8, 8, 18)])
 def test_hash_small_shapes(gpu_device, full_range, B, L, E, N, H):
     import torch
 
