@@ -39,7 +39,11 @@
 // - Launches whose 256-token tiles would leave CUs idle (a decode step of a
 //   few hundred tokens: 100 tiles for 256 CUs) use 128 x 256 tiles instead
 //   (NI = 2 token blocks per wave, 64 x 64 per wave, 48 KB stages), as long
-//   as those still fit the CUs in one pass: twice the CUs at work.
+//   as those still fit the CUs in one pass: twice the CUs at work.  Such a
+//   workgroup holds one tile, so it runs a three-stage ring (the slab loads,
+//   mostly from beyond L2 there, get two slab periods instead of one) and
+//   puts the stream rows and the epilogue exchange into the stages its last
+//   slabs free.
 // - K not a multiple of 64: a register-staged four-wave variant with a
 //   zero-filled K tail.
 #include <type_traits>
@@ -255,8 +259,12 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     constexpr int kABytes = kBM * BK * 2;      // the A slab: kBM rows x 128 B
     constexpr int kStageBytes = kABytes + kOpBytes;
     constexpr int kSlabLoads = 2 * NI + 8;     // direct-to-LDS loads per loader wave and slab
-    // [stage][A (kBM rows) | W (256 rows)][128 B] + exchange region: 160 KB at NI = 4, the whole LDS of a CU
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
+    // NI = 2 is launched only when every workgroup holds a single tile: its three-stage ring (144 KB) needs
+    // no exchange region, since the stream rows and the epilogue use the stages the last slabs free.
+    constexpr bool kOneTile = NI == 2;
+    constexpr int kStages = kOneTile ? 3 : 2;
+    // [stage][A (kBM rows) | W (256 rows)][128 B] (+ exchange region): 160 KB at NI = 4, the whole LDS of a CU
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes + (kOneTile ? 0 : kExBytes)];
 
     const int tiles = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
@@ -347,8 +355,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // the exchange region (64 rows of 512 B: row 32 wm + t, 16-byte pieces XOR-swizzled by row), then the
     // four storer waves write 16 whole rows each with full-line, non-temporal 16-byte stores (kv is not
     // read again here)
-    uint8_t* ex = lds + 2 * kStageBytes;
-    auto epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0) {
+    uint8_t* ex = lds + 2 * kStageBytes;  // (NI = 4 only)
+    auto epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0, uint8_t* xch) {
         // Every lane-derived address below is rebuilt from a freshly computed lane id, so the compiler
         // cannot hoist the epilogue addresses out of the tile loop (where they would pin VGPRs for the
         // whole kernel).
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     const int chunk = wn * 8 + 4 * j + gq;  // 16-byte piece of the 512-byte row
                     const u32x2 v = {pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1])),
                                      pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]))};
-                    *reinterpret_cast<u32x2*>(ex + wbase + ((chunk ^ key) << 4)) = v;
+                    *reinterpret_cast<u32x2*>(xch + wbase + ((chunk ^ key) << 4)) = v;
                 }
             sync_epi();
             if (!loader) {
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int rr = 16 * s + 2 * q + hi;  // exchange row: token half rr / 32, token rr % 32
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 512 + ((chunk ^ (rr & 31)) << 4));
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(xch + rr * 512 + ((chunk ^ (rr & 31)) << 4));
                     const int64_t m = m0 + (rr >> 5) * 32 * NI + 32 * i + (rr & 31);
                     if (m < p.M && col_ok)
                         __builtin_nontemporal_store(
@@ -403,8 +411,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // region once round 0 is reduced (NI = 2: rounds 0 and 1 only); each wave loads these for its own area and waits only for its
     // own loads, so the rounds need no workgroup barrier.  Loader waves hand their sums to their
     // partner, which stores both, so loaders never have stores outstanding at a slab barrier.
-    auto round_region = [&](int i, int free_stage) -> uint8_t* {
-        return (i == 1 || i == 2) ? lds + free_stage * kStageBytes + (i - 1) * kExBytes : ex;
+    // NI = 4: rounds 0 and 3 in the exchange region, 1 and 2 in stage sa.  One tile (NI = 2): round 0 in
+    // stage sa, round 1 in stage sb.
+    auto round_region = [&](int i, int sa, int sb) -> uint8_t* {
+        if constexpr (kOneTile) return lds + (i == 0 ? sa : sb) * kStageBytes;
+        return (i == 1 || i == 2) ? lds + sa * kStageBytes + (i - 1) * kExBytes : ex;
     };
     // storer wave: round i's 32 rows of its own area (v = 0) and its partner's (v = 1) into `region`,
     // 8 rows of 8 pieces per instruction (8 loads)
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // On entry the storers have round 0 of both their areas (8 loads) and rounds 1 and 2 (NI = 2: round 1)
     // of their own area (4 loads each) in flight, the loaders rounds 1 and 2 of their own area.  Round 0 reaches the loaders
     // through the one barrier; every later round is the wave's own loads, so it only waits for them.
-    auto gate_epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0, int free_stage) {
+    auto gate_epilogue = [&](const f32x16 (&acc)[NI][2], int64_t m0, int n0, int sa, int sb) {
         const int l = lane_id();
         const int c = n0 / p.dim;
         const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice
@@ -462,16 +473,20 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
                 wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
             }
-        // own loads in flight after round r has landed: rounds r+1 .. NI-1, 4 loads each
-        if (!loader) own_wait(std::integral_constant<int, 4 * (NI == 4 ? 2 : NI - 1)>{});
-        sync_epi();  // round 0's stream rows are in, for every wave
+        if constexpr (kOneTile) {
+            own_wait(std::integral_constant<int, 4>{});  // round 0 (own loads; round 1's 4 may still fly)
+        } else {
+            // own loads in flight after round 0 has landed: rounds 1 and 2, 4 loads each
+            if (!loader) own_wait(std::integral_constant<int, 8>{});
+            sync_epi();  // round 0's stream rows are in, for every wave
+        }
         float res[NI][3];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             if (i == 1) own_wait(std::integral_constant<int, 4 * (NI - 2)>{});  // rounds 2 .. NI-1 may still be in flight
             if (i == 2) own_wait(std::integral_constant<int, 4 * (NI > 3 ? NI - 3 : 0)>{});
             if (i == 3) own_wait(std::integral_constant<int, 0>{});
-            const uint8_t* xl = round_region(i, free_stage) + wave * kXArea;
+            const uint8_t* xl = round_region(i, sa, sb) + wave * kXArea;
             u32x2 xr[2][4];
             {
                 const int rr = l & 31, h = l >> 5;
@@ -507,9 +522,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
             res[i][2] = hh + __shfl_xor(hh, 32, 64);
         }
-        // hand-over: a loader wave leaves its sums in its own area of the exchange region (it has read its
-        // round 3 there); its SIMD partner adds them to its own and stores both
-        uint8_t* xl = ex + wave * kXArea;
+        // hand-over: a loader wave leaves its sums in its own area of the last round's region (it has read
+        // that round there); its SIMD partner adds them to its own and stores both
+        uint8_t* const hand = round_region(NI - 1, sa, sb);
+        uint8_t* xl = hand + wave * kXArea;
         if (loader) {
             lds_fence();
             if (l < 32) {
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             // one value per (copy, 128-column slice pair, token), always summed in this order
             const int ls = lane_id();
             if (ls < 32) {
-                const float* partner = reinterpret_cast<const float*>(ex + (wave - 4) * kXArea);
+                const float* partner = reinterpret_cast<const float*>(hand + (wave - 4) * kXArea);
                 const int64_t tbase = m0 + wm * 32 * NI + ls;
                 const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
                 float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
@@ -555,14 +571,25 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         SlabCursor ld{pid, 0};
         int issued = 0;
         if (kLoader) {
-            // prologue: two slabs in flight
-            issue_slab(ld, 0, true);
-            advance(ld);
-            ++issued;
-            issue_slab(ld, 1, issued < total_slabs_mine);
-            advance(ld);
-            ++issued;
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            if constexpr (kOneTile) {
+                // prologue: three slabs in flight (the one tile has at least four), wait for the first
+#pragma unroll
+                for (int s0 = 0; s0 < kStages; ++s0) {
+                    issue_slab(ld, s0, true);
+                    advance(ld);
+                    ++issued;
+                }
+                __builtin_amdgcn_s_waitcnt(wait_vmcnt((kStages - 1) * kSlabLoads));
+            } else {
+                // prologue: two slabs in flight
+                issue_slab(ld, 0, true);
+                advance(ld);
+                ++issued;
+                issue_slab(ld, 1, issued < total_slabs_mine);
+                advance(ld);
+                ++issued;
+                __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            }
         }
         sync();
 
@@ -602,8 +629,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 interleave8<NI, kSlabLoads>();
             } else if (kDefer) {
                 // rounds 1 and 2 (NI = 4) or round 1 (NI = 2) of this wave's stream rows: 4 loads a round
-                dma_x(m0, n0, 1, round_region(1, stage), std::false_type{});
-                if (NI == 4) dma_x(m0, n0, 2, round_region(2, stage), std::false_type{});
+                dma_x(m0, n0, 1, round_region(1, stage, 0), std::false_type{});
+                if (NI == 4) dma_x(m0, n0, 2, round_region(2, stage, 0), std::false_type{});
                 mfma_step8(acc, fa1, fw1);
                 interleave8<NI, 4 * (NI == 4 ? 2 : 1)>();
             } else {
@@ -612,6 +639,86 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             }
             stage ^= 1;
         };
+        // One-tile launches (NI = 2): a three-stage ring.  Phase 0: the slab three ahead goes into the freed
+        // stage; phases 1 and 2 (the third- and second-to-last slab): the freed stage takes this wave's
+        // stream rows of round 0 and round 1 (key tiles); phase 3: the last slab.  A loader's wait before a
+        // barrier leaves in flight only what it issued after the slab being published.
+        auto slab3 = [&](auto phase_tag, auto first_tag, auto key_tag, int64_t m0, int n0) {
+            constexpr int kPhase = decltype(phase_tag)::value;
+            constexpr bool kFirst = decltype(first_tag)::value;
+            constexpr bool kKey = decltype(key_tag)::value;
+            const int next = stage + 1 == kStages ? 0 : stage + 1;
+            read_frags(stage, 1, fa1, fw1);
+            if (kFirst)
+                mfma_step8_zero(acc, fa0, fw0);
+            else
+                mfma_step8(acc, fa0, fw0);
+            interleave8<NI, 0>();
+            read_frags(stage, 2, fa0, fw0);
+            mfma_step8(acc, fa1, fw1);
+            interleave8<NI, 0>();
+            read_frags(stage, 3, fa1, fw1);
+            mfma_step8(acc, fa0, fw0);
+            interleave8<NI, 0>();
+            if (kLoader) {
+                if constexpr (kPhase <= 1)
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));  // the next slab; the one after may fly
+                else if constexpr (kPhase == 2)
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kKey ? 4 : 0));  // the last slab; round 0 may fly
+            }
+            sync();
+            read_frags(next, 0, fa0, fw0);  // (phase 3: stale, unused)
+            if constexpr (kPhase == 0) {
+                if (kLoader) {
+                    issue_slab(ld, stage, true);
+                    advance(ld);
+                    ++issued;
+                    mfma_step8(acc, fa1, fw1);
+                    interleave8<NI, kSlabLoads>();
+                } else {
+                    mfma_step8(acc, fa1, fw1);
+                    interleave8<NI, 0>();
+                }
+            } else if constexpr ((kPhase == 1 || kPhase == 2) && kKey) {
+                dma_x(m0, n0, kPhase - 1, lds + stage * kStageBytes, std::false_type{});
+                mfma_step8(acc, fa1, fw1);
+                interleave8<NI, 4>();
+            } else {
+                mfma_step8(acc, fa1, fw1);
+                interleave8<NI, 0>();
+            }
+            stage = next;
+        };
+        if constexpr (kOneTile) {
+            for (; pid < tiles; pid += G) {  // one tile per workgroup
+                int tm, tn;
+                tile_coords(p, pid, tm, tn);
+                const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+                const int n0 = tn * BN;
+                auto body = [&](auto key_tag) {
+                    constexpr bool kKey = decltype(key_tag)::value;
+                    using Ph0 = std::integral_constant<int, 0>;
+                    slab3(Ph0{}, std::true_type{}, key_tag, m0, n0);
+                    for (int kt = 1; kt < KT - 3; ++kt) slab3(Ph0{}, std::false_type{}, key_tag, m0, n0);
+                    const int sa = stage;
+                    slab3(std::integral_constant<int, 1>{}, std::false_type{}, key_tag, m0, n0);
+                    const int sb = stage;
+                    slab3(std::integral_constant<int, 2>{}, std::false_type{}, key_tag, m0, n0);
+                    const int sc = stage;
+                    slab3(std::integral_constant<int, 3>{}, std::false_type{}, key_tag, m0, n0);
+                    if constexpr (kKey)
+                        gate_epilogue(acc, m0, n0, sa, sb);
+                    else
+                        epilogue(acc, m0, n0, lds + sc * kStageBytes);
+                };
+                if (kGate && n0 < p.out_col0)
+                    body(std::true_type{});
+                else
+                    body(std::false_type{});
+            }
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+            return;
+        }
         for (; pid < tiles; pid += G) {
             int tm, tn;
             tile_coords(p, pid, tm, tn);
@@ -630,7 +737,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     free_stage = stage;
                     slab(std::true_type{}, std::false_type{}, m0, n0);
                 }
-                gate_epilogue(acc, m0, n0, free_stage);
+                gate_epilogue(acc, m0, n0, free_stage, 0);
                 if (kLoader) {  // the slab after next, held back while the epilogue used its stage
                     issue_slab(ld, free_stage, issued < total_slabs_mine);
                     advance(ld);
@@ -639,7 +746,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             } else {
                 slab(std::false_type{}, std::true_type{}, m0, n0);
                 for (int kt = 1; kt < KT; ++kt) slab(std::false_type{}, std::false_type{}, m0, n0);
-                epilogue(acc, m0, n0);
+                epilogue(acc, m0, n0, ex);
             }
         }
         // the slabs issued past this workgroup's last one (empty resources) still write LDS: let them land
@@ -787,18 +894,19 @@ namespace {
 
 // Tokens per tile of the main kernel: 256 (NI = 4), or 128 (NI = 2) when 128-token tiles still fit the CUs
 // in one pass -- small launches (a decode step) then use twice the CUs.
-int tile_ni(int64_t T, int tiles_n) { return ((T + 127) / 128) * tiles_n <= kCUs ? 2 : 4; }
+int tile_ni(int64_t T, int tiles_n, int K) { return K >= 4 * BK && ((T + 127) / 128) * tiles_n <= kCUs ? 2 : 4; }
 
 // Launch the persistent main kernel over all tiles of p (p.tiles_n set; p.tiles_m filled in here).
 template <bool kGate>
 int launch_main(WkvArgs& p, int64_t T, hipStream_t stream, const char* what) {
-    const int ni = tile_ni(T, p.tiles_n);
+    const int ni = tile_ni(T, p.tiles_n, p.K);
     const int64_t bm = 64 * ni;
     const int64_t tiles_m = (T + bm - 1) / bm;
     if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
     p.tiles_m = static_cast<int>(tiles_m);
     const int64_t tiles = tiles_m * p.tiles_n;
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
+    if (ni == 2 && tiles > kCUs) return fail(ENGRAM_EINVAL, "%s: one-tile launch with %lld tiles", what, (long long)tiles);
     if (ni == 2)
         hipLaunchKernelGGL((wkv_kernel<kGate, 2>), dim3(grid), dim3(kMainThreads), 0, stream, p);
     else
