@@ -860,7 +860,7 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
     const float* src = part + static_cast<int64_t>(c) * slices * 3 * M + t;
     // The slices' loads go out in batches of kBatch (3 kBatch independent loads in flight per thread), so a
     // small launch pays a few memory latencies rather than one per slice; the sums still run in slice order.
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 20;
     float hwk = 0.f, kk = 0.f, hh = 0.f;
     int s0 = 0;
     for (; s0 + kBatch <= slices; s0 += kBatch) {
