@@ -13,7 +13,9 @@
 // multiplies by the weight product (the copy's q and k pieces are loaded once
 // for the 4 tokens; they stay in L2) and keeps three fp32 partial sums per
 // token.  A wave-wide butterfly finishes the sums; lane 0 applies the two
-// reciprocal square roots and writes one fp32 per token.
+// reciprocal square roots and writes one fp32 per token.  Launches with
+// fewer such waves than four per CU (a decode call) instead give each
+// (token, copy) a workgroup whose four waves split the row.
 //
 // engram_gate_output finishes the module (the end of Engram.forward): gate =
 // sigmoid(signed sqrt of max(|dot|, 1e-6)), 0 for masked tokens, and out =
@@ -30,6 +32,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTok = 4;  // tokens per wave: the copy's q/k chunks are loaded once for all of them
+// below this many (4-token, copy) waves -- four per CU -- the dot splits each row over a workgroup
+constexpr int64_t kSplitBelowWaves = 1024;
 
 struct GateArgs {
     const uint16_t* x;
@@ -107,6 +111,57 @@ __global__ __launch_bounds__(kThreads) void gate_dot_kernel(GateArgs a) {
             const float rstd = rsqrtf(shh * a.inv_dim + a.eps) * rsqrtf(skk * a.inv_dim + a.eps);
             a.dot[(t0 + u) * a.hc + c] = shwk * rstd * a.rsqrt_dim;
         }
+    }
+}
+
+// Small launches (a decode call: 256 tokens x 4 copies is 256 waves above, one per CU): one workgroup per
+// (token, copy), its four waves taking every fourth 64-piece stretch of the row; each wave's three sums go
+// through LDS and wave 0 adds the four in wave order.
+__global__ __launch_bounds__(kThreads) void gate_dot_split_kernel(GateArgs a) {
+    __shared__ float part[kWaves][3];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t tc = blockIdx.x;  // token * hc + copy
+    const int c = static_cast<int>(tc % a.hc);
+    const int64_t t = tc / a.hc;
+    const u32x4* q = reinterpret_cast<const u32x4*>(a.q + static_cast<int64_t>(c) * a.dim);
+    const u32x4* k = reinterpret_cast<const u32x4*>(a.k + static_cast<int64_t>(c) * a.dim);
+    const u32x4* h = reinterpret_cast<const u32x4*>(a.x + tc * a.dim);
+    const u32x4* key = reinterpret_cast<const u32x4*>(a.kv + t * a.ld_kv + static_cast<int64_t>(c) * a.dim);
+    const int chunks = a.dim / 8;
+    float hh = 0.f, kk = 0.f, hwk = 0.f;
+    for (int j = w * 64 + lane; j < chunks; j += kThreads) {
+        const u32x4 qv = q[j], kw = k[j], hv = h[j], kv = key[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float w0 = lo_bf16(qv[i]) * lo_bf16(kw[i]);  // exact: bf16 * bf16 fits fp32
+            const float w1 = hi_bf16(qv[i]) * hi_bf16(kw[i]);
+            const float h0 = lo_bf16(hv[i]), h1 = hi_bf16(hv[i]);
+            const float k0 = lo_bf16(kv[i]), k1 = hi_bf16(kv[i]);
+            hh += h0 * h0 + h1 * h1;
+            kk += k0 * k0 + k1 * k1;
+            hwk += h0 * w0 * k0 + h1 * w1 * k1;
+        }
+    }
+    hh = wave_sum(hh);
+    kk = wave_sum(kk);
+    hwk = wave_sum(hwk);
+    if (lane == 0) {
+        part[w][0] = hh;
+        part[w][1] = kk;
+        part[w][2] = hwk;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float shh = 0.f, skk = 0.f, shwk = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            shh += part[v][0];
+            skk += part[v][1];
+            shwk += part[v][2];
+        }
+        const float rstd = rsqrtf(shh * a.inv_dim + a.eps) * rsqrtf(skk * a.inv_dim + a.eps);
+        a.dot[tc] = shwk * rstd * a.rsqrt_dim;
     }
 }
 
@@ -325,7 +380,13 @@ extern "C" int engram_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld
     a.dim = dim;
     const int64_t blocks = (a.groups + kWaves - 1) / kWaves;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gate_dot: too many tokens");
-    hipLaunchKernelGGL(gate_dot_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, as_stream(stream), a);
+    if (a.groups < kSplitBelowWaves && dim >= 512 * kWaves) {
+        // fewer waves than the CUs need: a workgroup per (token, copy) instead, the row split over its waves
+        hipLaunchKernelGGL(gate_dot_split_kernel, dim3(static_cast<unsigned>(T * hc)), dim3(kThreads), 0,
+                           as_stream(stream), a);
+    } else {
+        hipLaunchKernelGGL(gate_dot_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, as_stream(stream), a);
+    }
     return check_launch("engram_gate_dot");
 }
 
