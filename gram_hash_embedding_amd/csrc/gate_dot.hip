@@ -24,6 +24,7 @@
 // once into registers up front, the dot is reduced as above, and the output
 // is written from the registers: x, key and value each cross HBM once, out is
 // written once (the value row is re-read by the hc waves of a token from L2).
+// Small launches split each row over a workgroup, as the dot does.
 #include "common.h"
 
 namespace engram {
@@ -301,13 +302,94 @@ __global__ __launch_bounds__(kThreads) void gate_output_kernel(OutArgs a) {
     }
 }
 
+// Small launches: one workgroup per (token, copy); wave w keeps the 16-byte pieces w*64 + lane + 256 i
+// (P of them) of the stream and value rows in registers, the four waves' sums go through LDS, and every
+// thread adds them in wave order, so all derive the same dot and gate.
+template <int P>
+__global__ __launch_bounds__(kThreads) void gate_output_split_kernel(OutArgs a) {
+    __shared__ float part[kWaves][3];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t tc = blockIdx.x;  // token * hc + copy
+    const int c = static_cast<int>(tc % a.hc);
+    const int64_t t = tc / a.hc;
+    const int chunks = a.dim / 8;
+    const u32x4* q = reinterpret_cast<const u32x4*>(a.q + static_cast<int64_t>(c) * a.dim);
+    const u32x4* k = reinterpret_cast<const u32x4*>(a.k + static_cast<int64_t>(c) * a.dim);
+    const uint16_t* row = a.kv + t * a.ld_kv;
+    const u32x4* h = reinterpret_cast<const u32x4*>(a.x + tc * a.dim);
+    const u32x4* key = reinterpret_cast<const u32x4*>(row + static_cast<int64_t>(c) * a.dim);
+    const u32x4* val = reinterpret_cast<const u32x4*>(row + static_cast<int64_t>(a.hc) * a.dim);
+    u32x4* out = reinterpret_cast<u32x4*>(a.out + tc * a.dim);
+
+    u32x4 hr[P], vr[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int j = w * 64 + lane + kThreads * i;
+        if (j < chunks) {
+            hr[i] = h[j];
+            vr[i] = val[j];
+        }
+    }
+    float hh = 0.f, kk = 0.f, hwk = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int j = w * 64 + lane + kThreads * i;
+        if (j < chunks) {
+            const u32x4 qv = q[j], kw = k[j], kr = key[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float w0 = lo_bf16(qv[e]) * lo_bf16(kw[e]);  // exact: bf16 * bf16 fits fp32
+                const float w1 = hi_bf16(qv[e]) * hi_bf16(kw[e]);
+                const float h0 = lo_bf16(hr[i][e]), h1 = hi_bf16(hr[i][e]);
+                const float k0 = lo_bf16(kr[e]), k1 = hi_bf16(kr[e]);
+                hh += h0 * h0 + h1 * h1;
+                kk += k0 * k0 + k1 * k1;
+                hwk += h0 * w0 * k0 + h1 * w1 * k1;
+            }
+        }
+    }
+    hh = wave_sum(hh);
+    kk = wave_sum(kk);
+    hwk = wave_sum(hwk);
+    if (lane == 0) {
+        part[w][0] = hh;
+        part[w][1] = kk;
+        part[w][2] = hwk;
+    }
+    __syncthreads();
+    float shh = 0.f, skk = 0.f, shwk = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        shh += part[v][0];
+        skk += part[v][1];
+        shwk += part[v][2];
+    }
+    const float rstd = rsqrtf(shh * a.inv_dim + a.eps) * rsqrtf(skk * a.inv_dim + a.eps);
+    const float d = shwk * rstd * a.rsqrt_dim;
+    if (a.dot && threadIdx.x == 0) a.dot[tc] = d;
+    const float gate = (a.mask && a.mask[t] == 0) ? 0.f : gate_of(d);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int j = w * 64 + lane + kThreads * i;
+        if (j < chunks) out[j] = residual(hr[i], vr[i], gate);
+    }
+}
+
 template <int P, int TOK>
 int launch_gate_output(const OutArgs& a, hipStream_t stream) {
     OutArgs b = a;
     b.groups = (a.T + TOK - 1) / TOK * a.hc;
     const int64_t blocks = (b.groups + kWaves - 1) / kWaves;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gate_output: too many tokens");
-    hipLaunchKernelGGL((gate_output_kernel<P, TOK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, b);
+    if (b.groups < kSplitBelowWaves && a.dim >= 512 * kWaves && a.dim <= 3 * 8 * kThreads) {
+        // fewer waves than the CUs need: a workgroup per (token, copy), the row split over its waves
+        hipLaunchKernelGGL(gate_output_split_kernel<3>, dim3(static_cast<unsigned>(a.T * a.hc)), dim3(kThreads), 0,
+                           stream, b);
+    } else {
+        hipLaunchKernelGGL((gate_output_kernel<P, TOK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                           b);
+    }
     return check_launch("engram_gate_output");
 }
 

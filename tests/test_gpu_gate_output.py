@@ -21,10 +21,13 @@ def _f(b):
     return oracle.bf16_bits_to_float(b).astype(np.float64)
 
 
-# (T, hc, dim, extra kv columns, masked): dim / 512 rounds up to 1, 2, 4, 6, 8, 10, 12 and 16 pieces per lane
+# (T, hc, dim, extra kv columns, masked): dim / 512 rounds up to 1, 2, 4, 6, 8, 10, 12 and 16 pieces per lane.
+# Launches of fewer than 1,024 (token group, copy) waves with 2048 <= dim <= 6144 split each row over a
+# workgroup (the small-T cases at dims 3000-6144 below); the larger T at those dims keep one wave per row.
 SHAPES = [(5, 4, 256, 0, False), (3, 7, 520, 8, True), (17, 1, 8, 0, False), (2, 64, 16, 0, True),
           (9, 3, 1024, 0, True), (11, 2, 3000, 16, False), (6, 4, 4096, 0, True), (64, 4, 5120, 5120, True),
-          (7, 2, 6144, 0, True), (3, 2, 8192, 8, False), (1, 4, 5120, 0, False)]
+          (7, 2, 6144, 0, True), (3, 2, 8192, 8, False), (1, 4, 5120, 0, False),
+          (1100, 2, 3000, 16, False), (520, 4, 4096, 0, True), (1030, 2, 6144, 0, True)]
 
 
 @pytest.mark.parametrize("T,hc,dim,extra,masked", SHAPES)
