@@ -347,6 +347,9 @@ def main(argv=None):
         "roofline": roofline,
         "paths": paths,
         "kernels": kern,
+        "kernel_timing": ("HIP events on the launch stream around each entry point of the eager loops"
+                          + ("; a decode call's kernels wait on the host between launches, so these include those "
+                             "gaps (the kernel trace holds the device durations)" if cfg.decode_steps else "")),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

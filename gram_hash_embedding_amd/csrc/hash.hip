@@ -17,8 +17,8 @@
 //   start_pos are read from the cache.  The lane then forms the running XOR
 //   of the products for every layer and parks the N-1 running values of
 //   each layer in LDS.
-// - Phase 2, all 256 lanes: one output id per lane and step, so the int64
-//   stores of the tile ([64 tokens, E, C] contiguous) are fully coalesced.
+// - Phase 2, all 256 lanes: the tile's ids ([64 tokens, E, C], contiguous),
+//   written with coalesced int64 stores.
 //   Each id costs one 64-bit floor modulo, done as a Barrett reduction
 //   (a 64 x 64 -> high-64 multiply by floor((2^64 - 1) / p), at most two
 //   corrections): exact integer arithmetic, without a 64-bit division per
@@ -82,17 +82,18 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
         const int64_t l = t - b * a.L;
         const int64_t p = a.start_pos + l;
         // Every slot's loads go out together (indices clamped into range, results selected afterwards), so
-        // the window costs two memory round trips (ids, then token_map) rather than one per slot.
+        // the window costs two memory round trips (ids, then token_map) rather than one per slot.  The cache
+        // is read only where a slot comes from it (before this chunk, after the sequence start): those
+        // positions were written by an earlier call, never by this launch.
         int64_t raw[kMaxN], cached[kMaxN];
         uint8_t mk[kMaxN];
 #pragma unroll
         for (int s = 0; s < kMaxN; ++s) {
             if (s < a.N) {
                 const int64_t flat = b * a.L + (l >= s ? l - s : 0);
-                const int64_t cpos = b * a.cache_L + (p >= s ? p - s : 0);
                 raw[s] = a.input_ids[flat];
                 mk[s] = a.mask != nullptr ? a.mask[flat] : 1;
-                cached[s] = a.cache[cpos];  // written by an earlier call
+                cached[s] = (l < s && p >= s) ? a.cache[b * a.cache_L + (p - s)] : 0;
             }
         }
         int64_t slot[kMaxN];
