@@ -111,10 +111,6 @@ __device__ inline void tile_coords(const WkvArgs& p, int pid, int& tm, int& tn) 
     tn = r / gsize;
 }
 
-// One accumulator element.  The accumulators are VGPRs (the library builds this file with LLVM's VGPR form
-// of the MFMA), so the epilogues read them in place, without a v_accvgpr_read per element.
-__device__ inline float acc_read(float a) { return a; }
-
 // lane id recomputed from the exec mask (two VALU ops) rather than kept live in a VGPR
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
@@ -225,7 +221,7 @@ __device__ inline void mfma_step8_zero(f32x16 (&acc)[NI][2], const bf16x8* fa, c
 template <int NI, int V>
 __device__ inline void interleave8() {
     constexpr int kReads = NI + 2, kMfmas = 2 * NI;
-    if (V == 0) {
+    if constexpr (V == 0) {
 #pragma unroll
         for (int s = 0; s < kReads; ++s) {
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
@@ -370,8 +366,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int chunk = wn * 8 + 4 * j + gq;  // 16-byte piece of the 512-byte row
-                    const u32x2 v = {pack_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1])),
-                                     pack_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]))};
+                    const u32x2 v = {pack_bf16(acc[i][j][4 * gq + 0], acc[i][j][4 * gq + 1]),
+                                     pack_bf16(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
                     *reinterpret_cast<u32x2*>(xch + wbase + ((chunk ^ key) << 4)) = v;
                 }
             sync_epi();
@@ -506,8 +502,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const uint32_t k01 = cvt_pk_bf16(acc_read(acc[i][j][4 * gq + 0]), acc_read(acc[i][j][4 * gq + 1]));
-                    const uint32_t k23 = cvt_pk_bf16(acc_read(acc[i][j][4 * gq + 2]), acc_read(acc[i][j][4 * gq + 3]));
+                    const uint32_t k01 = cvt_pk_bf16(acc[i][j][4 * gq + 0], acc[i][j][4 * gq + 1]);
+                    const uint32_t k23 = cvt_pk_bf16(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
                     const float key[4] = {lo_bf16(k01), hi_bf16(k01), lo_bf16(k23), hi_bf16(k23)};
                     const float h[4] = {lo_bf16(xr[j][gq][0]), hi_bf16(xr[j][gq][0]), lo_bf16(xr[j][gq][1]),
                                         hi_bf16(xr[j][gq][1])};
