@@ -7,7 +7,8 @@
 // the stream copy and of its key (each over `dim`, per copy, not jointly over
 // the copies), and dot = sum(h * w * key) * rstd * dim^-1/2.
 //
-// Design (gfx950): HBM-bound streaming reduction.  One wave per 4 tokens of
+// Design (gfx950): HBM-bound streaming reduction.  Rows that cross HBM once (the stream copies, the keys,
+// the output) use non-temporal loads and stores, leaving L2 to what is re-read (the value row, q and k).  One wave per 4 tokens of
 // one copy: every lane streams 16-byte pieces (8 bf16) of the 4 stream rows
 // and 4 key rows (8 loads in flight per lane and step), widens them to fp32,
 // multiplies by the weight product (the copy's q and k pieces are loaded once
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void gate_dot_kernel(GateArgs a) {
         u32x4 hv[kTok], kv[kTok];
 #pragma unroll
         for (int u = 0; u < kTok; ++u) {
-            hv[u] = h[u][j];
-            kv[u] = key[u][j];
+            hv[u] = __builtin_nontemporal_load(h[u] + j);  // stream and key rows are read once
+            kv[u] = __builtin_nontemporal_load(key[u] + j);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void gate_output_kernel(OutArgs a) {
         if (j < chunks) {
 #pragma unroll
             for (int u = 0; u < TOK; ++u) {
-                hr[u][i] = h[u][j];
+                hr[u][i] = __builtin_nontemporal_load(h[u] + j);  // read once; the value row is shared by the copies
                 vr[u][i] = val[u][j];
             }
         }
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void gate_output_kernel(OutArgs a) {
             const u32x4 qv = q[j], kw = k[j];
             u32x4 kr[TOK];
 #pragma unroll
-            for (int u = 0; u < TOK; ++u) kr[u] = key[u][j];
+            for (int u = 0; u < TOK; ++u) kr[u] = __builtin_nontemporal_load(key[u] + j);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float w0 = lo_bf16(qv[e]) * lo_bf16(kw[e]);  // exact: bf16 * bf16 fits fp32
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void gate_output_kernel(OutArgs a) {
         if (j < chunks) {
 #pragma unroll
             for (int u = 0; u < TOK; ++u)
-                if (u < ntok) out[u][j] = residual(hr[u][i], vr[u][i], gate[u]);
+                if (u < ntok) __builtin_nontemporal_store(residual(hr[u][i], vr[u][i], gate[u]), out[u] + j);
         }
     }
 }
@@ -423,9 +424,9 @@ __global__ __launch_bounds__(kThreads) void gate_residual_kernel(ResArgs a) {
         const int j = static_cast<int>(i - tc * a.chunks);
         const int64_t t = tc / a.hc;
         const float g = (a.mask && a.mask[t] == 0) ? 0.f : gate_of(a.dot[tc]);
-        const u32x4 h = reinterpret_cast<const u32x4*>(a.x)[i];
-        const u32x4 v = *reinterpret_cast<const u32x4*>(a.value + t * a.ld_value + 8 * j);
-        reinterpret_cast<u32x4*>(a.out)[i] = residual(h, v, g);
+        const u32x4 h = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x) + i);  // read once
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a.value + t * a.ld_value + 8 * j);    // shared by the copies
+        __builtin_nontemporal_store(residual(h, v, g), reinterpret_cast<u32x4*>(a.out) + i);
     }
 }
 
