@@ -547,7 +547,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
                         const float v = res[i][q] + partner[(i * 3 + q) * 32 + ls];
-                        if (t < p.M) out[q * p.M + t] = v;
+                        // streamed past L2, which the operand panels need; the finalize reads them once
+                        if (t < p.M) __builtin_nontemporal_store(v, out + q * p.M + t);
                     }
                 }
             }
