@@ -19,15 +19,19 @@ picks which layout the `value` path reads (default: packed).
 One step is timed five ways, each its own loop of `--steps` steps:
   fused           the path with the projection and the gate pre-activation in
                   one entry point (keys reduced in the projection, never
-                  stored) -- this is `value` and `ms_per_step`
+                  stored)
+  fused_hash_gather  the fused path with the hash and every layer's gather in one
+                  launch (engram_hash_gather_packed; packed table only)
+                  -- `value` and `ms_per_step` are the faster of these two
+                  (`config.value_path`)
   fused_*_table   the same on the other table layout
   unfused         the same path as four entry points (kv written, then read)
   module_fused    the whole module: fused path + gate, mask and residual
   module_unfused  the whole module: unfused projection + fused dot/gate/residual
-The decode workload (64 one-token calls per step) also replays the fused and
-unfused steps as HIP graphs (`fused_graph`, `unfused_graph`): launched one by
+The decode workload (64 one-token calls per step) also replays the fused,
+fused_hash_gather and unfused steps as HIP graphs (`*_graph`): launched one by
 one from Python the GPU waits on the host between kernels, so there `value`
-comes from the graph replay of the fused step (`config.launch`).
+comes from the graph replays (`config.launch`).
 Prints one JSON line: whole-job tokens/s, every path's time, per-kernel
 timings from HIP events on the launch stream, the roofline of the dominant
 kernel (the fused projection, bf16 MFMA), and the CPU oracle's throughput on
@@ -204,20 +208,20 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
 
-    def make_step(fused, output, packed):
+    def make_step(fused, output, packed, hg=False):
         def step(events=None):
             if cfg.decode_steps:
                 for s in range(cfg.decode_steps):
                     fwd.step(step_ids[s], cfg.start_pos + s, wl.x[s], None, events=events, output=output,
-                             fused=fused, packed=packed)
+                             fused=fused, packed=packed, hash_gather=hg)
             else:
                 fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output,
-                         fused=fused, packed=packed)
+                         fused=fused, packed=packed, hash_gather=hg)
         return step
 
-    def loop(fused, output, packed):
+    def loop(fused, output, packed, hg=False):
         """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
-        step = make_step(fused, output, packed)
+        step = make_step(fused, output, packed, hg)
 
         for _ in range(args.warmup):
             step()
@@ -236,13 +240,15 @@ def main(argv=None):
     main_packed = args.table == "packed"
     paths = {}
     kern_events = {}
-    for name, fused, output, packed in (("fused", True, False, main_packed),
-                                        ("fused_" + ("pages_table" if main_packed else "packed_table"), True, False,
-                                         not main_packed),
-                                        ("unfused", False, False, main_packed),
-                                        ("module_fused", True, True, main_packed),
-                                        ("module_unfused", False, True, main_packed)):
-        sec, ev = loop(fused, output, packed)
+    runs = [("fused", True, False, main_packed, False),
+            ("fused_" + ("pages_table" if main_packed else "packed_table"), True, False, not main_packed, False),
+            ("unfused", False, False, main_packed, False),
+            ("module_fused", True, True, main_packed, False),
+            ("module_unfused", False, True, main_packed, False)]
+    if main_packed:
+        runs.insert(1, ("fused_hash_gather", True, False, True, True))
+    for name, fused, output, packed, hg in runs:
+        sec, ev = loop(fused, output, packed, hg)
         paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
                        "table": "packed" if packed else "pages"}
         for k, v in ev.items():
@@ -253,8 +259,11 @@ def main(argv=None):
         # A decode step is 64 small calls: launched one by one from Python, the GPU waits on the host between
         # kernels.  The same step captured once as a HIP graph (the library's launches on torch's capture
         # stream; every buffer already allocated) and replayed measures the path itself; that is `value`.
-        for name, fused, output in (("fused", True, False), ("unfused", False, False)):
-            step = make_step(fused, output, main_packed)
+        graphs = [("fused", True, False, False), ("unfused", False, False, False)]
+        if main_packed:
+            graphs.insert(1, ("fused_hash_gather", True, False, True))
+        for name, fused, output, hg in graphs:
+            step = make_step(fused, output, main_packed, hg)
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
@@ -274,8 +283,13 @@ def main(argv=None):
             paths[name + "_graph"] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
                                       "table": "packed" if main_packed else "pages"}
             del graph
-        sec_main = paths["fused_graph"]["ms_per_step"] / 1e3
         value_mode = "hip_graph"
+    # `value`: the fused path, its hash and gathers as separate launches or as one (whichever is faster here:
+    # one launch at decode, separate at a long prefill, where the standalone gather hides more latency)
+    suffix = "_graph" if value_mode == "hip_graph" else ""
+    value_path = min((n + suffix for n in ("fused", "fused_hash_gather") if n + suffix in paths),
+                     key=lambda n: paths[n]["ms_per_step"])
+    sec_main = paths[value_path]["ms_per_step"] / 1e3
     value = T / sec_main
 
     algo = algorithmic(cfg, wl.token_mask is not None)
@@ -291,6 +305,11 @@ def main(argv=None):
         g = kern[name]
         g["GB/s"] = round(T_launch * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
         g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
+    if "hash_gather" in kern:  # the hash and every layer's gather in one launch (ids not read back)
+        hg = kern["hash_gather"]
+        hg_bytes = algo["hash_bytes"] + E * (algo["gather_bytes"] - 8 * cfg.n_hash_cols)
+        hg["GB/s"] = round(T_launch * hg_bytes / (hg["avg_us"] * 1e3), 1)
+        hg["frac_hbm"] = round(hg["GB/s"] / PEAK_HBM_GBS, 4)
     for name in ("wkv", "wkv_gate"):
         w = kern[name]
         w["TFLOP/s"] = round(T_launch * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
@@ -335,6 +354,7 @@ def main(argv=None):
             "tokens_per_step": T,
             "decode_steps": cfg.decode_steps,
             "launch": value_mode,
+            "value_path": value_path,
             "engram_layers": E,
             "table_rows": list(cfg.rows_alloc[:E]),
             "head_dim": cfg.head_dim,

@@ -8,6 +8,7 @@ kernels; there is no fallback: if libengram.so is missing or a call fails,
 an exception is raised.
 
     engram_hash            -- n-gram hash ids (+ compressed-id cache update)
+    engram_hash_gather_packed -- engram_hash and every layer's packed gather + dequant in one launch
     engram_gather_dequant  -- fp8 row gather + block-scale dequant -> bf16
     engram_pack_table      -- the table's rows and scales in one record per row (one-off layout conversion)
     engram_gather_dequant_packed -- engram_gather_dequant on a packed table (same output, fewer lines fetched)
@@ -46,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, p, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         L.engram_hash.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p, p]
+        L.engram_hash_gather_packed.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32,
+                                                i64, i64, p, p, p, p, i32, i32, p, p]
         L.engram_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p, p]
         L.engram_gather_dequant_packed.argtypes = [p, i64, i64, i32, p, i64, i64, i32, i32, p, p, p, p]
         L.engram_pack_table.argtypes = [p, p, i64, i32, i32, p, p]
@@ -56,7 +59,7 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
-        for f in (L.engram_hash, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
+        for f in (L.engram_hash, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
                   L.engram_abi_version):
             f.restype = ctypes.c_int
@@ -126,6 +129,56 @@ def engram_hash(input_ids, start_pos, token_mask, token_map, cache, multipliers,
         _dev(offsets, "offsets", torch.int64, 2), E, N, H, int(pad_id), int(dead),
         _dev(out, "out", torch.int64, 4), _stream(stream)))
     return out
+
+
+def engram_hash_gather_packed(input_ids, start_pos, token_mask, token_map, cache, multipliers, primes, offsets, pad_id,
+                              tables, block_size=32, row_starts=None, dead=-1, outs=None, hash_ids=None,
+                              stream=None):
+    """engram_hash, then for every layer e engram_gather_dequant_packed of its ids on tables[e], in one launch.
+
+    tables: E packed tables (uint8 [R_e, 2*D], engram_pack_table's layout); row_starts: E ints or None (0).
+    Returns (outs, hash_ids): outs[e] is bf16 [B*L, C, D]; hash_ids (int64 [B, L, E, C]) is written only if given.
+    `cache` is updated in place as by engram_hash."""
+    import torch
+
+    B, L = input_ids.shape
+    E, N = multipliers.shape
+    H = primes.shape[2]
+    C = (N - 1) * H
+    if len(tables) != E:
+        raise ValueError("one packed table per layer")
+    D = tables[0].shape[1] // 2
+    if tuple(primes.shape) != (E, N - 1, H) or tuple(offsets.shape) != (E, C):
+        raise ValueError("primes must be [E, N-1, H] and offsets [E, (N-1)*H]")
+    for t in tables:
+        if t.dim() != 2 or t.shape[1] != 2 * D:
+            raise ValueError("every packed table must be [R, 2*D] with the same D")
+    if outs is None:
+        outs = [torch.empty((B * L, C, D), dtype=torch.bfloat16, device=input_ids.device) for _ in range(E)]
+    if len(outs) != E or any(o.numel() != B * L * C * D for o in outs):
+        raise ValueError("outs must hold E tensors of B*L*C*D elements")
+    if hash_ids is not None and tuple(hash_ids.shape) != (B, L, E, C):
+        raise ValueError("hash_ids has the wrong shape")
+    mask_p = None
+    if token_mask is not None:
+        if tuple(token_mask.shape) != (B, L):
+            raise ValueError("token_mask must be [B, L]")
+        if token_mask.dtype == torch.bool:
+            token_mask = token_mask.view(torch.uint8)
+        mask_p = _dev(token_mask, "token_mask", torch.uint8, 2)
+    tab_arr = (ctypes.c_void_p * E)(*[_dev(t, "tables[%d]" % e, torch.uint8, 2).value for e, t in enumerate(tables)])
+    row_arr = (ctypes.c_int64 * E)(*[t.shape[0] for t in tables])
+    rs_arr = None if row_starts is None else (ctypes.c_int64 * E)(*[int(r) for r in row_starts])
+    out_arr = (ctypes.c_void_p * E)(*[_dev(o, "outs[%d]" % e, torch.bfloat16).value for e, o in enumerate(outs)])
+    ids_p = None if hash_ids is None else _dev(hash_ids, "hash_ids", torch.int64, 4)
+    _check(lib().engram_hash_gather_packed(
+        _dev(input_ids, "input_ids", torch.int64, 2), B, L, int(start_pos), mask_p,
+        _dev(token_map, "token_map", torch.int64, 1), token_map.numel(),
+        _dev(cache, "cache", torch.int64, 2), cache.shape[0], cache.shape[1],
+        _dev(multipliers, "multipliers", torch.int64, 2), _dev(primes, "primes", torch.int64, 3),
+        _dev(offsets, "offsets", torch.int64, 2), E, N, H, int(pad_id), int(dead), ids_p,
+        tab_arr, row_arr, rs_arr, D, int(block_size), out_arr, _stream(stream)))
+    return outs, hash_ids
 
 
 def _gather_ids(hash_ids, n_cols, layer):
@@ -360,7 +413,7 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
     return out
 
 
-__all__ = ["engram_hash", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
+__all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
            "engram_wkv_gate", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

@@ -27,15 +27,12 @@
 //   for 72 used.  A packed record of 2*D bytes holds the row and then its
 //   scales (zero padded), aligned to its size: at D <= 64 a lookup touches one
 //   line.  The dequant is the same code, so the outputs are bit-identical.
-#include "common.h"
+#include "dequant.h"
 
 namespace engram {
 namespace {
 
 constexpr int kThreads = 256;
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct GatherArgs {
     const int64_t* ids;
@@ -50,25 +47,6 @@ struct GatherArgs {
     uint8_t* out_fp8;
     float* out_scale;
 };
-
-__device__ inline uint32_t pack_bf16(float lo, float hi) {
-    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// 16 fp8 bytes times the scale -> 16 bf16 (two 16-byte vectors).
-__device__ inline void dequant16(const u32x4& v, float s, u32x4& o0, u32x4& o1) {
-    uint32_t r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[i]), false);  // bytes 0, 1
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[i]), true);   // bytes 2, 3
-        r[2 * i] = pack_bf16(a.x * s, a.y * s);
-        r[2 * i + 1] = pack_bf16(b.x * s, b.y * s);
-    }
-    o0 = u32x4{r[0], r[1], r[2], r[3]};
-    o1 = u32x4{r[4], r[5], r[6], r[7]};
-}
 
 template <int D, int U, bool kPacked>
 __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) {

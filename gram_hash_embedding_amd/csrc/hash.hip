@@ -24,7 +24,15 @@
 //   corrections): exact integer arithmetic, without a 64-bit division per
 //   id.  A lane keeps one (layer, column) for the whole tile, so its prime,
 //   offset and reciprocal are fetched and computed once.
-#include "common.h"
+// - A small call (a 256-token decode step) shrinks the tile, down to one
+//   token per workgroup, so its arithmetic spreads over the CUs.
+//
+// engram_hash_gather_packed: the same kernel with a phase 3 -- the tile's ids
+// stay in LDS and its lanes fetch and dequantise every layer's rows from the
+// packed tables (ParallelEngramEmbedding.forward of the same page, as
+// engram_gather_dequant_packed computes it), so a decode step makes one
+// launch and one memory round trip fewer per layer.
+#include "dequant.h"
 
 namespace engram {
 namespace {
@@ -33,6 +41,12 @@ constexpr int kMaxN = 8;
 constexpr int kMaxE = 8;
 constexpr int kMaxC = 1024;
 constexpr int kTileTokens = 64;
+// The fused gather: at most 16 tokens per workgroup and 8 rows per lane in flight (measured against 64 and
+// 4: equal at decode, 4 % faster on a long prefill's ids, 9 % on uniform ids).
+constexpr int kGatherTileTokens = 16;
+constexpr int kGatherUnroll = 8;
+constexpr int kSpreadBlocks = 256;  // a launch gets at least this many workgroups while tiles can shrink
+constexpr int kMaxTileIds = 4096;   // ids a tile keeps in LDS for the fused gather (32 KB)
 constexpr int kThreads = 256;
 
 struct HashArgs {
@@ -47,7 +61,17 @@ struct HashArgs {
     const int64_t* offsets;
     int64_t T, L, start_pos, pad, dead;
     int E, N, H, C;
-    int64_t* out;
+    int tile;  // tokens per workgroup (a power of two, at most kTileTokens)
+    int64_t* out;  // may be null when the rows are gathered
+};
+
+// Phase 3 of the fused call: per layer e, its packed table [R, 2D] and its rows [T, C, D] out.
+struct GatherSide {
+    const uint8_t* table[kMaxE];
+    int64_t R[kMaxE];
+    int64_t row_start[kMaxE];
+    uint16_t* out[kMaxE];
+    int blk;
 };
 
 // x mod p for x < 2^64 and p >= 1, given m = floor((2^64 - 1) / p): q = floor(x m / 2^64) is at most 2 below
@@ -68,11 +92,13 @@ __device__ inline int64_t floor_mod_pos(int64_t r, int64_t p, uint64_t m) {
     return static_cast<int64_t>(up - 1 - mod_barrett(a, up, m));
 }
 
-__global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
-    extern __shared__ int64_t roll[];  // [kTileTokens][E][N-1]
+// D = 0: hash only.  D > 0: the ids also go to LDS (after the running values) and phase 3 gathers the rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a, GatherSide gs) {
+    extern __shared__ int64_t roll[];  // [tile][E][N-1], then (D > 0) the ids [tile][E * C]
     const int NR = a.N - 1;
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kTileTokens;
-    const int ntok = static_cast<int>(min<int64_t>(kTileTokens, a.T - tile0));
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tile;
+    const int ntok = static_cast<int>(min<int64_t>(a.tile, a.T - tile0));
     const int tid = threadIdx.x;
     const int EC = a.E * a.C;
 
@@ -137,33 +163,91 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
     __syncthreads();
 
     const int total = ntok * EC;
-    int64_t* out = a.out + tile0 * EC;
+    int64_t* out = a.out != nullptr ? a.out + tile0 * EC : nullptr;
+    int64_t* ids = roll + static_cast<int64_t>(a.tile) * a.E * NR;
+    auto put = [&](int idx, int64_t id) {
+        if (out != nullptr) out[idx] = id;
+        if (D > 0) ids[idx] = id;
+    };
     if (EC <= kThreads) {
         // Lane l keeps one (layer, column) pc = l % EC for the whole tile: its prime, offset and Barrett
         // reciprocal are fetched once, then it walks tokens l / EC, + G, + 2G, ... (G = 256 / EC); the
         // lanes of one step write G consecutive token rows, so the stores stay coalesced.
         const int G = kThreads / EC;
-        if (tid >= G * EC) return;
-        const int pc = tid % EC;  // = e * C + (n - 2) * H + h: primes [E, N-1, H] flat is [E, C] in column order
-        const int e = pc / a.C;
-        const int n1 = (pc - e * a.C) / a.H;  // n-gram size minus 2
-        const int64_t prime = a.primes[pc];
-        const int64_t off = a.offsets[pc];
-        const uint64_t m = prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0;
-        for (int i = tid / EC; i < ntok; i += G) {
-            const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
-            out[i * EC + pc] = floor_mod_pos(r, prime, m) + off;
+        if (tid < G * EC) {
+            const int pc = tid % EC;  // = e * C + (n - 2) * H + h: primes [E, N-1, H] flat is [E, C] in column order
+            const int e = pc / a.C;
+            const int n1 = (pc - e * a.C) / a.H;  // n-gram size minus 2
+            const int64_t prime = a.primes[pc];
+            const int64_t off = a.offsets[pc];
+            const uint64_t m = prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0;
+            for (int i = tid / EC; i < ntok; i += G) {
+                const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
+                put(i * EC + pc, floor_mod_pos(r, prime, m) + off);
+            }
         }
-        return;
+    } else {
+        for (int idx = tid; idx < total; idx += kThreads) {  // more than 256 ids per token: one id per lane and step
+            const int i = idx / EC;
+            const int pc = idx - i * EC;
+            const int e = pc / a.C;
+            const int n1 = (pc - e * a.C) / a.H;
+            const int64_t prime = a.primes[pc];
+            const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
+            put(idx, floor_mod_pos(r, prime, prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0) + a.offsets[pc]);
+        }
     }
-    for (int idx = tid; idx < total; idx += kThreads) {  // more than 256 ids per token: one id per lane and step
-        const int i = idx / EC;
-        const int pc = idx - i * EC;
-        const int e = pc / a.C;
-        const int n1 = (pc - e * a.C) / a.H;
-        const int64_t prime = a.primes[pc];
-        const int64_t r = roll[(static_cast<int64_t>(i) * a.E + e) * NR + n1];
-        out[idx] = floor_mod_pos(r, prime, prime > 0 ? ~0ull / static_cast<uint64_t>(prime) : 0) + a.offsets[pc];
+    if constexpr (D > 0) {
+        // Phase 3: D/16 lanes per row (one 16-byte piece each), rows (token, layer, column) of the tile in
+        // order, kUnroll rows per lane in flight.  A row outside its layer's [row_start, row_start + R) is
+        // zero; the record's scales sit after its D bytes.
+        constexpr int LPR = D / 16;
+        constexpr int RPP = kThreads / LPR;  // rows per pass
+        constexpr int kUnroll = kGatherUnroll;
+        __syncthreads();
+        const int lr = tid % LPR;
+        const int sidx = (lr * 16) / gs.blk;
+        for (int r0 = tid / LPR; r0 < total; r0 += RPP * kUnroll) {
+            u32x4 v[kUnroll];
+            float sc[kUnroll];
+            bool ok[kUnroll];
+            uint16_t* dst[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int r = r0 + u * RPP;
+                const bool live = r < total;
+                const int i = live ? r / EC : 0;
+                const int pc = live ? r - i * EC : 0;
+                const int e = pc / a.C;
+                const int c = pc - e * a.C;
+                const uint8_t* table = gs.table[0];
+                int64_t R = gs.R[0], rs = gs.row_start[0];
+                uint16_t* o = gs.out[0];
+#pragma unroll
+                for (int k = 1; k < kMaxE; ++k)  // select the layer's arguments (no dynamic indexing)
+                    if (e == k) {
+                        table = gs.table[k];
+                        R = gs.R[k];
+                        rs = gs.row_start[k];
+                        o = gs.out[k];
+                    }
+                const int64_t local = (live ? ids[r] : rs) - rs;
+                ok[u] = live && local >= 0 && local < R;
+                const uint8_t* rec = table + (ok[u] ? local : 0) * (2 * D);
+                v[u] = *reinterpret_cast<const u32x4*>(rec + lr * 16);
+                sc[u] = reinterpret_cast<const float*>(rec + D)[sidx];
+                dst[u] = live ? o + ((tile0 + i) * a.C + c) * D + lr * 16 : nullptr;
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (dst[u] == nullptr) continue;
+                u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+                if (ok[u]) dequant16(v[u], sc[u], o0, o1);
+                u32x4* d = reinterpret_cast<u32x4*>(dst[u]);
+                __builtin_nontemporal_store(o0, d);
+                __builtin_nontemporal_store(o1, d + 1);
+            }
+        }
     }
 }
 
@@ -172,30 +256,32 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a) {
 
 using namespace engram;
 
-extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
-                           const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
-                           int64_t* cache, int64_t cache_B, int64_t cache_L,
-                           const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
-                           int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
-                           int64_t* hash_ids, void* stream) {
-    if (B < 0 || L < 0 || start_pos < 0) return fail(ENGRAM_EINVAL, "engram_hash: negative B, L or start_pos");
-    if (N < 2 || N > kMaxN) return fail(ENGRAM_EINVAL, "engram_hash: N=%d outside [2, %d]", N, kMaxN);
-    if (E < 1 || E > kMaxE) return fail(ENGRAM_EINVAL, "engram_hash: E=%d outside [1, %d]", E, kMaxE);
+namespace {
+
+// Validation and launch shared by both entry points; `gs` null = hash only.
+int hash_entry(const char* name, const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+               const uint8_t* token_mask, const int64_t* token_map, int64_t vocab, int64_t* cache, int64_t cache_B,
+               int64_t cache_L, const int64_t* multipliers, const int64_t* primes, const int64_t* offsets, int32_t E,
+               int32_t N, int32_t H, int64_t pad_id, int64_t dead, int64_t* hash_ids, int D, const GatherSide* gs,
+               void* stream) {
+    if (B < 0 || L < 0 || start_pos < 0) return fail(ENGRAM_EINVAL, "%s: negative B, L or start_pos", name);
+    if (N < 2 || N > kMaxN) return fail(ENGRAM_EINVAL, "%s: N=%d outside [2, %d]", name, N, kMaxN);
+    if (E < 1 || E > kMaxE) return fail(ENGRAM_EINVAL, "%s: E=%d outside [1, %d]", name, E, kMaxE);
     if (H < 1 || static_cast<int64_t>(N - 1) * H > kMaxC)
-        return fail(ENGRAM_EINVAL, "engram_hash: H=%d gives more than %d columns", H, kMaxC);
-    if (vocab < 1) return fail(ENGRAM_EINVAL, "engram_hash: vocab < 1");
+        return fail(ENGRAM_EINVAL, "%s: H=%d gives more than %d columns", name, H, kMaxC);
+    if (vocab < 1) return fail(ENGRAM_EINVAL, "%s: vocab < 1", name);
     if (B > cache_B || cache_L < 0 || start_pos + L > cache_L)
-        return fail(ENGRAM_ERANGE, "engram_hash: B=%lld, positions up to %lld need a cache of at least [%lld, %lld], "
-                    "have [%lld, %lld]", (long long)B, (long long)(start_pos + L), (long long)B,
+        return fail(ENGRAM_ERANGE, "%s: B=%lld, positions up to %lld need a cache of at least [%lld, %lld], "
+                    "have [%lld, %lld]", name, (long long)B, (long long)(start_pos + L), (long long)B,
                     (long long)(start_pos + L), (long long)cache_B, (long long)cache_L);
     const int64_t T = B * L;
     if (T == 0) return ENGRAM_OK;
-    if (!input_ids || !token_map || !cache || !multipliers || !primes || !offsets || !hash_ids)
-        return fail(ENGRAM_EINVAL, "engram_hash: null required pointer");
+    if (!input_ids || !token_map || !cache || !multipliers || !primes || !offsets || (!hash_ids && !gs))
+        return fail(ENGRAM_EINVAL, "%s: null required pointer", name);
     for (const void* p : {(const void*)input_ids, (const void*)token_map, (const void*)cache,
                           (const void*)multipliers, (const void*)primes, (const void*)offsets,
                           (const void*)hash_ids})
-        if (!aligned(p, 8)) return fail(ENGRAM_EINVAL, "engram_hash: int64 array not 8-byte aligned");
+        if (!aligned(p, 8)) return fail(ENGRAM_EINVAL, "%s: int64 array not 8-byte aligned", name);
 
     HashArgs a;
     a.input_ids = input_ids;
@@ -217,9 +303,75 @@ extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64
     a.H = H;
     a.C = (N - 1) * H;
     a.out = hash_ids;
-    const int64_t blocks = (T + kTileTokens - 1) / kTileTokens;
-    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_hash: too many tokens");
-    const size_t smem = sizeof(int64_t) * kTileTokens * E * (N - 1);
-    hipLaunchKernelGGL(hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, as_stream(stream), a);
-    return check_launch("engram_hash");
+    // A small call (a 256-token decode step) is spread over the CUs, down to one token per workgroup: its
+    // time is the dependent memory round trips plus the id arithmetic, which then runs on many CUs.  With
+    // the gather, a tile's ids must also fit the LDS beside the running values (at most 32 KB of ids).
+    const int EC = E * a.C;
+    int tile = gs != nullptr ? kGatherTileTokens : kTileTokens;
+    while (tile > 1 && gs != nullptr && tile * EC > kMaxTileIds) tile /= 2;
+    while (tile > 1 && (T + tile - 1) / tile < kSpreadBlocks) tile /= 2;
+    a.tile = tile;
+    const int64_t blocks = (T + tile - 1) / tile;
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tokens", name);
+    const size_t smem = sizeof(int64_t) * tile * (E * (N - 1) + (gs != nullptr ? EC : 0));
+    const GatherSide none{};
+    const dim3 grid(static_cast<unsigned>(blocks));
+    hipStream_t st = as_stream(stream);
+    switch (gs != nullptr ? D : 0) {
+        case 0: hipLaunchKernelGGL(hash_kernel<0>, grid, dim3(kThreads), smem, st, a, none); break;
+        case 32: hipLaunchKernelGGL(hash_kernel<32>, grid, dim3(kThreads), smem, st, a, *gs); break;
+        case 64: hipLaunchKernelGGL(hash_kernel<64>, grid, dim3(kThreads), smem, st, a, *gs); break;
+        case 128: hipLaunchKernelGGL(hash_kernel<128>, grid, dim3(kThreads), smem, st, a, *gs); break;
+        default: hipLaunchKernelGGL(hash_kernel<256>, grid, dim3(kThreads), smem, st, a, *gs); break;
+    }
+    return check_launch(name);
+}
+
+}  // namespace
+
+extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                           const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                           int64_t* cache, int64_t cache_B, int64_t cache_L,
+                           const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                           int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                           int64_t* hash_ids, void* stream) {
+    return hash_entry("engram_hash", input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B,
+                      cache_L, multipliers, primes, offsets, E, N, H, pad_id, dead, hash_ids, 0, nullptr, stream);
+}
+
+extern "C" int engram_hash_gather_packed(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                                         const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                                         int64_t* cache, int64_t cache_B, int64_t cache_L,
+                                         const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                                         int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                                         int64_t* hash_ids, const uint8_t* const* tables, const int64_t* rows,
+                                         const int64_t* row_starts, int32_t D, int32_t blk,
+                                         uint16_t* const* out_bf16, void* stream) {
+    const char* name = "engram_hash_gather_packed";
+    if (D != 32 && D != 64 && D != 128 && D != 256)
+        return fail(ENGRAM_EINVAL, "%s: D=%d not in {32, 64, 128, 256}", name, D);
+    if (blk < 16 || blk % 16 != 0 || D % blk != 0)
+        return fail(ENGRAM_EINVAL, "%s: blk=%d must be a multiple of 16 dividing D=%d", name, blk, D);
+    if (E < 1 || E > kMaxE) return fail(ENGRAM_EINVAL, "%s: E=%d outside [1, %d]", name, E, kMaxE);
+    if (B >= 0 && L >= 0 && B * L == 0)  // nothing to gather: the hash's own checks decide
+        return hash_entry(name, input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B, cache_L,
+                          multipliers, primes, offsets, E, N, H, pad_id, dead, hash_ids, 0, nullptr, stream);
+    if (!tables || !rows || !out_bf16) return fail(ENGRAM_EINVAL, "%s: null pointer array", name);
+    GatherSide gs{};
+    gs.blk = blk;
+    for (int e = 0; e < kMaxE; ++e) {
+        const int k = e < E ? e : 0;  // unused slots repeat layer 0 (never selected)
+        if (e < E) {
+            if (rows[e] < 1) return fail(ENGRAM_EINVAL, "%s: layer %d: R < 1", name, e);
+            if (!tables[e] || !out_bf16[e]) return fail(ENGRAM_EINVAL, "%s: layer %d: null pointer", name, e);
+            if (!aligned(tables[e], 2 * D) || !aligned(out_bf16[e], 16))
+                return fail(ENGRAM_EINVAL, "%s: layer %d: misaligned pointer", name, e);
+        }
+        gs.table[e] = tables[k];
+        gs.R[e] = rows[k];
+        gs.row_start[e] = row_starts != nullptr ? row_starts[k] : 0;
+        gs.out[e] = out_bf16[k];
+    }
+    return hash_entry(name, input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B, cache_L,
+                      multipliers, primes, offsets, E, N, H, pad_id, dead, hash_ids, D, &gs, stream);
 }

@@ -18,7 +18,8 @@ import dataclasses
 from typing import List, Optional
 
 from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
-               engram_gather_dequant_packed, engram_hash, engram_wkv, engram_wkv_gate, engram_wkv_gate_workspace_bytes)
+               engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_wkv, engram_wkv_gate,
+               engram_wkv_gate_workspace_bytes)
 
 
 @dataclasses.dataclass
@@ -96,12 +97,37 @@ class EngramForward:
             input_ids, start_pos, token_mask, s.token_map, s.cache, s.multipliers, s.primes, s.offsets, s.pad_id,
             s.dead, out=out))
 
-    def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False, packed=False):
+    def hash_gather(self, input_ids, start_pos: int, token_mask=None, events=None):
+        """The hash and every layer's gather from its packed table in one launch (engram_hash_gather_packed):
+        (ids [B, L, E, C], [a_e bf16 [T, C, D]]), in the buffers `hash` and `layer` use."""
+        import torch
+
+        B, L = input_ids.shape
+        T = B * L
+        dev = input_ids.device
+        if any(lw.packed is None for lw in self.layers):
+            raise ValueError("every layer needs its packed table")
+        D = self.layers[0].weight.shape[1]
+        blk = self.layers[0].block_size
+        if any(lw.weight.shape[1] != D or lw.block_size != blk for lw in self.layers):
+            raise ValueError("the layers' tables differ in row width or block size")
+        ids = self._buf("ids", (B, L, self.E, self.C), torch.int64, dev)
+        outs = [self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev) for e in range(self.E)]
+        s = self.state
+        self._timed(events, "hash_gather", lambda: engram_hash_gather_packed(
+            input_ids, start_pos, token_mask, s.token_map, s.cache, s.multipliers, s.primes, s.offsets, s.pad_id,
+            [lw.packed for lw in self.layers], blk, [lw.row_start for lw in self.layers], s.dead, outs=outs,
+            hash_ids=ids))
+        return ids, outs
+
+    def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False, packed=False,
+              a=None):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim]
         (or [B, L, hc, dim]); with `output`, also the layer's output stream bf16 (x's shape), where
         token_mask [B, L] (False = pass through) shuts the gate.  With `fused`, the second tensor is
         the value bf16 [T, dim] alone (the keys are never stored).  With `packed`, the rows come from
-        the layer's packed table (same values, one record per row).
+        the layer's packed table (same values, one record per row).  With `a` (the layer's rows, already
+        gathered by `hash_gather`), no gather is launched.
 
         The tensors are this object's buffers for layer e: the next call for the same layer
         overwrites them."""
@@ -111,15 +137,16 @@ class EngramForward:
         T = hash_ids.shape[0] * hash_ids.shape[1]
         D = lw.weight.shape[1]
         dev = hash_ids.device
-        a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
-        if packed:
-            if lw.packed is None:
-                raise ValueError(f"layer {e} has no packed table")
-            self._timed(events, "gather_dequant_packed", lambda: engram_gather_dequant_packed(
-                hash_ids, lw.packed, lw.block_size, lw.row_start, layer=e, out=a))
-        else:
-            self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
-                hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
+        if a is None:
+            a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
+            if packed:
+                if lw.packed is None:
+                    raise ValueError(f"layer {e} has no packed table")
+                self._timed(events, "gather_dequant_packed", lambda: engram_gather_dequant_packed(
+                    hash_ids, lw.packed, lw.block_size, lw.row_start, layer=e, out=a))
+            else:
+                self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
+                    hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
         x3 = x.reshape(T, x.shape[-2], x.shape[-1])
         dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
         if fused:
@@ -144,17 +171,21 @@ class EngramForward:
         return a, kv, dot
 
     def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False,
-             packed=False):
+             packed=False, hash_gather=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
         (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
+        With `hash_gather`, the hash and every layer's packed gather are one launch.
         `events`: optional dict that collects (start, end) timing events per entry point."""
-        ids = self.hash(input_ids, start_pos, token_mask, events)
+        if hash_gather:
+            ids, rows = self.hash_gather(input_ids, start_pos, token_mask, events)
+        else:
+            ids, rows = self.hash(input_ids, start_pos, token_mask, events), [None] * self.E
         res = []
         for e in range(self.E):
             x = xs[e] if isinstance(xs, (list, tuple)) else xs
             res.append(self.layer(e, ids, x, events, token_mask=token_mask, output=output, fused=fused,
-                                  packed=packed)[-1])
+                                  packed=packed, a=rows[e])[-1])
         return res
 
 

@@ -161,6 +161,40 @@ int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, int64_t id_
                                  uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale, void* stream);
 
 /*
+ * engram_hash_gather_packed -- engram_hash, then engram_gather_dequant_packed
+ * of every layer's ids, in one launch (stack-hashes page: the hash module's
+ * forward, then ParallelEngramEmbedding.forward per engram layer).  The ids
+ * stay on chip between the two; the results are those of the two entry points
+ * called in turn, bit for bit.
+ *
+ * For token t < B*L, layer e < E and column c < C = (N-1)*H, with
+ * id = the engram_hash id [t, e, c]:
+ *   ok = row_starts[e] <= id < row_starts[e] + rows[e]
+ *   out_bf16[e][t, c, j] = ok ? bf16(fp32(e4m3fn(byte j of record r)) * scale) : +0,
+ *   r = id - row_starts[e], scale = fp32 at byte D + 4*(j/blk) of record r.
+ *
+ * Hash arguments, the cache update, limits and errors: as engram_hash, except
+ * hash_ids  int64 [B, L, E, C] out, or NULL (the ids are then not stored).
+ * tables    host array of E device pointers: layer e's packed table,
+ *           uint8 [rows[e], 2*D] (engram_pack_table's layout), aligned to 2*D
+ * rows      host array of E row counts, each >= 1
+ * row_starts host array of E first rows (this GPU's share), or NULL = all 0
+ * D, blk    row width in {32, 64, 128, 256}; block size, a multiple of 16
+ *           that divides D
+ * out_bf16  host array of E device pointers: layer e's rows, uint16
+ *           [B*L, C, D] bf16 bits, out; 16-byte aligned
+ * The host arrays are read during the call only.
+ */
+int engram_hash_gather_packed(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                              const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                              int64_t* cache, int64_t cache_B, int64_t cache_L,
+                              const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                              int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                              int64_t* hash_ids, const uint8_t* const* tables, const int64_t* rows,
+                              const int64_t* row_starts, int32_t D, int32_t blk,
+                              uint16_t* const* out_bf16, void* stream);
+
+/*
  * engram_wkv -- the projection kv = A * W^T (stack-hashes page: Engram's
  * `wkv` Linear, n_hash_cols*head_dim -> dim*(hc_mult+1), no bias).
  *

@@ -20,7 +20,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert set(names) >= {"engram_hash", "engram_gather_dequant", "engram_gather_dequant_packed",
+    assert set(names) >= {"engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_gather_dequant_packed",
                           "engram_pack_table", "engram_wkv", "engram_gate_dot",
                           "engram_gate_output", "engram_wkv_gate", "engram_wkv_gate_workspace_bytes",
                           "engram_gate_residual", "engram_status_string", "engram_last_error",
@@ -75,6 +75,8 @@ def test_hash_validation(args, status, msg):
 def test_zero_tokens_is_a_valid_no_op():
     L = g.lib()
     assert L.engram_hash(None, 0, 5, 0, None, None, 10, None, 0, 5, None, None, None, 1, 4, 2, 2, -1, None, None) == 0
+    assert L.engram_hash_gather_packed(None, 0, 5, 0, None, None, 10, None, 0, 5, None, None, None, 1, 4, 2, 2, -1,
+                                       None, None, None, None, 64, 32, None, None) == 0
     assert L.engram_gather_dequant(None, 0, 24, 24, None, None, 10, 0, 64, 32, None, None, None, None) == 0
     assert L.engram_gather_dequant_packed(None, 0, 24, 24, None, 10, 0, 64, 32, None, None, None, None) == 0
     assert L.engram_pack_table(None, None, 0, 64, 32, None, None) == 0
@@ -83,6 +85,35 @@ def test_zero_tokens_is_a_valid_no_op():
     assert L.engram_gate_output(None, None, 80, None, None, 1e-20, None, None, None, 0, 4, 16, None) == 0
     assert L.engram_wkv_gate(None, None, None, None, None, 1e-20, None, 256, None, None, 0, 0, 64, 4, 256, None) == 0
     assert L.engram_gate_residual(None, None, 16, None, None, None, 0, 4, 16, None) == 0
+
+
+def _hash_gather(**kw):
+    a = dict(input_ids=FAKE, B=2, L=64, start_pos=0, mask=None, token_map=FAKE, vocab=10, cache=FAKE, cache_B=2,
+             cache_L=64, mult=FAKE, primes=FAKE, offsets=FAKE, E=2, N=4, H=2, pad=2, dead=-1, ids=None,
+             tables=[FAKE.value, FAKE.value], rows=[100, 100], row_starts=None, D=64, blk=32,
+             outs=[FAKE.value, FAKE.value])
+    a.update(kw)
+    arr = lambda t, v: None if v is None else (t * len(v))(*v)
+    return g.lib().engram_hash_gather_packed(
+        a["input_ids"], a["B"], a["L"], a["start_pos"], a["mask"], a["token_map"], a["vocab"], a["cache"],
+        a["cache_B"], a["cache_L"], a["mult"], a["primes"], a["offsets"], a["E"], a["N"], a["H"], a["pad"], a["dead"],
+        a["ids"], arr(ctypes.c_void_p, a["tables"]), arr(ctypes.c_int64, a["rows"]),
+        arr(ctypes.c_int64, a["row_starts"]), a["D"], a["blk"], arr(ctypes.c_void_p, a["outs"]), None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(D=48), 1, "D=48"), (dict(blk=8), 1, "blk=8"), (dict(blk=48), 1, "blk=48"), (dict(E=0), 1, "E=0"),
+    (dict(E=9), 1, "E=9"), (dict(N=1), 1, "N=1"), (dict(cache_L=63), 2, "cache"), (dict(tables=None), 1, "null"),
+    (dict(outs=None), 1, "null"), (dict(rows=[100, 0]), 1, "layer 1: R < 1"),
+    (dict(tables=[FAKE.value, None]), 1, "layer 1: null"), (dict(outs=[None, FAKE.value]), 1, "layer 0: null"),
+    (dict(tables=[FAKE.value, 0x100040]), 1, "layer 1: misaligned"),  # a 128-byte record needs 128
+    (dict(outs=[FAKE.value, 0x100008]), 1, "layer 1: misaligned"),
+    (dict(input_ids=None), 1, "null"), (dict(ids=ctypes.c_void_p(0x100004)), 1, "aligned"),
+])
+def test_hash_gather_validation(kw, status, msg):
+    assert _hash_gather(**kw) == status
+    assert msg in _err()
+    assert "engram_hash_gather_packed" in _err()
 
 
 @pytest.mark.parametrize("kw,msg", [

@@ -96,7 +96,8 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
 def test_decode_pipeline(gpu_device):
     """The decode workload as the benchmark runs it: the hash of the 4,096-token history, then 64 calls of
     one token per sequence through the whole path (through the residual), each with its own stream, the
-    fused and the four-entry-point projection in turn.  Steps 0, 1, 62 and 63 are checked against the
+    fused and the four-entry-point projection in turn, and the hash and gathers as one launch in half the
+    calls (steps 0 and 1 of every four).  Steps 0, 1, 62 and 63 are checked against the
     oracle: hash ids of all 256 sequences, and on sampled sequences the gathered rows (bit-exact), the gate
     pre-activation and the output stream (within tolerance)."""
     import torch
@@ -119,7 +120,7 @@ def test_decode_pipeline(gpu_device):
     for s in range(cfg.decode_steps):
         fused = s % 2 == 0
         outs = wl.fwd.step(wl.input_ids[:, P + s:P + s + 1].contiguous(), P + s, wl.x[s], None, output=True,
-                           fused=fused, packed=True)
+                           fused=fused, packed=True, hash_gather=s % 4 < 2)
         if s not in checked:
             continue
         torch.cuda.synchronize()
@@ -144,7 +145,7 @@ def test_decode_pipeline(gpu_device):
 
 def test_decode_step_graph_replays_match_eager(gpu_device):
     """The benchmark replays the decode step as a HIP graph: a graph of 8 one-token calls (fused and
-    four-entry-point projections alternating) replayed three times, with eager work and synchronisations in
+    four-entry-point projections alternating, the hash and gathers fused in half of them) replayed three times, with eager work and synchronisations in
     between, gives every call's dot and output bit for bit as the eager calls do, and leaves the same cache."""
     import torch
 
@@ -162,7 +163,8 @@ def test_decode_step_graph_replays_match_eager(gpu_device):
 
     def run():
         for s in range(steps):
-            outs = wl.fwd.step(step_ids[s], P + s, wl.x[s], None, output=True, fused=s % 2 == 0, packed=True)
+            outs = wl.fwd.step(step_ids[s], P + s, wl.x[s], None, output=True, fused=s % 2 == 0, packed=True,
+                               hash_gather=s % 4 < 2)
             for e in range(E):
                 hist[s, e].copy_(wl.fwd._bufs[("dot", e)][:B * hc].view(B, hc))
                 outs_hist[s, e].copy_(outs[e])
