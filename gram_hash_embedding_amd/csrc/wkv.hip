@@ -882,6 +882,49 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
     dot[t * hc + c] = hwk * rstd * rsqrt_dim;
 }
 
+// The same for a launch with few (token, copy) pairs (a decode step: 1,024 pairs, 4 workgroups above): the
+// slices of a pair are split over kGroups threads, kPer slices each, all their loads in flight at once
+// (one memory latency), and the group sums are added through LDS in group order.  Workgroup: kGroups x 32
+// consecutive tokens of one copy.
+constexpr int kFinGroups = 8;
+constexpr int kFinPer = 8;  // slices per thread at most: dim <= kFinGroups * kFinPer * 128
+__global__ __launch_bounds__(256) void gate_finalize_split_kernel(const float* part, float* dot, int64_t M, int hc,
+                                                                  int slices, float eps, float inv_dim,
+                                                                  float rsqrt_dim) {
+    __shared__ float red[kFinGroups][32][3];
+    const int g = threadIdx.x / 32, tl = threadIdx.x % 32;
+    const int64_t nb = (M + 31) / 32;
+    const int c = static_cast<int>(blockIdx.x / nb);
+    const int64_t t = (blockIdx.x - static_cast<int64_t>(c) * nb) * 32 + tl;
+    const int per = (slices + kFinGroups - 1) / kFinGroups;
+    const int s0 = g * per;
+    const float* src = part + static_cast<int64_t>(c) * slices * 3 * M + t;
+    float v[kFinPer][3];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            v[i][q] = (t < M && i < per && s0 + i < slices) ? src[(3 * (s0 + i) + q) * M] : 0.f;
+    float sum[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) sum[q] += v[i][q];  // slice order inside the group (zeros past its end)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) red[g][tl][q] = sum[q];
+    __syncthreads();
+    if (g != 0 || t >= M) return;
+    float hwk = 0.f, kk = 0.f, hh = 0.f;
+#pragma unroll
+    for (int j = 0; j < kFinGroups; ++j) {  // group order
+        hwk += red[j][tl][0];
+        kk += red[j][tl][1];
+        hh += red[j][tl][2];
+    }
+    const float rstd = rsqrtf(hh * inv_dim + eps) * rsqrtf(kk * inv_dim + eps);
+    dot[t * hc + c] = hwk * rstd * rsqrt_dim;
+}
+
 }  // namespace
 }  // namespace engram
 
@@ -991,8 +1034,16 @@ extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint1
     if (rc != ENGRAM_OK) return rc;
     const int64_t blocks = (T * hc + 255) / 256;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");
-    hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
-                       p.part, dot, T, hc, dim / 128, eps, 1.0f / static_cast<float>(dim),
-                       static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim))));
+    const int slices = dim / 128;
+    const float inv_dim = 1.0f / static_cast<float>(dim);
+    const float rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
+    if (blocks < kCUs && slices <= kFinGroups * kFinPer) {  // few pairs: one memory latency per pair
+        const int64_t split_blocks = static_cast<int64_t>(hc) * ((T + 31) / 32);
+        hipLaunchKernelGGL(gate_finalize_split_kernel, dim3(static_cast<unsigned>(split_blocks)), dim3(256), 0,
+                           as_stream(stream), p.part, dot, T, hc, slices, eps, inv_dim, rsqrt_dim);
+    } else {
+        hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
+                           p.part, dot, T, hc, slices, eps, inv_dim, rsqrt_dim);
+    }
     return check_launch("engram_wkv_gate (finalize)");
 }
