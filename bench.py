@@ -22,7 +22,9 @@ One step is timed five ways, each its own loop of `--steps` steps:
                   stored)
   fused_hash_gather  the fused path with the hash and every layer's gather in one
                   launch (engram_hash_gather_packed; packed table only)
-                  -- `value` and `ms_per_step` are the faster of these two
+  *_layers        (several layers) the same with every layer's projection in
+                  one launch (engram_wkv_gate_layers)
+                  -- `value` and `ms_per_step` are the fastest of these
                   (`config.value_path`)
   fused_*_table   the same on the other table layout
   unfused         the same path as four entry points (kv written, then read)
@@ -208,20 +210,20 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
 
-    def make_step(fused, output, packed, hg=False):
+    def make_step(fused, output, packed, hg=False, al=False):
         def step(events=None):
             if cfg.decode_steps:
                 for s in range(cfg.decode_steps):
                     fwd.step(step_ids[s], cfg.start_pos + s, wl.x[s], None, events=events, output=output,
-                             fused=fused, packed=packed, hash_gather=hg)
+                             fused=fused, packed=packed, hash_gather=hg, all_layers=al)
             else:
                 fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output,
-                         fused=fused, packed=packed, hash_gather=hg)
+                         fused=fused, packed=packed, hash_gather=hg, all_layers=al)
         return step
 
-    def loop(fused, output, packed, hg=False):
+    def loop(fused, output, packed, hg=False, al=False):
         """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
-        step = make_step(fused, output, packed, hg)
+        step = make_step(fused, output, packed, hg, al)
 
         for _ in range(args.warmup):
             step()
@@ -240,15 +242,20 @@ def main(argv=None):
     main_packed = args.table == "packed"
     paths = {}
     kern_events = {}
-    runs = [("fused", True, False, main_packed, False),
-            ("fused_" + ("pages_table" if main_packed else "packed_table"), True, False, not main_packed, False),
-            ("unfused", False, False, main_packed, False),
-            ("module_fused", True, True, main_packed, False),
-            ("module_unfused", False, True, main_packed, False)]
+    # the fused path's launch arrangements: hash and gathers separate or one launch (packed table), the layers'
+    # projections one launch each or one for all (more than one layer)
+    variants = [("fused", False, False)]
     if main_packed:
-        runs.insert(1, ("fused_hash_gather", True, False, True, True))
-    for name, fused, output, packed, hg in runs:
-        sec, ev = loop(fused, output, packed, hg)
+        variants.append(("fused_hash_gather", True, False))
+    if cfg.n_layers > 1:
+        variants += [(n + "_layers", hg, True) for n, hg, _ in variants]
+    runs = [(n, True, False, main_packed, hg, al) for n, hg, al in variants]
+    runs += [("fused_" + ("pages_table" if main_packed else "packed_table"), True, False, not main_packed, False, False),
+             ("unfused", False, False, main_packed, False, False),
+             ("module_fused", True, True, main_packed, False, False),
+             ("module_unfused", False, True, main_packed, False, False)]
+    for name, fused, output, packed, hg, al in runs:
+        sec, ev = loop(fused, output, packed, hg, al)
         paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
                        "table": "packed" if packed else "pages"}
         for k, v in ev.items():
@@ -259,11 +266,9 @@ def main(argv=None):
         # A decode step is 64 small calls: launched one by one from Python, the GPU waits on the host between
         # kernels.  The same step captured once as a HIP graph (the library's launches on torch's capture
         # stream; every buffer already allocated) and replayed measures the path itself; that is `value`.
-        graphs = [("fused", True, False, False), ("unfused", False, False, False)]
-        if main_packed:
-            graphs.insert(1, ("fused_hash_gather", True, False, True))
-        for name, fused, output, hg in graphs:
-            step = make_step(fused, output, main_packed, hg)
+        graphs = [(n, True, False, hg, al) for n, hg, al in variants] + [("unfused", False, False, False, False)]
+        for name, fused, output, hg, al in graphs:
+            step = make_step(fused, output, main_packed, hg, al)
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
@@ -284,11 +289,11 @@ def main(argv=None):
                                       "table": "packed" if main_packed else "pages"}
             del graph
         value_mode = "hip_graph"
-    # `value`: the fused path, its hash and gathers as separate launches or as one (whichever is faster here:
-    # one launch at decode, separate at a long prefill, where the standalone gather hides more latency)
+    # `value`: the fused path in its fastest launch arrangement here (hash and gathers: one launch at decode,
+    # separate at a long prefill, where the standalone gather hides more latency; with several layers, their
+    # projections as one launch or one each)
     suffix = "_graph" if value_mode == "hip_graph" else ""
-    value_path = min((n + suffix for n in ("fused", "fused_hash_gather") if n + suffix in paths),
-                     key=lambda n: paths[n]["ms_per_step"])
+    value_path = min((n + suffix for n, _, _ in variants), key=lambda n: paths[n]["ms_per_step"])
     sec_main = paths[value_path]["ms_per_step"] / 1e3
     value = T / sec_main
 
@@ -310,9 +315,11 @@ def main(argv=None):
         hg_bytes = algo["hash_bytes"] + E * (algo["gather_bytes"] - 8 * cfg.n_hash_cols)
         hg["GB/s"] = round(T_launch * hg_bytes / (hg["avg_us"] * 1e3), 1)
         hg["frac_hbm"] = round(hg["GB/s"] / PEAK_HBM_GBS, 4)
-    for name in ("wkv", "wkv_gate"):
+    for name, layers in (("wkv", 1), ("wkv_gate", 1), ("wkv_gate_layers", E)):
+        if name not in kern:
+            continue
         w = kern[name]
-        w["TFLOP/s"] = round(T_launch * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
+        w["TFLOP/s"] = round(layers * T_launch * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
         w["frac_mfma"] = round(w["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
     for name, key in (("gate_dot", "gate_bytes"), ("gate_output", "gate_output_bytes"),
                       ("gate_residual", "gate_residual_bytes")):

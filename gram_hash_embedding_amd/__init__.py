@@ -16,6 +16,7 @@ an exception is raised.
     engram_gate_dot        -- per-(token, copy) RMS-normalised gate pre-activation
     engram_gate_output     -- the dot, the sigmoid gate, the token mask and the residual add
     engram_wkv_gate        -- wkv + gate dot fused: value columns and dot out, keys never stored
+    engram_wkv_gate_layers -- engram_wkv_gate for several engram layers in one launch
     engram_gate_residual   -- gate, token mask and residual add from a given dot
 """
 from __future__ import annotations
@@ -57,10 +58,12 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_output.argtypes = [p, p, i64, p, p, f32, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate.argtypes = [p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
+        L.engram_wkv_gate_layers.argtypes = [i32, p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
         for f in (L.engram_hash, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
+                  L.engram_wkv_gate_layers,
                   L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
@@ -382,6 +385,57 @@ def engram_wkv_gate(a, w, x, q_weight, k_weight, eps, value=None, dot=None, work
     return value, dot
 
 
+def engram_wkv_gate_layers(a, w, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None, stream=None):
+    """engram_wkv_gate for E layers in one launch: a, w, x, q_weight, k_weight are lists of E tensors shaped as
+    engram_wkv_gate takes them (one T, K, hc and dim for all); returns (values, dots), lists of E tensors.
+    `value` (list) entries may be [T, ld >= dim] row-strided views, all with one row stride; `workspace` a uint8
+    device tensor of E * engram_wkv_gate_workspace_bytes bytes (allocated here if not given)."""
+    import torch
+
+    E = len(a)
+    if not (len(w) == len(x) == len(q_weight) == len(k_weight) == E) or E < 1:
+        raise ValueError("one a, w, x, q_weight and k_weight per layer")
+    x3 = [t.reshape(-1, t.shape[-2], t.shape[-1]) for t in x]
+    T, hc, dim = x3[0].shape
+    K = a[0].shape[1] if a[0].dim() == 2 else -1
+    for e in range(E):
+        if a[e].dim() != 2 or tuple(a[e].shape) != (T, K):
+            raise ValueError("every a must be [T, K] with one T and K")
+        if tuple(x3[e].shape) != (T, hc, dim):
+            raise ValueError("every x must be [T, hc, dim] with one T, hc and dim")
+        if tuple(w[e].shape) != ((hc + 1) * dim, K):
+            raise ValueError("every w must be [(hc+1)*dim, K]")
+        if tuple(q_weight[e].shape) != (hc, dim) or tuple(k_weight[e].shape) != (hc, dim):
+            raise ValueError("q_weight and k_weight must be [hc, dim]")
+    if value is None:
+        value = [torch.empty((T, dim), dtype=torch.bfloat16, device=a[0].device) for _ in range(E)]
+    if dot is None:
+        dot = [torch.empty((T, hc), dtype=torch.float32, device=a[0].device) for _ in range(E)]
+    if len(value) != E or len(dot) != E:
+        raise ValueError("one value and one dot per layer")
+    ld = value[0].stride(0)
+    for v in value:
+        if v.dim() != 2 or v.shape[0] != T or v.shape[1] < dim or v.stride(1) != 1 or v.stride(0) != ld:
+            raise ValueError("every value must be [T, >= dim] with unit column stride and one row stride")
+        if v.dtype != torch.bfloat16 or not v.is_cuda:
+            raise TypeError("value must be a bf16 GPU tensor")
+    for d in dot:
+        if tuple(d.shape) != (T, hc):
+            raise ValueError("dot must be [T, hc]")
+    need = E * engram_wkv_gate_workspace_bytes(T, hc, dim)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a[0].device)
+    arr = lambda ts, name, dt, nd: (ctypes.c_void_p * E)(*[_dev(t, f"{name}[{i}]", dt, nd).value
+                                                          for i, t in enumerate(ts)])
+    vals = (ctypes.c_void_p * E)(*[v.data_ptr() for v in value])
+    _check(lib().engram_wkv_gate_layers(
+        E, arr(a, "a", torch.bfloat16, 2), arr(w, "w", torch.bfloat16, 2), arr(x3, "x", torch.bfloat16, 3),
+        arr(q_weight, "q_weight", torch.bfloat16, 2), arr(k_weight, "k_weight", torch.bfloat16, 2), float(eps),
+        vals, ld, arr(dot, "dot", torch.float32, 2), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        T, K, hc, dim, _stream(stream)))
+    return value, dot
+
+
 def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
     """out bf16 (x's shape: [T, hc, dim] or [B, L, hc, dim]) = x + gate(dot) * value, from value bf16
     [T, >= dim] (row-strided view allowed) and dot float32 [T, hc]; token_mask [T] or [B, L]
@@ -414,6 +468,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
-           "engram_wkv_gate", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

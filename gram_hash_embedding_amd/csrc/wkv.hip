@@ -79,35 +79,47 @@ constexpr int kNonTemporal = 2;
 // word 3 of a raw buffer resource on gfx9-family targets (32-bit data format, no swizzle)
 constexpr int kBufferWord3 = 0x00020000;
 
-struct WkvArgs {
+constexpr int kMaxLayers = 8;  // engram layers one launch may take (their tiles share the CUs)
+
+// One layer's operands (every layer of a launch has the same M, N, K, hc and dim).
+struct LayerPtrs {
     const uint16_t* a;
     const uint16_t* w;
-    uint16_t* kv;      // stored output rows: columns [out_col0, N) of the product, row stride ld_out
-    int64_t M;
-    int N, K;
-    int tiles_m, tiles_n;
-    int64_t ld_out;
-    int out_col0;
+    uint16_t* kv;       // stored output rows: columns [out_col0, N) of the product, row stride ld_out
     // fused gate partial sums (key columns [0, hc*dim) are reduced, not stored)
     const uint16_t* x;  // [M, hc, dim] bf16
     const uint16_t* q;  // [hc, dim] bf16
     const uint16_t* k;  // [hc, dim] bf16
     float* part;        // [hc][dim/128][3][M] fp32: per 128-column slice pair sum(h w key), sum(key^2), sum(h^2)
+};
+
+struct WkvArgs {
+    LayerPtrs lay[kMaxLayers];  // indexed with a wave-uniform layer: one scalar load from the kernel arguments
+    int64_t M;
+    int N, K;
+    int tiles_m, tiles_n;  // tiles_m = layers * tiles_ml: the layers' M tiles stacked, layer by layer
+    int tiles_ml;          // M tiles of one layer
+    int64_t ld_out;
+    int out_col0;
     int hc, dim;
 };
 
-// pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
+// pid -> (tm, tn).  Layer by layer (a persistent workgroup finishes its tiles of one layer before it starts
+// the next, so the CUs share one layer's W panels at a time); inside a layer, contiguous runs per XCD (pid % 8
+// is the XCD a workgroup lands on), grouped kGroupM deep.
 __device__ inline void tile_coords(const WkvArgs& p, int pid, int& tm, int& tn) {
-    const int n = p.tiles_m * p.tiles_n;
+    const int n = p.tiles_ml * p.tiles_n;
+    const int layer = pid / n;
+    pid -= layer * n;
     const int xcd = pid % kXcds, idx = pid / kXcds;
     const int per = n / kXcds, rem = n % kXcds;
     const int logical = xcd * per + min(xcd, rem) + idx;
     const int in_group = kGroupM * p.tiles_n;
     const int group = logical / in_group;
     const int first_m = group * kGroupM;
-    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int gsize = min(p.tiles_ml - first_m, kGroupM);
     const int r = logical - group * in_group;
-    tm = first_m + r % gsize;
+    tm = layer * p.tiles_ml + first_m + r % gsize;
     tn = r / gsize;
 }
 
@@ -171,7 +183,7 @@ __device__ inline void store_tile(const WkvArgs& p, const f32x16 (&acc)[4][4], i
     for (int i = 0; i < 4; ++i) {
         const int64_t m = tok0 + 32 * i;
         if (m >= p.M) continue;
-        uint16_t* row = p.kv + m * p.N;
+        uint16_t* row = p.lay[0].kv + m * p.N;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -270,6 +282,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     const int wm = wave & 1, wn = wave >> 1;
     const bool loader = wave < 4;
     const int KT = p.K / BK;
+    // tile pid -> its layer, first token inside the layer and first output column
+    auto tile_of = [&](int pid, int& e, int64_t& m0, int& n0) {
+        int tm, tn;
+        tile_coords(p, pid, tm, tn);
+        e = tm / p.tiles_ml;
+        m0 = static_cast<int64_t>(tm - e * p.tiles_ml) * kBM;
+        n0 = tn * BN;
+    };
+    int cur = 0;  // the layer of the tile in the epilogue (the tile loops set it)
 
     // A barrier that publishes LDS: every wave's LDS accesses are done (lgkmcnt); the loaders wait for
     // their slab loads (vmcnt) right before it.  The empty asm statements keep the compiler from moving
@@ -303,16 +324,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
     // block as the MFMAs they are interleaved with.  An empty resource zero-fills a free stage.
     auto issue_slab = [&](const SlabCursor& c, int stage, bool live) {
-        int tm, tn;
-        tile_coords(p, live ? c.pid : static_cast<int>(blockIdx.x), tm, tn);
-        const int64_t m0 = static_cast<int64_t>(tm) * kBM;
-        const int n0 = tn * BN;
+        int e, n0;
+        int64_t m0;
+        tile_of(live ? c.pid : static_cast<int>(blockIdx.x), e, m0, n0);
+        const LayerPtrs& L = p.lay[e];
         const int rows_a = live ? static_cast<int>(min<int64_t>(kBM, p.M - m0)) : 0;
         const int rows_w = live ? min(BN, p.N - n0) : 0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(p.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
+            const_cast<uint16_t*>(L.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(p.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
+            const_cast<uint16_t*>(L.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
         const uint32_t k0b = static_cast<uint32_t>(c.kt * BK * 2);
         uint8_t* sa = lds + stage * kStageBytes + wave * 16 * NI * 128;
         uint8_t* sw = lds + stage * kStageBytes + kABytes + wave * 64 * 128;
@@ -383,7 +404,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                     const int64_t m = m0 + (rr >> 5) * 32 * NI + 32 * i + (rr & 31);
                     if (m < p.M && col_ok)
                         __builtin_nontemporal_store(
-                            v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + (n0 - p.out_col0) + chunk * 8));
+                            v, reinterpret_cast<u32x4*>(p.lay[cur].kv + m * p.ld_out + (n0 - p.out_col0) + chunk * 8));
                 }
             }
             sync_epi();
@@ -424,7 +445,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
         for (int v = 0; v < kAreas; ++v) {
             const int ow = wave - 4 * v;  // owner wave of the area
-            const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
+            const uint16_t* xs = p.lay[cur].x + static_cast<int64_t>(c) * p.dim + colw + (ow >> 1) * 64;
 #pragma unroll
             for (int ins = 0; ins < 4; ++ins) {
                 const int r = 8 * ins + (ll >> 3);
@@ -455,8 +476,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         const int l = lane_id();
         const int c = n0 / p.dim;
         const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice
-        const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
-        const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        const uint16_t* qrow = p.lay[cur].q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        const uint16_t* krow = p.lay[cur].k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
         float wgt[2][4][4];  // q * k (exact in fp32) for the lane's 32 columns
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -540,7 +561,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 const float* partner = reinterpret_cast<const float*>(hand + (wave - 4) * kXArea);
                 const int64_t tbase = m0 + wm * 32 * NI + ls;
                 const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
-                float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
+                float* out = p.lay[cur].part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int64_t t = tbase + 32 * i;
@@ -688,10 +709,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         };
         if constexpr (kOneTile) {
             for (; pid < tiles; pid += G) {  // one tile per workgroup
-                int tm, tn;
-                tile_coords(p, pid, tm, tn);
-                const int64_t m0 = static_cast<int64_t>(tm) * kBM;
-                const int n0 = tn * BN;
+                int64_t m0;
+                int n0;
+                tile_of(pid, cur, m0, n0);
                 auto body = [&](auto key_tag) {
                     constexpr bool kKey = decltype(key_tag)::value;
                     using Ph0 = std::integral_constant<int, 0>;
@@ -717,10 +737,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             return;
         }
         for (; pid < tiles; pid += G) {
-            int tm, tn;
-            tile_coords(p, pid, tm, tn);
-            const int64_t m0 = static_cast<int64_t>(tm) * kBM;
-            const int n0 = tn * BN;
+            int64_t m0;
+            int n0;
+            tile_of(pid, cur, m0, n0);
             const bool key_tile = kGate && n0 < p.out_col0;
             if (key_tile) {
                 // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
@@ -784,8 +803,8 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_staged(WkvArgs p) {
         if (m >= p.M) m = p.M - 1;
         int n = n0 + ld_row + 32 * i;
         if (n >= p.N) n = p.N - 1;
-        a_src[i] = p.a + m * p.K + ld_col;
-        w_src[i] = p.w + static_cast<int64_t>(n) * p.K + ld_col;
+        a_src[i] = p.lay[0].a + m * p.K + ld_col;
+        w_src[i] = p.lay[0].w + static_cast<int64_t>(n) * p.K + ld_col;
     }
     u32x4 ra[8], rw[8];
     auto load_slab = [&](int k0) {
@@ -848,8 +867,21 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_kernel_staged(WkvArgs p) {
 // ============================================================================
 // gate finalize: the fused kernel's per-slice partial sums -> dot (fixed summation order)
 // ============================================================================
-__global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, float* dot, int64_t M, int hc,
-                                                            int slices, float eps, float inv_dim, float rsqrt_dim) {
+// The finalize of every layer of a launch: blockIdx.y is the layer.
+struct FinArgs {
+    const float* part;    // layer 0's workspace; layer e's follows at e * part_stride floats
+    int64_t part_stride;
+    float* dot[kMaxLayers];
+    int64_t M;
+    int hc, slices;
+    float eps, inv_dim, rsqrt_dim;
+};
+
+__global__ __launch_bounds__(256) void gate_finalize_kernel(FinArgs f) {
+    const float* part = f.part + blockIdx.y * f.part_stride;
+    float* dot = f.dot[blockIdx.y];
+    const int64_t M = f.M;
+    const int hc = f.hc, slices = f.slices;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (idx >= M * hc) return;
     const int c = static_cast<int>(idx / M);  // consecutive threads: consecutive tokens of one copy
@@ -878,8 +910,8 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
         kk += src[(3 * s0 + 1) * M];
         hh += src[(3 * s0 + 2) * M];
     }
-    const float rstd = rsqrtf(hh * inv_dim + eps) * rsqrtf(kk * inv_dim + eps);
-    dot[t * hc + c] = hwk * rstd * rsqrt_dim;
+    const float rstd = rsqrtf(hh * f.inv_dim + f.eps) * rsqrtf(kk * f.inv_dim + f.eps);
+    dot[t * hc + c] = hwk * rstd * f.rsqrt_dim;
 }
 
 // The same for a launch with few (token, copy) pairs (a decode step: 1,024 pairs, 4 workgroups above): the
@@ -888,10 +920,12 @@ __global__ __launch_bounds__(256) void gate_finalize_kernel(const float* part, f
 // consecutive tokens of one copy.
 constexpr int kFinGroups = 8;
 constexpr int kFinPer = 8;  // slices per thread at most: dim <= kFinGroups * kFinPer * 128
-__global__ __launch_bounds__(256) void gate_finalize_split_kernel(const float* part, float* dot, int64_t M, int hc,
-                                                                  int slices, float eps, float inv_dim,
-                                                                  float rsqrt_dim) {
+__global__ __launch_bounds__(256) void gate_finalize_split_kernel(FinArgs f) {
     __shared__ float red[kFinGroups][32][3];
+    const float* part = f.part + blockIdx.y * f.part_stride;
+    float* dot = f.dot[blockIdx.y];
+    const int64_t M = f.M;
+    const int hc = f.hc, slices = f.slices;
     const int g = threadIdx.x / 32, tl = threadIdx.x % 32;
     const int64_t nb = (M + 31) / 32;
     const int c = static_cast<int>(blockIdx.x / nb);
@@ -921,8 +955,8 @@ __global__ __launch_bounds__(256) void gate_finalize_split_kernel(const float* p
         kk += red[j][tl][1];
         hh += red[j][tl][2];
     }
-    const float rstd = rsqrtf(hh * inv_dim + eps) * rsqrtf(kk * inv_dim + eps);
-    dot[t * hc + c] = hwk * rstd * rsqrt_dim;
+    const float rstd = rsqrtf(hh * f.inv_dim + f.eps) * rsqrtf(kk * f.inv_dim + f.eps);
+    dot[t * hc + c] = hwk * rstd * f.rsqrt_dim;
 }
 
 }  // namespace
@@ -932,19 +966,22 @@ using namespace engram;
 
 namespace {
 
-// Tokens per tile of the main kernel: 256 (NI = 4), or 128 (NI = 2) when 128-token tiles still fit the CUs
-// in one pass -- small launches (a decode step) then use twice the CUs.
-int tile_ni(int64_t T, int tiles_n, int K) { return K >= 4 * BK && ((T + 127) / 128) * tiles_n <= kCUs ? 2 : 4; }
+// Tokens per tile of the main kernel: 256 (NI = 4), or 128 (NI = 2) when 128-token tiles of all the launch's
+// layers still fit the CUs in one pass -- small launches (a decode step of one layer) then use twice the CUs.
+int tile_ni(int64_t T, int tiles_n, int K, int layers) {
+    return K >= 4 * BK && ((T + 127) / 128) * tiles_n * layers <= kCUs ? 2 : 4;
+}
 
-// Launch the persistent main kernel over all tiles of p (p.tiles_n set; p.tiles_m filled in here).
+// Launch the persistent main kernel over all tiles of p's `layers` layers (p.tiles_n set; the M tiles here).
 template <bool kGate>
-int launch_main(WkvArgs& p, int64_t T, hipStream_t stream, const char* what) {
-    const int ni = tile_ni(T, p.tiles_n, p.K);
+int launch_main(WkvArgs& p, int64_t T, int layers, hipStream_t stream, const char* what) {
+    const int ni = tile_ni(T, p.tiles_n, p.K, layers);
     const int64_t bm = 64 * ni;
-    const int64_t tiles_m = (T + bm - 1) / bm;
-    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
-    p.tiles_m = static_cast<int>(tiles_m);
-    const int64_t tiles = tiles_m * p.tiles_n;
+    const int64_t tiles_ml = (T + bm - 1) / bm;
+    if (tiles_ml * layers * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
+    p.tiles_ml = static_cast<int>(tiles_ml);
+    p.tiles_m = static_cast<int>(tiles_ml * layers);
+    const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
     if (ni == 2 && tiles > kCUs) return fail(ENGRAM_EINVAL, "%s: one-tile launch with %lld tiles", what, (long long)tiles);
     if (ni == 2)
@@ -965,20 +1002,21 @@ extern "C" int engram_wkv(const uint16_t* a, const uint16_t* w, uint16_t* kv, in
     if (!a || !w || !kv) return fail(ENGRAM_EINVAL, "engram_wkv: null pointer");
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(kv, 16)) return fail(ENGRAM_EINVAL, "engram_wkv: misaligned pointer");
     WkvArgs p = {};
-    p.a = a;
-    p.w = w;
-    p.kv = kv;
+    p.lay[0].a = a;
+    p.lay[0].w = w;
+    p.lay[0].kv = kv;
     p.M = T;
     p.N = Nout;
     p.K = K;
     p.ld_out = Nout;
     p.out_col0 = 0;
     p.tiles_n = (Nout + BN - 1) / BN;
-    if (K % BK == 0) return launch_main<false>(p, T, as_stream(stream), "engram_wkv");
+    if (K % BK == 0) return launch_main<false>(p, T, 1, as_stream(stream), "engram_wkv");
     {
         const int64_t tiles_m = (T + BM - 1) / BM;
         if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv: too many tiles");
         p.tiles_m = static_cast<int>(tiles_m);
+        p.tiles_ml = p.tiles_m;
         const int64_t tiles = tiles_m * p.tiles_n;
         hipLaunchKernelGGL(wkv_kernel_staged, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
                            as_stream(stream), p);
@@ -991,59 +1029,99 @@ extern "C" int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_
     return static_cast<int64_t>(hc) * (dim / 128) * 3 * T * static_cast<int64_t>(sizeof(float));
 }
 
-extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
-                               const uint16_t* k_weight, float eps, uint16_t* value, int64_t ld_value, float* dot,
-                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc,
-                               int32_t dim, void* stream) {
-    if (T < 0) return fail(ENGRAM_EINVAL, "engram_wkv_gate: T < 0");
-    if (K < BK || K % BK != 0) return fail(ENGRAM_EINVAL, "engram_wkv_gate: K=%d must be a positive multiple of %d", K, BK);
-    if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "engram_wkv_gate: hc=%d outside [1, 64]", hc);
+namespace {
+
+// engram_wkv_gate over `layers` layers in one launch of the main kernel and one of the finalize; arrays of
+// `layers` entries (host memory).  The workspace holds the layers' partial sums one after another.
+int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const uint16_t* const* w,
+                   const uint16_t* const* x, const uint16_t* const* q_weight, const uint16_t* const* k_weight,
+                   float eps, uint16_t* const* value, int64_t ld_value, float* const* dot, void* workspace,
+                   int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc, int32_t dim, void* stream) {
+    if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", what);
+    if (K < BK || K % BK != 0) return fail(ENGRAM_EINVAL, "%s: K=%d must be a positive multiple of %d", what, K, BK);
+    if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "%s: hc=%d outside [1, 64]", what, hc);
     if (dim < 256 || dim % 256 != 0)
-        return fail(ENGRAM_EINVAL, "engram_wkv_gate: dim=%d must be a positive multiple of 256", dim);
+        return fail(ENGRAM_EINVAL, "%s: dim=%d must be a positive multiple of 256", what, dim);
     if (ld_value < dim || ld_value % 8 != 0)
-        return fail(ENGRAM_EINVAL, "engram_wkv_gate: ld_value=%lld must be >= dim and a multiple of 8",
-                    (long long)ld_value);
-    const int64_t need = engram_wkv_gate_workspace_bytes(T, hc, dim);
+        return fail(ENGRAM_EINVAL, "%s: ld_value=%lld must be >= dim and a multiple of 8", what, (long long)ld_value);
+    const int64_t per_layer = engram_wkv_gate_workspace_bytes(T, hc, dim);
+    const int64_t need = per_layer * layers;
     if (workspace_bytes < need)
-        return fail(ENGRAM_ERANGE, "engram_wkv_gate: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+        return fail(ENGRAM_ERANGE, "%s: workspace of %lld bytes, %lld needed", what, (long long)workspace_bytes,
                     (long long)need);
     if (T == 0) return ENGRAM_OK;
-    if (!a || !w || !x || !q_weight || !k_weight || !value || !dot || !workspace)
-        return fail(ENGRAM_EINVAL, "engram_wkv_gate: null pointer");
-    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(x, 16) || !aligned(q_weight, 16) || !aligned(k_weight, 16) ||
-        !aligned(value, 16) || !aligned(dot, 4) || !aligned(workspace, 16))
-        return fail(ENGRAM_EINVAL, "engram_wkv_gate: misaligned pointer");
+    if (!workspace) return fail(ENGRAM_EINVAL, "%s: null pointer", what);
+    if (!aligned(workspace, 16)) return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
     const int Nout = (hc + 1) * dim;
     WkvArgs p = {};
-    p.a = a;
-    p.w = w;
-    p.kv = value;
+    FinArgs f = {};
+    for (int e = 0; e < layers; ++e) {
+        if (!a[e] || !w[e] || !x[e] || !q_weight[e] || !k_weight[e] || !value[e] || !dot[e])
+            return fail(ENGRAM_EINVAL, "%s: layer %d: null pointer", what, e);
+        if (!aligned(a[e], 16) || !aligned(w[e], 16) || !aligned(x[e], 16) || !aligned(q_weight[e], 16) ||
+            !aligned(k_weight[e], 16) || !aligned(value[e], 16) || !aligned(dot[e], 4))
+            return fail(ENGRAM_EINVAL, "%s: layer %d: misaligned pointer", what, e);
+        LayerPtrs& L = p.lay[e];
+        L.a = a[e];
+        L.w = w[e];
+        L.kv = value[e];
+        L.x = x[e];
+        L.q = q_weight[e];
+        L.k = k_weight[e];
+        L.part = static_cast<float*>(workspace) + e * (per_layer / static_cast<int64_t>(sizeof(float)));
+        f.dot[e] = dot[e];
+    }
     p.M = T;
     p.N = Nout;
     p.K = K;
     p.ld_out = ld_value;
     p.out_col0 = hc * dim;
-    p.x = x;
-    p.q = q_weight;
-    p.k = k_weight;
-    p.part = static_cast<float*>(workspace);
     p.hc = hc;
     p.dim = dim;
     p.tiles_n = Nout / BN;
-    int rc = launch_main<true>(p, T, as_stream(stream), "engram_wkv_gate");
+    int rc = launch_main<true>(p, T, layers, as_stream(stream), what);
     if (rc != ENGRAM_OK) return rc;
     const int64_t blocks = (T * hc + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_wkv_gate: too many tokens");
-    const int slices = dim / 128;
-    const float inv_dim = 1.0f / static_cast<float>(dim);
-    const float rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
-    if (blocks < kCUs && slices <= kFinGroups * kFinPer) {  // few pairs: one memory latency per pair
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tokens", what);
+    f.part = static_cast<const float*>(workspace);
+    f.part_stride = per_layer / static_cast<int64_t>(sizeof(float));
+    f.M = T;
+    f.hc = hc;
+    f.slices = dim / 128;
+    f.eps = eps;
+    f.inv_dim = 1.0f / static_cast<float>(dim);
+    f.rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
+    if (blocks * layers < kCUs && f.slices <= kFinGroups * kFinPer) {  // few pairs: one memory latency per pair
         const int64_t split_blocks = static_cast<int64_t>(hc) * ((T + 31) / 32);
-        hipLaunchKernelGGL(gate_finalize_split_kernel, dim3(static_cast<unsigned>(split_blocks)), dim3(256), 0,
-                           as_stream(stream), p.part, dot, T, hc, slices, eps, inv_dim, rsqrt_dim);
+        hipLaunchKernelGGL(gate_finalize_split_kernel, dim3(static_cast<unsigned>(split_blocks), layers), dim3(256),
+                           0, as_stream(stream), f);
     } else {
-        hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream),
-                           p.part, dot, T, hc, slices, eps, inv_dim, rsqrt_dim);
+        hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks), layers), dim3(256), 0,
+                           as_stream(stream), f);
     }
-    return check_launch("engram_wkv_gate (finalize)");
+    return check_launch(what);
+}
+
+}  // namespace
+
+extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint16_t* x, const uint16_t* q_weight,
+                               const uint16_t* k_weight, float eps, uint16_t* value, int64_t ld_value, float* dot,
+                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc,
+                               int32_t dim, void* stream) {
+    return wkv_gate_entry("engram_wkv_gate", 1, &a, &w, &x, &q_weight, &k_weight, eps, &value, ld_value, &dot,
+                          workspace, workspace_bytes, T, K, hc, dim, stream);
+}
+
+extern "C" int engram_wkv_gate_layers(int32_t layers, const uint16_t* const* a, const uint16_t* const* w,
+                                      const uint16_t* const* x, const uint16_t* const* q_weight,
+                                      const uint16_t* const* k_weight, float eps, uint16_t* const* value,
+                                      int64_t ld_value, float* const* dot, void* workspace, int64_t workspace_bytes,
+                                      int64_t T, int32_t K, int32_t hc, int32_t dim, void* stream) {
+    const char* what = "engram_wkv_gate_layers";
+    if (layers < 1 || layers > kMaxLayers)
+        return fail(ENGRAM_EINVAL, "%s: layers=%d outside [1, %d]", what, layers, kMaxLayers);
+    if (T > 0 && (!a || !w || !x || !q_weight || !k_weight || !value || !dot))
+        return fail(ENGRAM_EINVAL, "%s: null pointer array", what);
+    return wkv_gate_entry(what, layers, a, w, x, q_weight, k_weight, eps, value, ld_value, dot, workspace,
+                          workspace_bytes, T, K, hc, dim, stream);
 }

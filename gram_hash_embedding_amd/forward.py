@@ -19,7 +19,7 @@ from typing import List, Optional
 
 from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
                engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_wkv, engram_wkv_gate,
-               engram_wkv_gate_workspace_bytes)
+               engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes)
 
 
 @dataclasses.dataclass
@@ -120,6 +120,23 @@ class EngramForward:
             hash_ids=ids))
         return ids, outs
 
+    def gather(self, e: int, hash_ids, events=None, packed=False):
+        """Layer e's rows bf16 [T, C, D] (this object's buffer) from its table, or its packed copy."""
+        import torch
+
+        lw = self.layers[e]
+        T = hash_ids.shape[0] * hash_ids.shape[1]
+        a = self._buf(("a", e), (T, self.C, lw.weight.shape[1]), torch.bfloat16, hash_ids.device)
+        if packed:
+            if lw.packed is None:
+                raise ValueError(f"layer {e} has no packed table")
+            self._timed(events, "gather_dequant_packed", lambda: engram_gather_dequant_packed(
+                hash_ids, lw.packed, lw.block_size, lw.row_start, layer=e, out=a))
+        else:
+            self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
+                hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
+        return a
+
     def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False, packed=False,
               a=None):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim]
@@ -135,18 +152,9 @@ class EngramForward:
 
         lw = self.layers[e]
         T = hash_ids.shape[0] * hash_ids.shape[1]
-        D = lw.weight.shape[1]
         dev = hash_ids.device
         if a is None:
-            a = self._buf(("a", e), (T, self.C, D), torch.bfloat16, dev)
-            if packed:
-                if lw.packed is None:
-                    raise ValueError(f"layer {e} has no packed table")
-                self._timed(events, "gather_dequant_packed", lambda: engram_gather_dequant_packed(
-                    hash_ids, lw.packed, lw.block_size, lw.row_start, layer=e, out=a))
-            else:
-                self._timed(events, "gather_dequant", lambda: engram_gather_dequant(
-                    hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
+            a = self.gather(e, hash_ids, events, packed)
         x3 = x.reshape(T, x.shape[-2], x.shape[-1])
         dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
         if fused:
@@ -171,21 +179,54 @@ class EngramForward:
         return a, kv, dot
 
     def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False,
-             packed=False, hash_gather=False):
+             packed=False, hash_gather=False, all_layers=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
         (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
-        With `hash_gather`, the hash and every layer's packed gather are one launch.
+        With `hash_gather`, the hash and every layer's packed gather are one launch; with `all_layers`
+        (fused only), every layer's projection and gate pre-activation are one launch (their tiles share
+        the CUs).
         `events`: optional dict that collects (start, end) timing events per entry point."""
         if hash_gather:
             ids, rows = self.hash_gather(input_ids, start_pos, token_mask, events)
         else:
             ids, rows = self.hash(input_ids, start_pos, token_mask, events), [None] * self.E
+        if all_layers:
+            if not fused:
+                raise ValueError("all_layers needs the fused projection")
+            return self._fused_all_layers(ids, rows, xs, events, token_mask, output, packed)
         res = []
         for e in range(self.E):
             x = xs[e] if isinstance(xs, (list, tuple)) else xs
             res.append(self.layer(e, ids, x, events, token_mask=token_mask, output=output, fused=fused,
                                   packed=packed, a=rows[e])[-1])
+        return res
+
+
+    def _fused_all_layers(self, ids, rows, xs, events, token_mask, output, packed):
+        import torch
+
+        dev = ids.device
+        T = ids.shape[0] * ids.shape[1]
+        rows = [r if r is not None else self.gather(e, ids, events, packed) for e, r in enumerate(rows)]
+        x_of = [xs[e] if isinstance(xs, (list, tuple)) else xs for e in range(self.E)]
+        x3 = [x.reshape(T, x.shape[-2], x.shape[-1]) for x in x_of]
+        hc, dim = x3[0].shape[1], x3[0].shape[2]
+        values = [self._buf(("value", e), (T, dim), torch.bfloat16, dev) for e in range(self.E)]
+        dots = [self._buf(("dot", e), (T, hc), torch.float32, dev) for e in range(self.E)]
+        ws = self._buf("workspace", (self.E * engram_wkv_gate_workspace_bytes(T, hc, dim),), torch.uint8, dev)
+        L = self.layers
+        self._timed(events, "wkv_gate_layers", lambda: engram_wkv_gate_layers(
+            [r.view(T, -1) for r in rows], [lw.wkv for lw in L], x3, [lw.q_weight for lw in L],
+            [lw.k_weight for lw in L], self.eps, value=values, dot=dots, workspace=ws))
+        if not output:
+            return dots
+        res = []
+        for e in range(self.E):
+            out = self._buf(("out", e), tuple(x_of[e].shape), torch.bfloat16, dev)
+            self._timed(events, "gate_residual", lambda: engram_gate_residual(x_of[e], values[e], dots[e], token_mask,
+                                                                              out=out))
+            res.append(out)
         return res
 
 

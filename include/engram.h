@@ -319,6 +319,28 @@ int engram_gate_residual(const uint16_t* x, const uint16_t* value, int64_t ld_va
  * floats), or -1 if hc or dim is outside the limits above. */
 int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_t dim);
 
+/*
+ * engram_wkv_gate_layers -- engram_wkv_gate for `layers` engram layers of one
+ * forward call (stack-hashes page: each engram layer's Engram.forward, up to
+ * `dot`), as one launch of the projection and one of the finalize: the layers'
+ * tiles share the CUs, so a call too small to fill them with one layer (a
+ * decode step) fills them with all.  Per layer the results are engram_wkv_gate's
+ * (the value columns bit for bit; the dot up to the order of its fp32 sums).
+ *
+ * a, w, x, q_weight, k_weight, value, dot  host arrays of `layers` device
+ *          pointers, each as engram_wkv_gate takes it; one T, K, hc, dim and
+ *          ld_value for all layers
+ * workspace  layers * engram_wkv_gate_workspace_bytes(T, hc, dim) bytes, 16-byte
+ *          aligned; caller-owned scratch
+ * Limits and errors: as engram_wkv_gate; 1 <= layers <= 8.  The host arrays are
+ * read during the call only.
+ */
+int engram_wkv_gate_layers(int32_t layers, const uint16_t* const* a, const uint16_t* const* w,
+                           const uint16_t* const* x, const uint16_t* const* q_weight,
+                           const uint16_t* const* k_weight, float eps, uint16_t* const* value, int64_t ld_value,
+                           float* const* dot, void* workspace, int64_t workspace_bytes, int64_t T, int32_t K,
+                           int32_t hc, int32_t dim, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) >= {"engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_gather_dequant_packed",
                           "engram_pack_table", "engram_wkv", "engram_gate_dot",
                           "engram_gate_output", "engram_wkv_gate", "engram_wkv_gate_workspace_bytes",
-                          "engram_gate_residual", "engram_status_string", "engram_last_error",
+                          "engram_gate_residual", "engram_wkv_gate_layers", "engram_status_string", "engram_last_error",
                           "engram_abi_version"}
     L = g.lib()
     for n in names:
@@ -85,6 +85,8 @@ def test_zero_tokens_is_a_valid_no_op():
     assert L.engram_gate_output(None, None, 80, None, None, 1e-20, None, None, None, 0, 4, 16, None) == 0
     assert L.engram_wkv_gate(None, None, None, None, None, 1e-20, None, 256, None, None, 0, 0, 64, 4, 256, None) == 0
     assert L.engram_gate_residual(None, None, 16, None, None, None, 0, 4, 16, None) == 0
+    assert L.engram_wkv_gate_layers(2, None, None, None, None, None, 1e-20, None, 256, None, None, 0, 0, 64, 4, 256,
+                                    None) == 0
 
 
 def _hash_gather(**kw):
@@ -236,3 +238,22 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g, "_lib", None)
     with pytest.raises(ImportError):
         g.lib()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(layers=0), 1, "layers=0"), (dict(layers=9), 1, "layers=9"), (dict(a=None), 1, "null pointer array"),
+    (dict(dot=None), 1, "null pointer array"), (dict(K=96), 1, "K=96"), (dict(dim=320), 1, "dim=320"),
+    (dict(ws_bytes=2 * 10 * 4 * 2 * 3 * 4 - 4), 2, "workspace"), (dict(ws=None), 1, "null"),
+    (dict(value=[FAKE.value, 0x100008]), 1, "layer 1: misaligned"), (dict(x=[FAKE.value, None]), 1, "layer 1: null"),
+])
+def test_wkv_gate_layers_validation(kw, status, msg):
+    a = dict(layers=2, a=[FAKE.value] * 2, w=[FAKE.value] * 2, x=[FAKE.value] * 2, q=[FAKE.value] * 2,
+             k=[FAKE.value] * 2, value=[FAKE.value] * 2, ld_value=256, dot=[FAKE.value] * 2, ws=FAKE,
+             ws_bytes=2 * 10 * 4 * 2 * 3 * 4, T=10, K=128, hc=4, dim=256)
+    a.update(kw)
+    arr = lambda v: None if v is None else (ctypes.c_void_p * len(v))(*v)
+    rc = g.lib().engram_wkv_gate_layers(a["layers"], arr(a["a"]), arr(a["w"]), arr(a["x"]), arr(a["q"]), arr(a["k"]),
+                                        1e-20, arr(a["value"]), a["ld_value"], arr(a["dot"]), a["ws"], a["ws_bytes"],
+                                        a["T"], a["K"], a["hc"], a["dim"], None)
+    assert rc == status
+    assert msg in _err()

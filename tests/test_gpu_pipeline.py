@@ -79,6 +79,15 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
                 v_got = bits(wl.fwd._bufs[("value", e)].view(T, -1)[sidx])
                 np.testing.assert_array_equal(v_got, bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])[:, hcd:],
                                               err_msg=f"fused value columns, layer {e}")
+            # every layer's fused projection in one launch (engram_wkv_gate_layers)
+            dots_l = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, fused=True, all_layers=True)
+            torch.cuda.synchronize()
+            for e in range(cfg.n_layers):
+                kv_o, dot_o = want[e]
+                assert_close(dots_l[e].view(T, -1)[sidx].cpu().numpy(), dot_o, what=f"dot (all layers) layer {e}")
+                v_got = bits(wl.fwd._bufs[("value", e)].view(T, -1)[sidx])
+                np.testing.assert_array_equal(v_got, bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])[:, hcd:],
+                                              err_msg=f"value columns (all layers), layer {e}")
         outs = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, output=True, fused=fused)
         torch.cuda.synchronize()
         for e in range(cfg.n_layers):
@@ -97,7 +106,8 @@ def test_decode_pipeline(gpu_device):
     """The decode workload as the benchmark runs it: the hash of the 4,096-token history, then 64 calls of
     one token per sequence through the whole path (through the residual), each with its own stream, the
     fused and the four-entry-point projection in turn, and the hash and gathers as one launch in half the
-    calls (steps 0 and 1 of every four).  Steps 0, 1, 62 and 63 are checked against the
+    calls (steps 0 and 1 of every four), the fused projections of both layers as one launch in a quarter
+    (step 0 of every four).  Steps 0, 1, 62 and 63 are checked against the
     oracle: hash ids of all 256 sequences, and on sampled sequences the gathered rows (bit-exact), the gate
     pre-activation and the output stream (within tolerance)."""
     import torch
@@ -120,7 +130,7 @@ def test_decode_pipeline(gpu_device):
     for s in range(cfg.decode_steps):
         fused = s % 2 == 0
         outs = wl.fwd.step(wl.input_ids[:, P + s:P + s + 1].contiguous(), P + s, wl.x[s], None, output=True,
-                           fused=fused, packed=True, hash_gather=s % 4 < 2)
+                           fused=fused, packed=True, hash_gather=s % 4 < 2, all_layers=s % 4 == 0)
         if s not in checked:
             continue
         torch.cuda.synchronize()
@@ -145,7 +155,8 @@ def test_decode_pipeline(gpu_device):
 
 def test_decode_step_graph_replays_match_eager(gpu_device):
     """The benchmark replays the decode step as a HIP graph: a graph of 8 one-token calls (fused and
-    four-entry-point projections alternating, the hash and gathers fused in half of them) replayed three times, with eager work and synchronisations in
+    four-entry-point projections alternating, the hash and gathers fused in half of them, both layers'
+    projections in one launch in a quarter) replayed three times, with eager work and synchronisations in
     between, gives every call's dot and output bit for bit as the eager calls do, and leaves the same cache."""
     import torch
 
@@ -164,7 +175,7 @@ def test_decode_step_graph_replays_match_eager(gpu_device):
     def run():
         for s in range(steps):
             outs = wl.fwd.step(step_ids[s], P + s, wl.x[s], None, output=True, fused=s % 2 == 0, packed=True,
-                               hash_gather=s % 4 < 2)
+                               hash_gather=s % 4 < 2, all_layers=s % 4 == 0)
             for e in range(E):
                 hist[s, e].copy_(wl.fwd._bufs[("dot", e)][:B * hc].view(B, hc))
                 outs_hist[s, e].copy_(outs[e])

@@ -123,3 +123,50 @@ def test_gate_residual_matches_gate_output_bit_for_bit(gpu_device, T, hc, dim, m
     x2 = x.clone()
     g.engram_gate_residual(x2, kv[:, hc * dim:], dot, mask, out=x2)
     np.testing.assert_array_equal(bits(x2), bits(want))
+
+
+# (E, T, K, hc, dim): the decode step's two layers (one launch of 2 x 100 tiles of 256 tokens, where one layer
+# alone takes 200 tiles of 128), a ragged token count, three layers whose 128-token tiles still fit the CUs
+# together, and layers of several tiles per CU.
+LAYER_SHAPES = [(2, 256, 1536, 4, 5120), (2, 130, 1536, 4, 5120), (3, 200, 256, 2, 512), (2, 700, 192, 3, 768),
+                (4, 64, 64, 1, 256)]
+
+
+@pytest.mark.parametrize("E,T,K,hc,dim", LAYER_SHAPES)
+def test_wkv_gate_layers_matches_per_layer_calls_and_the_oracle(gpu_device, E, T, K, hc, dim):
+    """engram_wkv_gate_layers: every layer's value columns bit for bit as engram_wkv_gate's (the same MFMA
+    sums over K), its dot within the fp32 summation-order tolerance of engram_wkv_gate's, and both against
+    the oracle on sampled tokens."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(E * 1000 + T + K + hc + dim)
+    ins = [_inputs(rng, T, K, hc, dim, gpu_device) for _ in range(E)]
+    values, dots = g.engram_wkv_gate_layers([i[0] for i in ins], [i[1] for i in ins], [i[2] for i in ins],
+                                            [i[3] for i in ins], [i[4] for i in ins], 1e-20)
+    singles = [g.engram_wkv_gate(*i, 1e-20) for i in ins]
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 256 else np.unique(np.r_[0, 127, 128, 255, 256, T - 1, rng.integers(0, T, 40)])
+    for e, (a, w, x, q, k) in enumerate(ins):
+        np.testing.assert_array_equal(bits(values[e]), bits(singles[e][0]), err_msg=f"layer {e} value")
+        assert_close(dots[e].cpu().numpy(), singles[e][1].cpu().numpy(), rtol=1e-3, atol=1e-4, what=f"layer {e} dot")
+        kv_want = oracle.wkv(bits(a)[rows], bits(w))
+        dot_want = oracle.gate_dot(bits(x)[rows], _kv_bf16(kv_want), bits(q), bits(k), 1e-20)
+        assert_close(dots[e].cpu().numpy()[rows], dot_want, what=f"layer {e} dot vs oracle")
+
+
+def test_wkv_gate_layers_workspace_and_layer_count_checked(gpu_device):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(3)
+    T, K, hc, dim = 40, 64, 1, 256
+    ins = [_inputs(rng, T, K, hc, dim, gpu_device) for _ in range(2)]
+    cols = [[i[j] for i in ins] for j in range(5)]
+    small = torch.empty(2 * g.engram_wkv_gate_workspace_bytes(T, hc, dim) - 16, dtype=torch.uint8, device=gpu_device)
+    with pytest.raises(g.EngramError, match="workspace"):
+        g.engram_wkv_gate_layers(*cols, 1e-20, workspace=small)
+    with pytest.raises(g.EngramError, match="layers=9"):
+        g.engram_wkv_gate_layers(*[[c[0]] * 9 for c in cols], 1e-20)
