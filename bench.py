@@ -315,6 +315,25 @@ def main(argv=None):
         hg_bytes = algo["hash_bytes"] + E * (algo["gather_bytes"] - 8 * cfg.n_hash_cols)
         hg["GB/s"] = round(T_launch * hg_bytes / (hg["avg_us"] * 1e3), 1)
         hg["frac_hbm"] = round(hg["GB/s"] / PEAK_HBM_GBS, 4)
+    if not cfg.decode_steps:
+        # The gathers also back to back (the same launch 20 times between two events): inside the step a
+        # gather follows the previous step's projection, whose stores are still draining to HBM.
+        ids = fwd._buf("ids", (cfg.batch, cfg.seqlen, E, cfg.n_hash_cols), torch.int64, wl.input_ids.device)
+        for name, packed in (("gather_dequant_packed", True), ("gather_dequant", False)):
+            for _ in range(3):
+                fwd.gather(0, ids, packed=packed)
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(20):
+                fwd.gather(0, ids, packed=packed)
+            t1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * t0.elapsed_time(t1) / 20
+            g = kern[name]
+            g["back_to_back_us"] = round(us, 2)
+            g["back_to_back_GB/s"] = round(T_launch * algo["gather_bytes"] / (us * 1e3), 1)
+            g["back_to_back_frac_hbm"] = round(g["back_to_back_GB/s"] / PEAK_HBM_GBS, 4)
     for name, layers in (("wkv", 1), ("wkv_gate", 1), ("wkv_gate_layers", E)):
         if name not in kern:
             continue
