@@ -129,7 +129,7 @@ def test_gate_residual_matches_gate_output_bit_for_bit(gpu_device, T, hc, dim, m
 # alone takes 200 tiles of 128), a ragged token count, three layers whose 128-token tiles still fit the CUs
 # together, and layers of several tiles per CU.
 LAYER_SHAPES = [(2, 256, 1536, 4, 5120), (2, 130, 1536, 4, 5120), (3, 200, 256, 2, 512), (2, 700, 192, 3, 768),
-                (4, 64, 64, 1, 256)]
+                (4, 64, 64, 1, 256), (8, 40, 256, 1, 256)]
 
 
 @pytest.mark.parametrize("E,T,K,hc,dim", LAYER_SHAPES)
@@ -170,3 +170,26 @@ def test_wkv_gate_layers_workspace_and_layer_count_checked(gpu_device):
         g.engram_wkv_gate_layers(*cols, 1e-20, workspace=small)
     with pytest.raises(g.EngramError, match="layers=9"):
         g.engram_wkv_gate_layers(*[[c[0]] * 9 for c in cols], 1e-20)
+
+
+def test_wkv_gate_layers_strided_values(gpu_device):
+    """Row-strided value views (one stride for all layers): only each view's dim columns are written."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(17)
+    E, T, K, hc, dim = 3, 150, 128, 2, 256
+    ins = [_inputs(rng, T, K, hc, dim, gpu_device) for _ in range(E)]
+    wide = torch.full((E, T, dim + 48), 3.0, dtype=torch.bfloat16, device=gpu_device)
+    views = [wide[e, :, 16:16 + dim] for e in range(E)]
+    values, dots = g.engram_wkv_gate_layers([i[0] for i in ins], [i[1] for i in ins], [i[2] for i in ins],
+                                            [i[3] for i in ins], [i[4] for i in ins], 1e-20, value=views)
+    torch.cuda.synchronize()
+    three = bits(torch.tensor([3.0], dtype=torch.bfloat16))[0]
+    for e in range(E):
+        v1, d1 = g.engram_wkv_gate(*ins[e], 1e-20)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(wide[e, :, 16:16 + dim]), bits(v1), err_msg=f"layer {e}")
+        assert (bits(wide[e, :, :16]) == three).all() and (bits(wide[e, :, 16 + dim:]) == three).all()
+        assert_close(dots[e].cpu().numpy(), d1.cpu().numpy(), rtol=1e-3, atol=1e-4, what=f"layer {e} dot")
