@@ -353,6 +353,9 @@ extern "C" int engram_hash_gather_packed(const int64_t* input_ids, int64_t B, in
     if (blk < 16 || blk % 16 != 0 || D % blk != 0)
         return fail(ENGRAM_EINVAL, "%s: blk=%d must be a multiple of 16 dividing D=%d", name, blk, D);
     if (E < 1 || E > kMaxE) return fail(ENGRAM_EINVAL, "%s: E=%d outside [1, %d]", name, E, kMaxE);
+    if (N >= 2 && H >= 1 && static_cast<int64_t>(E) * (N - 1) * H > kMaxTileIds)
+        return fail(ENGRAM_EINVAL, "%s: E*(N-1)*H=%lld ids per token, at most %d (a token's ids stay in LDS)", name,
+                    static_cast<long long>(E) * (N - 1) * H, kMaxTileIds);
     if (B >= 0 && L >= 0 && B * L == 0)  // nothing to gather: the hash's own checks decide
         return hash_entry(name, input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B, cache_L,
                           multipliers, primes, offsets, E, N, H, pad_id, dead, hash_ids, 0, nullptr, stream);

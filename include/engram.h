@@ -183,6 +183,7 @@ int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, int64_t id_
  *           that divides D
  * out_bf16  host array of E device pointers: layer e's rows, uint16
  *           [B*L, C, D] bf16 bits, out; 16-byte aligned
+ * Limits: engram_hash's, and E*C <= 4096 ids per token.
  * The host arrays are read during the call only.
  */
 int engram_hash_gather_packed(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,

@@ -111,6 +111,7 @@ def _hash_gather(**kw):
     (dict(tables=[FAKE.value, 0x100040]), 1, "layer 1: misaligned"),  # a 128-byte record needs 128
     (dict(outs=[FAKE.value, 0x100008]), 1, "layer 1: misaligned"),
     (dict(input_ids=None), 1, "null"), (dict(ids=ctypes.c_void_p(0x100004)), 1, "aligned"),
+    (dict(E=8, N=8, H=100, tables=[FAKE.value] * 8, rows=[100] * 8, outs=[FAKE.value] * 8), 1, "at most 4096"),
 ])
 def test_hash_gather_validation(kw, status, msg):
     assert _hash_gather(**kw) == status
