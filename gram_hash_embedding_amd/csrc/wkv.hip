@@ -44,6 +44,11 @@
 //   mostly from beyond L2 there, get two slab periods instead of one) and
 //   puts the stream rows and the epilogue exchange into the stages its last
 //   slabs free.
+// - Several engram layers in one launch (engram_wkv_gate_layers): their M tiles
+//   are stacked and numbered layer by layer, each tile reading its layer's
+//   operand pointers with a wave-uniform index into the kernel arguments; the
+//   tile height is chosen for all layers together, so a decode call of two
+//   layers runs 2 x 100 tiles of 256 tokens in one pass.
 // - K not a multiple of 64: a register-staged four-wave variant with a
 //   zero-filled K tail.
 #include <type_traits>

@@ -19,12 +19,24 @@
  *   engram_gate_residual   -- the gate, the token mask and the residual add
  *                             from a given dot (after engram_wkv_gate)
  *
+ * and forms of the same steps that save memory traffic or launches:
+ *
+ *   engram_pack_table, engram_gather_dequant_packed
+ *                          -- the table as one record per row (its fp8 bytes
+ *                             and its scales), gathered with one line per row
+ *   engram_hash_gather_packed
+ *                          -- engram_hash and every layer's packed gather in
+ *                             one launch
+ *   engram_wkv_gate_layers -- engram_wkv_gate for every layer in one launch
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every array argument is a DEVICE pointer (memory the caller allocated on
  *   the current HIP device), row-major and contiguous unless a stride is
- *   given.  The caller owns all memory; the library allocates nothing and
- *   keeps no pointer after a call returns.
+ *   given -- except the per-layer lists of engram_hash_gather_packed and
+ *   engram_wkv_gate_layers, which are HOST arrays of device pointers (or of
+ *   sizes), read during the call only.  The caller owns all memory; the
+ *   library allocates nothing and keeps no pointer after a call returns.
  * - bf16 values are passed as their 16-bit patterns (uint16_t).
  * - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *   kernels on it and never synchronise; results are ready when the stream
