@@ -258,6 +258,10 @@ __device__ inline void interleave8() {
 struct SlabCursor {
     int pid;  // tile being loaded
     int kt;   // slab inside that tile
+    // that tile's layer, first token and first column, and the next tile's (computed once per tile, off the
+    // slab loop, so the per-slab issue does no index arithmetic)
+    int e, n0, nxt_e, nxt_n0;
+    int64_t m0, nxt_m0;
 };
 
 // Eight waves, two per SIMD: wave w runs on SIMD w % 4, so each SIMD hosts one loader wave (0-3) and one
@@ -329,9 +333,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
     // block as the MFMAs they are interleaved with.  An empty resource zero-fills a free stage.
     auto issue_slab = [&](const SlabCursor& c, int stage, bool live) {
-        int e, n0;
-        int64_t m0;
-        tile_of(live ? c.pid : static_cast<int>(blockIdx.x), e, m0, n0);
+        const int e = c.e, n0 = c.n0;
+        const int64_t m0 = c.m0;
         const LayerPtrs& L = p.lay[e];
         const int rows_a = live ? static_cast<int>(min<int64_t>(kBM, p.M - m0)) : 0;
         const int rows_w = live ? min(BN, p.N - n0) : 0;
@@ -358,6 +361,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         const bool wrap = c.kt + 1 == KT;
         c.kt = wrap ? 0 : c.kt + 1;
         c.pid += wrap ? G : 0;
+        c.e = wrap ? c.nxt_e : c.e;
+        c.n0 = wrap ? c.nxt_n0 : c.n0;
+        c.m0 = wrap ? c.nxt_m0 : c.m0;
+    };
+    // the tile after tile pid, for the cursor's next wrap (past the last one: any valid tile; its loads are
+    // issued against an empty resource)
+    auto prepare_next = [&](SlabCursor& c, int pid) {
+        const int np = pid + G < p.tiles_m * p.tiles_n ? pid + G : static_cast<int>(blockIdx.x);
+        tile_of(np, c.nxt_e, c.nxt_m0, c.nxt_n0);
     };
 
     // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
@@ -591,7 +603,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     auto run = [&](auto loader_tag) {
         constexpr bool kLoader = decltype(loader_tag)::value;
         int pid = blockIdx.x;
-        SlabCursor ld{pid, 0};
+        SlabCursor ld{};
+        ld.pid = pid;
+        tile_of(pid, ld.e, ld.m0, ld.n0);
+        prepare_next(ld, pid);
         int issued = 0;
         if (kLoader) {
             if constexpr (kOneTile) {
@@ -600,6 +615,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 for (int s0 = 0; s0 < kStages; ++s0) {
                     issue_slab(ld, s0, true);
                     advance(ld);
+                    prepare_next(ld, ld.pid);
                     ++issued;
                 }
                 __builtin_amdgcn_s_waitcnt(wait_vmcnt((kStages - 1) * kSlabLoads));
@@ -607,9 +623,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 // prologue: two slabs in flight
                 issue_slab(ld, 0, true);
                 advance(ld);
+                prepare_next(ld, ld.pid);
                 ++issued;
                 issue_slab(ld, 1, issued < total_slabs_mine);
                 advance(ld);
+                prepare_next(ld, ld.pid);
                 ++issued;
                 __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
             }
@@ -745,6 +763,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
             int64_t m0;
             int n0;
             tile_of(pid, cur, m0, n0);
+            // the loader wraps to its next tile exactly once during this tile's slabs: have that tile ready
+            if (kLoader) prepare_next(ld, ld.pid);
             const bool key_tile = kGate && n0 < p.out_col0;
             if (key_tile) {
                 // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
