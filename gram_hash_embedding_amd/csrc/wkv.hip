@@ -258,10 +258,14 @@ __device__ inline void interleave8() {
 struct SlabCursor {
     int pid;  // tile being loaded
     int kt;   // slab inside that tile
-    // that tile's layer, first token and first column, and the next tile's (computed once per tile, off the
-    // slab loop, so the per-slab issue does no index arithmetic)
-    int e, n0, nxt_e, nxt_n0;
-    int64_t m0, nxt_m0;
+    // that tile's A and W panels (first row, bytes of valid rows), and the next tile's: computed once per
+    // tile, off the slab loop, so a slab's issue does no index arithmetic and no argument load
+    const uint16_t* a;
+    const uint16_t* w;
+    int a_bytes, w_bytes;
+    const uint16_t* nxt_a;
+    const uint16_t* nxt_w;
+    int nxt_a_bytes, nxt_w_bytes;
 };
 
 // Eight waves, two per SIMD: wave w runs on SIMD w % 4, so each SIMD hosts one loader wave (0-3) and one
@@ -333,15 +337,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     // resource: they touch no memory, and keeping them unconditional lets them sit in the same basic
     // block as the MFMAs they are interleaved with.  An empty resource zero-fills a free stage.
     auto issue_slab = [&](const SlabCursor& c, int stage, bool live) {
-        const int e = c.e, n0 = c.n0;
-        const int64_t m0 = c.m0;
-        const LayerPtrs& L = p.lay[e];
-        const int rows_a = live ? static_cast<int>(min<int64_t>(kBM, p.M - m0)) : 0;
-        const int rows_w = live ? min(BN, p.N - n0) : 0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(L.a + m0 * p.K), 0, rows_a * row_bytes, kBufferWord3);
+            const_cast<uint16_t*>(c.a), 0, live ? c.a_bytes : 0, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(L.w + static_cast<int64_t>(n0) * p.K), 0, rows_w * row_bytes, kBufferWord3);
+            const_cast<uint16_t*>(c.w), 0, live ? c.w_bytes : 0, kBufferWord3);
         const uint32_t k0b = static_cast<uint32_t>(c.kt * BK * 2);
         uint8_t* sa = lds + stage * kStageBytes + wave * 16 * NI * 128;
         uint8_t* sw = lds + stage * kStageBytes + kABytes + wave * 64 * 128;
@@ -361,15 +360,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         const bool wrap = c.kt + 1 == KT;
         c.kt = wrap ? 0 : c.kt + 1;
         c.pid += wrap ? G : 0;
-        c.e = wrap ? c.nxt_e : c.e;
-        c.n0 = wrap ? c.nxt_n0 : c.n0;
-        c.m0 = wrap ? c.nxt_m0 : c.m0;
+        c.a = wrap ? c.nxt_a : c.a;
+        c.w = wrap ? c.nxt_w : c.w;
+        c.a_bytes = wrap ? c.nxt_a_bytes : c.a_bytes;
+        c.w_bytes = wrap ? c.nxt_w_bytes : c.w_bytes;
+    };
+    // the panels of tile pid (rows past M or N left out of the resource: they read as zero)
+    auto panels = [&](int pid, const uint16_t*& a, const uint16_t*& w, int& a_bytes, int& w_bytes) {
+        int e, n0;
+        int64_t m0;
+        tile_of(pid, e, m0, n0);
+        a = p.lay[e].a + m0 * p.K;
+        w = p.lay[e].w + static_cast<int64_t>(n0) * p.K;
+        a_bytes = static_cast<int>(min<int64_t>(kBM, p.M - m0)) * row_bytes;
+        w_bytes = min(BN, p.N - n0) * row_bytes;
     };
     // the tile after tile pid, for the cursor's next wrap (past the last one: any valid tile; its loads are
     // issued against an empty resource)
     auto prepare_next = [&](SlabCursor& c, int pid) {
         const int np = pid + G < p.tiles_m * p.tiles_n ? pid + G : static_cast<int>(blockIdx.x);
-        tile_of(np, c.nxt_e, c.nxt_m0, c.nxt_n0);
+        panels(np, c.nxt_a, c.nxt_w, c.nxt_a_bytes, c.nxt_w_bytes);
     };
 
     // ---- fragments: lane reads row (lane % 32) of a 32-row block, pieces 2kk + lane/32 ----
@@ -605,7 +615,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
         int pid = blockIdx.x;
         SlabCursor ld{};
         ld.pid = pid;
-        tile_of(pid, ld.e, ld.m0, ld.n0);
+        panels(pid, ld.a, ld.w, ld.a_bytes, ld.w_bytes);
         prepare_next(ld, pid);
         int issued = 0;
         if (kLoader) {
