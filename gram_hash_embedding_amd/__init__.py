@@ -203,6 +203,23 @@ def _gather_ids(hash_ids, n_cols, layer):
     return T, C, stride, ctypes.c_void_p(hash_ids.data_ptr() + 8 * base)
 
 
+def _raw_outputs(out_fp8, out_scale, T, C, D, block_size):
+    """Pointers of the optional raw-gather outputs, after checking that each holds exactly what the kernel
+    writes (T*C*D bytes; T*C*(D/blk) floats)."""
+    import torch
+
+    p8 = ps = None
+    if out_fp8 is not None:
+        if out_fp8.numel() != T * C * D:
+            raise ValueError(f"out_fp8 must hold T*C*D = {T * C * D} bytes, has {out_fp8.numel()}")
+        p8 = _dev(out_fp8, "out_fp8", torch.uint8)
+    if out_scale is not None:
+        if block_size <= 0 or out_scale.numel() != T * C * (D // block_size):
+            raise ValueError(f"out_scale must hold T*C*(D/block_size) floats, has {out_scale.numel()}")
+        ps = _dev(out_scale, "out_scale", torch.float32)
+    return p8, ps
+
+
 def engram_pack_table(weight, scale, block_size=32, out=None, stream=None):
     """uint8 [R, 2*D]: record r = weight[r] (D fp8 bytes), then scale[r] (fp32), then zeros."""
     import torch
@@ -233,8 +250,7 @@ def engram_gather_dequant_packed(hash_ids, table, block_size=32, row_start=0, n_
         out = torch.empty((T, C, D), dtype=torch.bfloat16, device=hash_ids.device)
     if out.numel() != T * C * D:
         raise ValueError("out has the wrong size")
-    p8 = None if out_fp8 is None else _dev(out_fp8, "out_fp8", torch.uint8)
-    ps = None if out_scale is None else _dev(out_scale, "out_scale", torch.float32)
+    p8, ps = _raw_outputs(out_fp8, out_scale, T, C, D, int(block_size))
     _check(lib().engram_gather_dequant_packed(
         ids_ptr, T, stride, C, _dev(table, "table", torch.uint8, 2), R, int(row_start), D, int(block_size),
         _dev(out, "out", torch.bfloat16), p8, ps, _stream(stream)))
@@ -261,8 +277,7 @@ def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n
         raise ValueError("out has the wrong size")
     if tuple(scale.shape) != (R, D // block_size):
         raise ValueError("scale must be [R, D/block_size]")
-    p8 = None if out_fp8 is None else _dev(out_fp8, "out_fp8", torch.uint8)
-    ps = None if out_scale is None else _dev(out_scale, "out_scale", torch.float32)
+    p8, ps = _raw_outputs(out_fp8, out_scale, T, C, D, int(block_size))
     _check(lib().engram_gather_dequant(
         ids_ptr, T, stride, C, _dev(weight, "weight", torch.uint8, 2), _dev(scale, "scale", torch.float32, 2),
         R, int(row_start), D, int(block_size), _dev(out, "out", torch.bfloat16), p8, ps, _stream(stream)))
@@ -299,6 +314,8 @@ def engram_gate_dot(x, kv, q_weight, k_weight, eps, out=None, stream=None):
         raise ValueError("q_weight and k_weight must be [hc, dim]")
     if out is None:
         out = torch.empty((T, hc), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (T, hc):
+        raise ValueError("out must be [T, hc]")
     _check(lib().engram_gate_dot(
         _dev(x3, "x", torch.bfloat16, 3), _dev(kv, "kv", torch.bfloat16, 2), kv.shape[1],
         _dev(q_weight, "q_weight", torch.bfloat16, 2), _dev(k_weight, "k_weight", torch.bfloat16, 2),

@@ -125,6 +125,22 @@ def wkv(a_bits, w_bits):
     return out
 
 
+def wkv_matmul(a_bits, w_bits, chunk: int = 4096):
+    """The same projection as `wkv` (stack-hashes page: Engram's `wkv` Linear, y = a w^T, no bias), with
+    numpy's float64 matrix product as the contraction step: bf16 operands decoded exactly to float64, the
+    sum over K taken by the library routine.  For parity checks over whole workloads, where the plain C
+    loop would take minutes; both are pinned against closed forms and against each other."""
+    a = bf16_bits_to_float(_c(a_bits, np.uint16)).astype(np.float64)
+    w = bf16_bits_to_float(_c(w_bits, np.uint16)).astype(np.float64)
+    if a.ndim != 2 or w.ndim != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError("wkv_matmul: a must be [T, K] and w [Nout, K]")
+    wt = np.ascontiguousarray(w.T)
+    out = np.empty((a.shape[0], w.shape[0]), dtype=np.float64)
+    for t0 in range(0, a.shape[0], chunk):
+        np.matmul(a[t0:t0 + chunk], wt, out=out[t0:t0 + chunk])
+    return out
+
+
 def gate_dot(x_bits, kv_bits, q_bits, k_bits, eps):
     """x [T, hc, dim]; kv [T, >= hc*dim] (key = first hc*dim columns); q, k [hc, dim];
     all bf16 bits -> float64 dot [T, hc]."""

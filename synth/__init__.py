@@ -309,9 +309,9 @@ def table_rows(seed: int, rows: np.ndarray, head_dim: int, block_size: int):
     n = rows.astype(np.uint64)[:, None] * np.uint64(W) + np.arange(W, dtype=np.uint64)[None, :]
     u = splitmix64(seed, n)
     lut = normal_fp8_lut()
-    wb = u[:, :nb]
-    idx = np.stack([(wb >> np.uint64(16 * i)) & np.uint64(0xFFFF) for i in range(4)], axis=-1)
-    weight = lut[idx.astype(np.int64)].reshape(rows.size, head_dim)
+    # the four 16-bit fields of word w, low field first, are its little-endian uint16 pieces 4w .. 4w+3
+    idx = np.ascontiguousarray(u[:, :nb]).astype("<u8", copy=False).view("<u2")
+    weight = lut[idx].reshape(rows.size, head_dim)
     us = u[:, nb:]
     mant = (us & np.uint64(0x7FFFFF)).astype(np.uint32)
     ex = ((us >> np.uint64(32)) % np.uint64(6)).astype(np.uint32)

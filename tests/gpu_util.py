@@ -37,20 +37,24 @@ def bf16_tensor(bits_arr, device):
     return torch.from_numpy(np.ascontiguousarray(bits_arr, dtype=np.uint16).view(np.int16)).to(device).view(torch.bfloat16)
 
 
-def sample_tokens(T: int, n: int, seed: int, L: int = None, mask=None, extra=()) -> np.ndarray:
-    """Sorted token indices: the first and last tokens, tile edges of 256, the first three
-    positions of each sequence and the three after every masked span, plus random others."""
+def sample_tokens(T: int, n: int, seed: int, L: int = None, mask=None, extra=(), tile: int = 256) -> np.ndarray:
+    """Sorted token indices: the first and last tokens; the first and last token and one random token of
+    every `tile`-token block (every M tile of the projection, the ragged last one included); the first three
+    positions of every sequence and the three after every masked span; then random others up to n."""
     rng = np.random.default_rng(seed)
-    pick = {0, T - 1, min(255, T - 1), min(256, T - 1), max(0, T - 256), max(0, T - 257)}
+    pick = {0, T - 1}
     pick.update(int(e) for e in extra if 0 <= e < T)
+    for t0 in range(0, T, tile):
+        t1 = min(T, t0 + tile)
+        pick.update((t0, t1 - 1, int(rng.integers(t0, t1))))
     if L is not None:
         B = T // L
-        for b in range(min(B, 8)):
+        for b in range(B):
             pick.update(b * L + i for i in range(min(3, L)))
         if mask is not None:
             m = np.asarray(mask).reshape(B, L)
             ends = np.argwhere((m[:, :-1] == 0) & (m[:, 1:] == 1))
-            for b, l in ends[:32]:
+            for b, l in ends:
                 pick.update(int(b * L + l + 1 + i) for i in range(3) if l + 1 + i < L)
     while len(pick) < min(n, T):
         pick.add(int(rng.integers(0, T)))

@@ -51,6 +51,32 @@ def test_wkv_identity_and_one_hot():
     np.testing.assert_array_equal(got[2], -wf[:, K - 1])
 
 
+def test_wkv_matmul_closed_forms_and_the_c_loop():
+    """The library-contraction form of the projection (used for whole-workload parity) on the same closed
+    forms as the C loop, and equal to it on random operands up to float64 summation order."""
+    rng = np.random.default_rng(5)
+    K = 96
+    a = _bf16_bits(rng.normal(size=(11, K)))
+    eye = np.zeros((K + 8, K), dtype=np.float32)
+    eye[:K] = np.eye(K)
+    got = oracle.wkv_matmul(a, _bf16_bits(eye), chunk=4)
+    np.testing.assert_array_equal(got[:, :K], _bits_to_f64(a))
+    assert (got[:, K:] == 0).all()
+    w = _bf16_bits(rng.normal(size=(20, K)))
+    onehot = np.zeros((2, K), dtype=np.float32)
+    onehot[0, 7], onehot[1, K - 1] = -4.0, 0.5
+    got = oracle.wkv_matmul(_bf16_bits(onehot), w)
+    np.testing.assert_array_equal(got[0], -4 * _bits_to_f64(w)[:, 7])
+    np.testing.assert_array_equal(got[1], 0.5 * _bits_to_f64(w)[:, K - 1])
+    # a row of ones sums each W row (integers: exact in any order)
+    wi = _bf16_bits(rng.integers(-100, 100, size=(13, K)).astype(np.float32))
+    got = oracle.wkv_matmul(_bf16_bits(np.ones((1, K), np.float32)), wi)
+    np.testing.assert_array_equal(got[0], _bits_to_f64(wi).sum(axis=1))
+    a = _bf16_bits(rng.normal(size=(70, 256)))
+    w = _bf16_bits(rng.normal(scale=0.02, size=(300, 256)))
+    np.testing.assert_allclose(oracle.wkv_matmul(a, w, chunk=16), oracle.wkv(a, w), rtol=1e-12, atol=1e-14)
+
+
 def _gate(x, key, q=None, k=None, eps=1e-20):
     T, hc, dim = x.shape
     if q is None:
