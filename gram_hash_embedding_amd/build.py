@@ -16,6 +16,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libengram.so")
+# the measured-ceiling microbenchmarks (include/engram_probe.h), a library of their own
+PROBE_SRC = os.path.join(HERE, "probe")
+PROBE_LIB_PATH = os.path.join(HERE, "libengram_probe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ROOT = os.path.dirname(HERE)
 
@@ -63,18 +66,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libengram.so.  Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, lib_path: str, verbose: bool) -> None:
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip into libengram.so and probe/*.hip into libengram_probe.so.  Always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    probes = sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC) if f.endswith(".hip"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probes))
+    _link(objs[:len(srcs)], LIB_PATH, verbose)
+    _link(objs[len(srcs):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

@@ -21,6 +21,25 @@ def assert_close(got, want, rtol=RTOL, atol=ATOL, what=""):
                              f"want {want[i]!r}")
 
 
+def bf16_ulp(v) -> np.ndarray:
+    """One unit in the last place of bf16 at each |v| (the spacing of bf16 values around it)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), 2.0 ** -133)
+
+
+def assert_output_close(got_bits, out_want, value_want, x_bits=None, mask=None, what=""):
+    """The output stream h + gate * value against the oracle's pipeline.  The device's bf16 value may sit one
+    bf16 ulp from the oracle's (its fp32 sum and the oracle's float64 sum can round to neighbouring bf16
+    values), and h + gate * value can cancel, so besides the gate bar (1e-3 + 2e-2 |out|) each element may
+    differ by |gate| <= 1 times one ulp of its value element."""
+    import oracle
+
+    got = oracle.bf16_bits_to_float(got_bits).astype(np.float64)
+    v = np.asarray(value_want, dtype=np.float64)[:, None, :]
+    assert_close(got, out_want, atol=ATOL + bf16_ulp(v), what=what)
+
+
 def bits(t) -> np.ndarray:
     """uint16 host copy of a bf16 (or uint16/int16) tensor."""
     import torch

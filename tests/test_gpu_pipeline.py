@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import assert_close, bits, compact_rows, sample_tokens
+from tests.gpu_util import assert_close, assert_output_close, bits, compact_rows, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,17 @@ def test_forward_pipeline(gpu_device, cfg_index, n_sample):
                          what=f"dot (output, fused={fused}) layer {e}")
             _, out_want = oracle.gate_output(x_bits, kv_o, dot_o, m)
             out_got = bits(outs[e].view(T, cfg.hc_mult, cfg.dim)[sidx])
-            assert_close(oracle.bf16_bits_to_float(out_got), out_want, what=f"out (fused={fused}) layer {e}")
+            assert_output_close(out_got, out_want, oracle.bf16_bits_to_float(kv_o[:, hcd:]), what=f"out (fused={fused}) layer {e}")
+            # the gate, mask and residual alone: the oracle fed the device's own value and dot (only the
+            # output's fp32 sum and bf16 rounding differ)
+            v_dev = bits(wl.fwd._bufs[("value", e)].view(T, -1)[sidx]) if fused else \
+                bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])[:, hcd:]
+            kv_dev = np.zeros((len(sample), hcd + cfg.dim), np.uint16)
+            kv_dev[:, hcd:] = v_dev[:, :cfg.dim]
+            d_dev = wl.fwd._bufs[("dot", e)].view(T, -1)[sidx].cpu().numpy().astype(np.float64)
+            _, out_unit = oracle.gate_output(x_bits, kv_dev, d_dev, m)
+            assert_close(oracle.bf16_bits_to_float(out_got), out_unit, rtol=2.0 ** -8, atol=1e-5,
+                         what=f"out from the device's value and dot (fused={fused}) layer {e}")
             if m is not None:
                 np.testing.assert_array_equal(out_got[m == 0], x_bits[m == 0],
                                               err_msg=f"masked tokens (fused={fused}), layer {e}")
@@ -155,7 +165,8 @@ def test_decode_pipeline(gpu_device):
             assert_close(dot_got, dot_want, what=f"dot, step {s}, layer {e}, fused={fused}")
             _, out_want = oracle.gate_output(x_bits, kv_want, dot_want, None)
             out_got = bits(outs[e].view(B, hc, dim)[sidx])
-            assert_close(oracle.bf16_bits_to_float(out_got), out_want, what=f"out, step {s}, layer {e}, fused={fused}")
+            assert_output_close(out_got, out_want, oracle.bf16_bits_to_float(kv_want[:, hc * dim:]),
+                                what=f"out, step {s}, layer {e}, fused={fused}")
 
 
 def test_decode_step_graph_replays_match_eager(gpu_device):
