@@ -17,6 +17,7 @@ an exception is raised.
     engram_gate_output     -- the dot, the sigmoid gate, the token mask and the residual add
     engram_wkv_gate        -- wkv + gate dot fused: value columns and dot out, keys never stored
     engram_wkv_gate_layers -- engram_wkv_gate for several engram layers in one launch
+    engram_wkv_gate_layers_noalloc -- the same with the library's own device scratch (allocates nothing)
     engram_gate_residual   -- gate, token mask and residual add from a given dot
 """
 from __future__ import annotations
@@ -59,11 +60,12 @@ def lib() -> ctypes.CDLL:
         L.engram_wkv_gate.argtypes = [p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_layers.argtypes = [i32, p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
+        L.engram_wkv_gate_layers_noalloc.argtypes = [i32, p, p, p, p, p, f32, p, i64, p, i64, i32, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
         for f in (L.engram_hash, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
-                  L.engram_wkv_gate_layers,
+                  L.engram_wkv_gate_layers, L.engram_wkv_gate_layers_noalloc,
                   L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
@@ -402,11 +404,8 @@ def engram_wkv_gate(a, w, x, q_weight, k_weight, eps, value=None, dot=None, work
     return value, dot
 
 
-def engram_wkv_gate_layers(a, w, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None, stream=None):
-    """engram_wkv_gate for E layers in one launch: a, w, x, q_weight, k_weight are lists of E tensors shaped as
-    engram_wkv_gate takes them (one T, K, hc and dim for all); returns (values, dots), lists of E tensors.
-    `value` (list) entries may be [T, ld >= dim] row-strided views, all with one row stride; `workspace` a uint8
-    device tensor of E * engram_wkv_gate_workspace_bytes bytes (allocated here if not given)."""
+def _layers_args(a, w, x, q_weight, k_weight, value, dot):
+    """Checked shapes and host pointer arrays of the per-layer operands of engram_wkv_gate_layers(_noalloc)."""
     import torch
 
     E = len(a)
@@ -439,17 +438,44 @@ def engram_wkv_gate_layers(a, w, x, q_weight, k_weight, eps, value=None, dot=Non
     for d in dot:
         if tuple(d.shape) != (T, hc):
             raise ValueError("dot must be [T, hc]")
+    arr = lambda ts, name, dt, nd: (ctypes.c_void_p * E)(*[_dev(t, f"{name}[{i}]", dt, nd).value
+                                                          for i, t in enumerate(ts)])
+    ptrs = (arr(a, "a", torch.bfloat16, 2), arr(w, "w", torch.bfloat16, 2), arr(x3, "x", torch.bfloat16, 3),
+            arr(q_weight, "q_weight", torch.bfloat16, 2), arr(k_weight, "k_weight", torch.bfloat16, 2))
+    vals = (ctypes.c_void_p * E)(*[v.data_ptr() for v in value])
+    return E, T, K, hc, dim, value, dot, ptrs, vals, ld, arr(dot, "dot", torch.float32, 2)
+
+
+def engram_wkv_gate_layers(a, w, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None, stream=None):
+    """engram_wkv_gate for E layers in one launch: a, w, x, q_weight, k_weight are lists of E tensors shaped as
+    engram_wkv_gate takes them (one T, K, hc and dim for all); returns (values, dots), lists of E tensors.
+    `value` (list) entries may be [T, ld >= dim] row-strided views, all with one row stride; `workspace` a uint8
+    device tensor of E * engram_wkv_gate_workspace_bytes bytes (allocated here if not given)."""
+    import torch
+
+    E, T, K, hc, dim, value, dot, ptrs, vals, ld, dots = _layers_args(a, w, x, q_weight, k_weight, value, dot)
     need = E * engram_wkv_gate_workspace_bytes(T, hc, dim)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a[0].device)
-    arr = lambda ts, name, dt, nd: (ctypes.c_void_p * E)(*[_dev(t, f"{name}[{i}]", dt, nd).value
-                                                          for i, t in enumerate(ts)])
-    vals = (ctypes.c_void_p * E)(*[v.data_ptr() for v in value])
     _check(lib().engram_wkv_gate_layers(
-        E, arr(a, "a", torch.bfloat16, 2), arr(w, "w", torch.bfloat16, 2), arr(x3, "x", torch.bfloat16, 3),
-        arr(q_weight, "q_weight", torch.bfloat16, 2), arr(k_weight, "k_weight", torch.bfloat16, 2), float(eps),
-        vals, ld, arr(dot, "dot", torch.float32, 2), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        E, *ptrs, float(eps), vals, ld, dots, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         T, K, hc, dim, _stream(stream)))
+    return value, dot
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES of include/engram.h
+
+
+def engram_wkv_gate_layers_noalloc(a, w, x, q_weight, k_weight, eps, value, dot, stream=None):
+    """engram_wkv_gate_layers with the partial sums in the library's own device scratch (no workspace, nothing
+    allocated by the call): for callers that cannot allocate.  `value` and `dot` (lists of E tensors) must be
+    given.  At most NOALLOC_SCRATCH_BYTES of partial sums (E * engram_wkv_gate_workspace_bytes); calls that
+    overlap in time on one GPU share that scratch and race."""
+    if value is None or dot is None:
+        raise ValueError("engram_wkv_gate_layers_noalloc writes into caller-provided value and dot tensors")
+    E, T, K, hc, dim, value, dot, ptrs, vals, ld, dots = _layers_args(a, w, x, q_weight, k_weight, value, dot)
+    _check(lib().engram_wkv_gate_layers_noalloc(E, *ptrs, float(eps), vals, ld, dots, T, K, hc, dim,
+                                                _stream(stream)))
     return value, dot
 
 
@@ -485,6 +511,7 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
-           "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_layers_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

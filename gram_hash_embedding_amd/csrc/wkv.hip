@@ -51,6 +51,8 @@
 //   layers runs 2 x 100 tiles of 256 tokens in one pass.
 // - K not a multiple of 64: a register-staged four-wave variant with a
 //   zero-filled K tail.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1064,14 +1066,48 @@ extern "C" int64_t engram_wkv_gate_workspace_bytes(int64_t T, int32_t hc, int32_
     return static_cast<int64_t>(hc) * (dim / 128) * 3 * T * static_cast<int64_t>(sizeof(float));
 }
 
+// ---- the allocation-free form: the partial sums live in a file-scope device array ----
+// Each GPU the library runs on holds its own copy of `scratch` until the process ends.  In host code the
+// array's name is only a stand-in for the symbol: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept below.
 namespace {
+
+static __device__ __align__(256) float scratch[ENGRAM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// the device address of `scratch` on the current GPU (looked up on the first call made on that GPU)
+int scratch_address(void** out, const char* what) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ENGRAM_EHIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ENGRAM_EINVAL, "%s: device %d outside [0, %d)", what, dev, kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(ENGRAM_EHIP, "%s: hipGetSymbolAddress(scratch): %s", what, hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ENGRAM_OK;
+}
 
 // engram_wkv_gate over `layers` layers in one launch of the main kernel and one of the finalize; arrays of
 // `layers` entries (host memory).  The workspace holds the layers' partial sums one after another.
+// `static_scratch`: the workspace is the library's `scratch` array (workspace and workspace_bytes ignored),
+// whose address is looked up only once every argument has been checked.
 int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const uint16_t* const* w,
                    const uint16_t* const* x, const uint16_t* const* q_weight, const uint16_t* const* k_weight,
                    float eps, uint16_t* const* value, int64_t ld_value, float* const* dot, void* workspace,
-                   int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc, int32_t dim, void* stream) {
+                   int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc, int32_t dim, void* stream,
+                   bool static_scratch = false) {
     if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", what);
     if (K < BK || K % BK != 0) return fail(ENGRAM_EINVAL, "%s: K=%d must be a positive multiple of %d", what, K, BK);
     if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "%s: hc=%d outside [1, 64]", what, hc);
@@ -1081,12 +1117,18 @@ int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const
         return fail(ENGRAM_EINVAL, "%s: ld_value=%lld must be >= dim and a multiple of 8", what, (long long)ld_value);
     const int64_t per_layer = engram_wkv_gate_workspace_bytes(T, hc, dim);
     const int64_t need = per_layer * layers;
-    if (workspace_bytes < need)
+    if (static_scratch) {
+        if (need > ENGRAM_NOALLOC_SCRATCH_BYTES)
+            return fail(ENGRAM_ERANGE, "%s: %d layer(s) of T=%lld need %lld bytes of partial sums, more than the %lld "
+                        "bytes of scratch this entry point holds (engram_wkv_gate_layers takes a workspace)", what,
+                        layers, (long long)T, (long long)need, (long long)ENGRAM_NOALLOC_SCRATCH_BYTES);
+    } else if (workspace_bytes < need) {
         return fail(ENGRAM_ERANGE, "%s: workspace of %lld bytes, %lld needed", what, (long long)workspace_bytes,
                     (long long)need);
+    }
     if (T == 0) return ENGRAM_OK;
-    if (!workspace) return fail(ENGRAM_EINVAL, "%s: null pointer", what);
-    if (!aligned(workspace, 16)) return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
+    if (!static_scratch && !workspace) return fail(ENGRAM_EINVAL, "%s: null pointer", what);
+    if (!static_scratch && !aligned(workspace, 16)) return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
     const int Nout = (hc + 1) * dim;
     WkvArgs p = {};
     FinArgs f = {};
@@ -1096,6 +1138,12 @@ int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const
         if (!aligned(a[e], 16) || !aligned(w[e], 16) || !aligned(x[e], 16) || !aligned(q_weight[e], 16) ||
             !aligned(k_weight[e], 16) || !aligned(value[e], 16) || !aligned(dot[e], 4))
             return fail(ENGRAM_EINVAL, "%s: layer %d: misaligned pointer", what, e);
+    }
+    if (static_scratch) {
+        const int rc = scratch_address(&workspace, what);
+        if (rc != ENGRAM_OK) return rc;
+    }
+    for (int e = 0; e < layers; ++e) {
         LayerPtrs& L = p.lay[e];
         L.a = a[e];
         L.w = w[e];
@@ -1145,6 +1193,20 @@ extern "C" int engram_wkv_gate(const uint16_t* a, const uint16_t* w, const uint1
                                int32_t dim, void* stream) {
     return wkv_gate_entry("engram_wkv_gate", 1, &a, &w, &x, &q_weight, &k_weight, eps, &value, ld_value, &dot,
                           workspace, workspace_bytes, T, K, hc, dim, stream);
+}
+
+extern "C" int engram_wkv_gate_layers_noalloc(int32_t layers, const uint16_t* const* a, const uint16_t* const* w,
+                                              const uint16_t* const* x, const uint16_t* const* q_weight,
+                                              const uint16_t* const* k_weight, float eps, uint16_t* const* value,
+                                              int64_t ld_value, float* const* dot, int64_t T, int32_t K, int32_t hc,
+                                              int32_t dim, void* stream) {
+    const char* what = "engram_wkv_gate_layers_noalloc";
+    if (layers < 1 || layers > kMaxLayers)
+        return fail(ENGRAM_EINVAL, "%s: layers=%d outside [1, %d]", what, layers, kMaxLayers);
+    if (T > 0 && (!a || !w || !x || !q_weight || !k_weight || !value || !dot))
+        return fail(ENGRAM_EINVAL, "%s: null pointer array", what);
+    return wkv_gate_entry(what, layers, a, w, x, q_weight, k_weight, eps, value, ld_value, dot, nullptr, 0, T, K, hc,
+                          dim, stream, true);
 }
 
 extern "C" int engram_wkv_gate_layers(int32_t layers, const uint16_t* const* a, const uint16_t* const* w,

@@ -354,6 +354,32 @@ int engram_wkv_gate_layers(int32_t layers, const uint16_t* const* a, const uint1
                            float* const* dot, void* workspace, int64_t workspace_bytes, int64_t T, int32_t K,
                            int32_t hc, int32_t dim, void* stream);
 
+/*
+ * engram_wkv_gate_layers_noalloc -- engram_wkv_gate_layers without a workspace
+ * argument, for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The per-slice partial sums go to a file-scope device array of
+ * ENGRAM_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, held
+ * until the process ends); the call itself allocates nothing.  Results equal
+ * engram_wkv_gate_layers' bit for bit (same kernels, same launch shape).
+ *
+ * Arguments, limits and errors: as engram_wkv_gate_layers without
+ * `workspace`/`workspace_bytes`; ENGRAM_ERANGE if the layers need more than
+ * ENGRAM_NOALLOC_SCRATCH_BYTES of partial sums (layers * hc * dim/128 * 3 * T
+ * floats: e.g. 2 layers of 256 tokens at hc 4, dim 5120 need 983,040 bytes; at
+ * most 8,738 token-layers fit at that shape).  The scratch needs no
+ * initialisation (every call overwrites what it reads).
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (on different streams, or from several host threads without
+ * ordering) race and give wrong dots.  Order them on one stream.
+ */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int engram_wkv_gate_layers_noalloc(int32_t layers, const uint16_t* const* a, const uint16_t* const* w,
+                                   const uint16_t* const* x, const uint16_t* const* q_weight,
+                                   const uint16_t* const* k_weight, float eps, uint16_t* const* value,
+                                   int64_t ld_value, float* const* dot, int64_t T, int32_t K, int32_t hc,
+                                   int32_t dim, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

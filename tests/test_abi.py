@@ -258,3 +258,30 @@ def test_wkv_gate_layers_validation(kw, status, msg):
                                         a["T"], a["K"], a["hc"], a["dim"], None)
     assert rc == status
     assert msg in _err()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(layers=0), 1, "layers=0"), (dict(a=None), 1, "null pointer array"), (dict(K=96), 1, "K=96"),
+    (dict(dim=320), 1, "dim=320"), (dict(ld_value=200), 1, "ld_value"),
+    (dict(value=[FAKE.value, 0x100008]), 1, "layer 1: misaligned"),
+    # 2 layers x 4370 tokens x 4 copies x 40 slice pairs x 3 floats x 4 bytes = 16,780,800 > 16 MiB of scratch
+    (dict(T=4370, dim=5120), 2, "scratch"),
+])
+def test_wkv_gate_layers_noalloc_validation(kw, status, msg):
+    """The allocation-free entry point checks every argument, and its scratch limit, before it looks up the
+    scratch's device address (no HIP call happens here)."""
+    a = dict(layers=2, a=[FAKE.value] * 2, w=[FAKE.value] * 2, x=[FAKE.value] * 2, q=[FAKE.value] * 2,
+             k=[FAKE.value] * 2, value=[FAKE.value] * 2, ld_value=256, dot=[FAKE.value] * 2, T=10, K=128, hc=4,
+             dim=256)
+    a.update(kw)
+    if a["dim"] == 5120:
+        a["ld_value"] = 5120
+    arr = lambda v: None if v is None else (ctypes.c_void_p * len(v))(*v)
+    rc = g.lib().engram_wkv_gate_layers_noalloc(a["layers"], arr(a["a"]), arr(a["w"]), arr(a["x"]), arr(a["q"]),
+                                                arr(a["k"]), 1e-20, arr(a["value"]), a["ld_value"], arr(a["dot"]),
+                                                a["T"], a["K"], a["hc"], a["dim"], None)
+    assert rc == status
+    assert msg in _err()
+    assert g.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # 2 layers x 4369 tokens fit
+    assert 2 * g.lib().engram_wkv_gate_workspace_bytes(4369, 4, 5120) <= g.NOALLOC_SCRATCH_BYTES
