@@ -46,12 +46,21 @@ def lib():
         L.oracle_wkv.argtypes = [p, p, p, i64, i32, i32]
         L.oracle_gate_dot.argtypes = [p, p, i64, p, p, ctypes.c_double, p, i64, i32, i32]
         L.oracle_gate_output.argtypes = [p, p, i64, p, p, p, p, i64, i32, i32]
+        L.oracle_mx_quant.argtypes = [p, i64, i32, i32, p, p]
+        L.oracle_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, i32]
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
+        L.oracle_e4m3fn_encode_sat.argtypes = [ctypes.c_double]
+        L.oracle_e4m3fn_encode_sat.restype = ctypes.c_uint8
         L.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3fn_decode.restype = ctypes.c_float
         L.oracle_bf16_rne.argtypes = [ctypes.c_float]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_num_threads.restype = ctypes.c_int
-        for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot, L.oracle_gate_output):
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
+        for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot, L.oracle_gate_output,
+                  L.oracle_mx_quant, L.oracle_wkv_mx):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -141,6 +150,61 @@ def wkv_matmul(a_bits, w_bits, chunk: int = 4096):
     return out
 
 
+MX_BLOCK = 32  # columns per E8M0 scale of the fp8 block-scaled projection
+
+
+def mx_quant(x_bits, block_size: int = MX_BLOCK):
+    """bf16 bits [rows, K] -> (q uint8 [rows, K] E4M3FN bytes, scale uint8 [rows, K/block] E8M0 bytes) by the
+    OCP MX rule (shared exponent floor(log2 amax) - 8, elements rounded to nearest even and saturated)."""
+    x = _c(x_bits, np.uint16)
+    rows, K = x.shape
+    q = np.empty((rows, K), dtype=np.uint8)
+    sc = np.empty((rows, K // block_size), dtype=np.uint8)
+    _check(lib().oracle_mx_quant(_ptr(x), rows, K, block_size, _ptr(q), _ptr(sc)), "oracle_mx_quant")
+    return q, sc
+
+
+def wkv_mx(a_q, a_s, w_q, w_s, block_size: int = MX_BLOCK):
+    """The fp8 block-scaled projection: (a_q [T, K], a_s [T, K/blk]) x (w_q [Nout, K], w_s [Nout, K/blk])^T
+    -> float64 [T, Nout] (per block: scale_a * scale_w * sum of the E4M3 products, summed over blocks)."""
+    aq, as_, wq, ws = (_c(v, np.uint8) for v in (a_q, a_s, w_q, w_s))
+    T, K = aq.shape
+    Nout = wq.shape[0]
+    if wq.shape[1] != K or as_.shape != (T, K // block_size) or ws.shape != (Nout, K // block_size):
+        raise ValueError("wkv_mx: operand shapes disagree")
+    out = np.empty((T, Nout), dtype=np.float64)
+    _check(lib().oracle_wkv_mx(_ptr(aq), _ptr(as_), _ptr(wq), _ptr(ws), _ptr(out), T, K, Nout, block_size),
+           "oracle_wkv_mx")
+    return out
+
+
+def e8m0_decode(byte: int) -> float:
+    return float(lib().oracle_e8m0_decode(byte))
+
+
+def e4m3fn_encode_sat(value: float) -> int:
+    return int(lib().oracle_e4m3fn_encode_sat(float(value)))
+
+
+def mx_dequant(q, scale, block_size: int = MX_BLOCK):
+    """float64 values of MX operands: e4m3(q) * e8m0(scale of the block), through the oracle's decoders."""
+    dec8 = np.array([e4m3fn_decode(b) for b in range(256)], dtype=np.float64)
+    dec_s = np.array([e8m0_decode(b) for b in range(256)], dtype=np.float64)
+    q = np.asarray(q, dtype=np.uint8)
+    return dec8[q] * np.repeat(dec_s[np.asarray(scale, dtype=np.uint8)], block_size, axis=-1)
+
+
+def wkv_mx_matmul(a_q, a_s, w_q, w_s, block_size: int = MX_BLOCK, chunk: int = 4096):
+    """`wkv_mx` with numpy's float64 matmul as the contraction over the exactly dequantised operands (every
+    E4M3 value times a power of two is exact in float64): for whole-workload parity checks."""
+    a = mx_dequant(a_q, a_s, block_size)
+    wt = np.ascontiguousarray(mx_dequant(w_q, w_s, block_size).T)
+    out = np.empty((a.shape[0], wt.shape[1]), dtype=np.float64)
+    for t0 in range(0, a.shape[0], chunk):
+        np.matmul(a[t0:t0 + chunk], wt, out=out[t0:t0 + chunk])
+    return out
+
+
 def gate_dot(x_bits, kv_bits, q_bits, k_bits, eps):
     """x [T, hc, dim]; kv [T, >= hc*dim] (key = first hc*dim columns); q, k [hc, dim];
     all bf16 bits -> float64 dot [T, hc]."""
@@ -193,3 +257,8 @@ def bf16_bits_to_float(bits) -> np.ndarray:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on in this process."""
+    lib().oracle_set_num_threads(int(n))

@@ -196,6 +196,103 @@ int oracle_wkv(const uint16_t* a, const uint16_t* w, double* kv, int64_t T, int 
 }
 
 /* ------------------------------------------------------------------------ */
+/* step 4, fp8 block-scaled form: the `wkv` Linear under the released         */
+/* config's "dtype": "fp8"                                                   */
+/* ------------------------------------------------------------------------ */
+/* Reading (the pages name the fp8 Linear but do not show it): weights and
+ * inputs in the OCP microscaling (MX) fp8 format -- E4M3FN elements in blocks
+ * of 32 consecutive input columns of a row, each block with one E8M0 scale,
+ * the block-32/E8M0 format the pages name for the indexer's quantised
+ * activations.  The input rows are quantised to it by the OCP MX rule; the
+ * product accumulates scale_a * scale_w * sum(a * w) over the blocks. */
+
+/* E8M0: eight exponent bits, bias 127, no sign and no mantissa; 0xFF is NaN. */
+double oracle_e8m0_decode(uint8_t s) {
+    if (s == 0xFF) return NAN;
+    return ldexp(1.0, (int)s - 127);
+}
+
+/* Round half to even of a non-negative double (the quotient by the quantum is exact). */
+static double round_half_even(double n) {
+    const double fl = floor(n);
+    const double frac = n - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) return fl + 1.0;
+    return fl;
+}
+
+/* A finite double -> float8_e4m3fn byte: round to nearest, ties to even, on the E4M3 grid (subnormal
+ * quantum 2^-9 below 2^-6, 3 mantissa bits above), magnitudes past the largest finite value 448
+ * saturated to 448; the sign is kept (-0 -> 0x80); NaN -> 0x7F. */
+uint8_t oracle_e4m3fn_encode_sat(double v) {
+    if (isnan(v)) return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double m = fabs(v);
+    if (m >= 448.0) return sign | 0x7E;
+    if (m < ldexp(1.0, -6)) {                      /* subnormal: n * 2^-9, n in [0, 8] */
+        const int n = (int)round_half_even(m / ldexp(1.0, -9));
+        return sign | (uint8_t)n;                   /* n == 8 is the smallest normal, code 0x08 */
+    }
+    int e;
+    frexp(m, &e);                                   /* m = f * 2^e, f in [0.5, 1): floor(log2 m) = e - 1 */
+    e -= 1;
+    double n = round_half_even(m / ldexp(1.0, e - 3));  /* in [8, 16] */
+    if (n == 16.0) { n = 8.0; e += 1; }
+    if (e > 8 || (e == 8 && n > 14.0)) return sign | 0x7E; /* rounds past 448 */
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)n - 8));
+}
+
+/* OCP MX quantisation of bf16 rows: for row r and block b of `blk` columns, with amax the largest
+ * magnitude in the block, the shared exponent is floor(log2(amax)) - 8 (8 = the largest exponent of
+ * E4M3), kept within the E8M0 range [-127, 127] (an all-zero block takes -127); scale[r, b] = that
+ * exponent + 127, and q[r, k] = e4m3_sat(x[r, k] / 2^exponent).  Inputs must be finite. */
+int oracle_mx_quant(const uint16_t* x, int64_t rows, int K, int blk, uint8_t* q, uint8_t* scale) {
+    if (rows < 0 || K < 1 || blk < 1 || K % blk != 0) return ORACLE_EINVAL;
+    const int nb = K / blk;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + r * K + (int64_t)b * blk;
+            double amax = 0.0;
+            for (int k = 0; k < blk; ++k) amax = fmax(amax, fabs(oracle_bf16_to_double(xb[k])));
+            int shared = -127;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e);
+                shared = (e - 1) - 8;
+                if (shared < -127) shared = -127;
+                if (shared > 127) shared = 127;
+            }
+            scale[r * nb + b] = (uint8_t)(shared + 127);
+            for (int k = 0; k < blk; ++k)
+                q[r * K + (int64_t)b * blk + k] = oracle_e4m3fn_encode_sat(ldexp(oracle_bf16_to_double(xb[k]), -shared));
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The block-scaled projection: kv[t,o] = sum over blocks b of
+ * e8m0(a_s[t,b]) * e8m0(w_s[o,b]) * sum_{k in b} e4m3(a_q[t,k]) * e4m3(w_q[o,k]), in double. */
+int oracle_wkv_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s, double* kv,
+                  int64_t T, int K, int Nout, int blk) {
+    if (T < 0 || K < 1 || Nout < 1 || blk < 1 || K % blk != 0) return ORACLE_EINVAL;
+    const int nb = K / blk;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int o = 0; o < Nout; ++o) {
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                double part = 0.0;
+                for (int k = b * blk; k < (b + 1) * blk; ++k)
+                    part += (double)oracle_e4m3fn_decode(a_q[t * K + k]) * (double)oracle_e4m3fn_decode(w_q[(int64_t)o * K + k]);
+                acc += oracle_e8m0_decode(a_s[t * nb + b]) * oracle_e8m0_decode(w_s[(int64_t)o * nb + b]) * part;
+            }
+            kv[t * Nout + o] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* step 5: gate pre-activation                                               */
 /* ------------------------------------------------------------------------ */
 
@@ -267,5 +364,14 @@ int oracle_num_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Set the threads of the parallel loops above (a no-op without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

@@ -36,6 +36,16 @@ int oracle_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_s
 /* wkv: kv[t,o] = sum_k a[t,k] w[o,k] in double (a [T,K], w [Nout,K] bf16 bits). */
 int oracle_wkv(const uint16_t* a, const uint16_t* w, double* kv, int64_t T, int K, int Nout);
 
+/* fp8 block-scaled projection (OCP MX: E4M3FN elements, one E8M0 scale per
+ * `blk` consecutive columns of a row).  mx_quant: bf16 x [rows,K] -> q
+ * [rows,K] e4m3fn bytes and scale [rows,K/blk] E8M0 bytes; wkv_mx: kv[t,o] in
+ * double from a (q, scale) [T,K] and w (q, scale) [Nout,K]. */
+double oracle_e8m0_decode(uint8_t s);
+uint8_t oracle_e4m3fn_encode_sat(double v);
+int oracle_mx_quant(const uint16_t* x, int64_t rows, int K, int blk, uint8_t* q, uint8_t* scale);
+int oracle_wkv_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s, double* kv,
+                  int64_t T, int K, int Nout, int blk);
+
 /* gate pre-activation: x [T,hc,dim] bf16; key = kv[t, c*dim + j] with row stride
  * ld_kv (bf16); q_weight, k_weight [hc,dim] bf16 -> dot [T,hc] double. */
 int oracle_gate_dot(const uint16_t* x, const uint16_t* kv, int64_t ld_kv, const uint16_t* q_weight,
@@ -52,6 +62,7 @@ float oracle_e4m3fn_decode(uint8_t byte);
 uint16_t oracle_bf16_rne(float f);
 double oracle_bf16_to_double(uint16_t h);
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

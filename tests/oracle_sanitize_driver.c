@@ -125,10 +125,37 @@ static void drive_wkv_gate(void) {
     EXPECT(oracle_wkv(a, w, kv, 0, K, NOUT) == 0);
 }
 
+static void drive_mx(void) {
+    enum { T = 4, K = 96, N = 7, BLK = 32 };
+    uint16_t x[T * K], w[N * K];
+    for (int i = 0; i < T * K; ++i) x[i] = (uint16_t)next_u64();  /* any bf16 pattern but NaN/inf: */
+    for (int i = 0; i < T * K; ++i)
+        if ((x[i] & 0x7F80) == 0x7F80) x[i] &= 0xBFFF;
+    for (int i = 0; i < N * K; ++i) w[i] = (uint16_t)(0x3C00 + (next_u64() % 0x200));
+    memset(x + K, 0, sizeof(uint16_t) * BLK);  /* an all-zero block */
+    x[2 * K] = 0x0001;                         /* the smallest subnormal */
+    uint8_t aq[T * K], as_[T * (K / BLK)], wq[N * K], ws[N * (K / BLK)];
+    EXPECT(oracle_mx_quant(x, T, K, BLK, aq, as_) == 0);
+    EXPECT(oracle_mx_quant(w, N, K, BLK, wq, ws) == 0);
+    EXPECT(as_[K / BLK] == 0); /* row 1, block 0: all zero */
+    double kv[T * N];
+    EXPECT(oracle_wkv_mx(aq, as_, wq, ws, kv, T, K, N, BLK) == 0);
+    EXPECT(oracle_mx_quant(x, T, K, 40, aq, as_) == ORACLE_EINVAL); /* 96 % 40 != 0 */
+    for (int b = 0; b < 256; ++b) {
+        const double v = oracle_e8m0_decode((uint8_t)b);
+        EXPECT(isnan(v) == (b == 255));
+        if ((b & 0x7F) != 0x7F) EXPECT(oracle_e4m3fn_encode_sat(oracle_e4m3fn_decode((uint8_t)b)) == b);
+    }
+    EXPECT(oracle_e4m3fn_encode_sat(1e300) == 0x7E);
+    EXPECT(oracle_e4m3fn_encode_sat(-1e-300) == 0x80);
+    EXPECT(oracle_e4m3fn_encode_sat(NAN) == 0x7F);
+}
+
 int main(void) {
     drive_hash();
     drive_gather();
     drive_wkv_gate();
+    drive_mx();
     if (fails) {
         fprintf(stderr, "%d expectations failed\n", fails);
         return 1;

@@ -17,8 +17,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "engram_oracle.c")
 
-HASH, DEQ, WKV_GATE, OUT = ("tests/test_oracle_hash.py", "tests/test_oracle_dequant.py",
-                            "tests/test_oracle_wkv_gate.py", "tests/test_oracle_gate_output.py")
+HASH, DEQ, WKV_GATE, OUT, MX = ("tests/test_oracle_hash.py", "tests/test_oracle_dequant.py",
+                                "tests/test_oracle_wkv_gate.py", "tests/test_oracle_gate_output.py",
+                                "tests/test_oracle_mx.py")
 
 # name -> (text in the oracle, planted replacement, pin file that must fail)
 MUTANTS = {
@@ -50,6 +51,18 @@ MUTANTS = {
     "mask_ignored": ("if (token_mask && !token_mask[t]) g = 0.0;", "(void)token_mask;", OUT),
     "value_of_copy_0": ("const uint16_t* value = kv + t * ld_kv + (int64_t)hc * dim;",
                         "const uint16_t* value = kv + t * ld_kv;", OUT),
+    "e8m0_bias": ("return ldexp(1.0, (int)s - 127);", "return ldexp(1.0, (int)s - 128);", MX),
+    "e4m3_ties_away": ("if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) return fl + 1.0;",
+                       "if (frac >= 0.5) return fl + 1.0;", MX),
+    "e4m3_no_saturation": ("if (m >= 448.0) return sign | 0x7E;", "if (m >= 464.0) return sign | 0x7F;", MX),
+    "mx_exponent_ceil": ("shared = (e - 1) - 8;", "shared = e - 8;", MX),
+    "mx_zero_block_exponent": ("int shared = -127;", "int shared = 0;", MX),
+    "mx_sign_dropped": ("oracle_e4m3fn_encode_sat(ldexp(oracle_bf16_to_double(xb[k]), -shared))",
+                        "oracle_e4m3fn_encode_sat(ldexp(fabs(oracle_bf16_to_double(xb[k])), -shared))", MX),
+    "mx_subnormal_quantum": ("const int n = (int)round_half_even(m / ldexp(1.0, -9));",
+                             "const int n = (int)round_half_even(m / ldexp(1.0, -8));", MX),
+    "wkv_mx_first_block_scale": ("acc += oracle_e8m0_decode(a_s[t * nb + b])", "acc += oracle_e8m0_decode(a_s[t * nb])",
+                                 MX),
 }
 
 _RUNNER = ("import sys; sys.path.insert(0, {root!r}); import oracle; oracle.LIB_PATH = sys.argv[1]; "
