@@ -19,6 +19,8 @@ an exception is raised.
     engram_wkv_gate_layers -- engram_wkv_gate for several engram layers in one launch
     engram_wkv_gate_layers_noalloc -- the same with the library's own device scratch (allocates nothing)
     engram_gate_residual   -- gate, token mask and residual add from a given dot
+    engram_mx_quant        -- bf16 rows -> OCP MX fp8 (E4M3 + E8M0 scale per 32 columns)
+    engram_wkv_mx          -- the wkv projection on MX fp8 operands (fp8 matrix cores with block scales)
 """
 from __future__ import annotations
 
@@ -61,11 +63,15 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_residual.argtypes = [p, p, i64, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_layers.argtypes = [i32, p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_wkv_gate_layers_noalloc.argtypes = [i32, p, p, p, p, p, f32, p, i64, p, i64, i32, i32, i32, p]
+        L.engram_mx_scale_bytes.argtypes = [i64, i32]
+        L.engram_mx_scale_bytes.restype = i64
+        L.engram_mx_quant.argtypes = [p, i64, i32, p, p, p]
+        L.engram_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
         for f in (L.engram_hash, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
-                  L.engram_wkv_gate_layers, L.engram_wkv_gate_layers_noalloc,
+                  L.engram_wkv_gate_layers, L.engram_wkv_gate_layers_noalloc, L.engram_mx_quant, L.engram_wkv_mx,
                   L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
@@ -360,6 +366,58 @@ def engram_gate_output(x, kv, q_weight, k_weight, eps, token_mask=None, out=None
     return out
 
 
+def engram_mx_scale_bytes(rows: int, K: int) -> int:
+    n = lib().engram_mx_scale_bytes(int(rows), int(K))
+    if n < 0:
+        raise ValueError(f"MX operands need K a positive multiple of 128, got {K}")
+    return n
+
+
+def engram_mx_quant(x, q=None, scale=None, stream=None):
+    """bf16 x [rows, K] -> (q uint8 [rows, K] E4M3FN bytes, scale uint8 [K/128, rows4, 4] E8M0 bytes), the OCP MX
+    quantisation (include/engram.h for the scale layout)."""
+    import torch
+
+    x2 = x.reshape(x.shape[0], -1) if x.dim() == 3 else x
+    rows, K = x2.shape
+    nbytes = engram_mx_scale_bytes(rows, K)
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((K // 128, (rows + 3) // 4 * 4, 4), dtype=torch.uint8, device=x.device)
+    if tuple(q.shape) != (rows, K):
+        raise ValueError("q must be [rows, K]")
+    if scale.numel() != nbytes:
+        raise ValueError(f"scale must hold {nbytes} bytes")
+    _check(lib().engram_mx_quant(_dev(x2, "x", torch.bfloat16, 2), rows, K, _dev(q, "q", torch.uint8, 2),
+                                 _dev(scale, "scale", torch.uint8), _stream(stream)))
+    return q, scale
+
+
+def engram_wkv_mx(a, a_scale, w, w_scale, out=None, stream=None):
+    """kv bf16 [T, Nout] from MX fp8 operands a (uint8 [T, K]) and w (uint8 [Nout, K]) with their scales."""
+    import torch
+
+    if a.dtype == torch.float8_e4m3fn:
+        a = a.view(torch.uint8)
+    if w.dtype == torch.float8_e4m3fn:
+        w = w.view(torch.uint8)
+    T, K = a.shape
+    Nout, K2 = w.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: a has {K}, w has {K2}")
+    if a_scale.numel() != engram_mx_scale_bytes(T, K) or w_scale.numel() != engram_mx_scale_bytes(Nout, K):
+        raise ValueError("a_scale / w_scale must be MX scale arrays of a and w")
+    if out is None:
+        out = torch.empty((T, Nout), dtype=torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (T, Nout):
+        raise ValueError("out must be [T, Nout]")
+    _check(lib().engram_wkv_mx(_dev(a, "a", torch.uint8, 2), _dev(a_scale, "a_scale", torch.uint8),
+                               _dev(w, "w", torch.uint8, 2), _dev(w_scale, "w_scale", torch.uint8),
+                               _dev(out, "out", torch.bfloat16, 2), T, K, Nout, _stream(stream)))
+    return out
+
+
 def engram_wkv_gate_workspace_bytes(T: int, hc: int, dim: int) -> int:
     n = lib().engram_wkv_gate_workspace_bytes(int(T), int(hc), int(dim))
     if n < 0:
@@ -512,6 +570,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
            "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_layers_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "engram_wkv_gate_workspace_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate_workspace_bytes", "engram_mx_quant", "engram_wkv_mx", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

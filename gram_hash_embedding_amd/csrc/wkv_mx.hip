@@ -1,0 +1,476 @@
+// The `wkv` Linear on fp8 block-scaled operands (the released config's "dtype": "fp8"; DeepSeek V4.1
+// "stack-hashes" page: the config block and Engram.__init__), in the OCP microscaling (MX) fp8 format:
+// E4M3FN elements, one E8M0 scale per 32 consecutive input columns of a row.
+//
+//   engram_mx_quant  -- bf16 rows -> MX fp8 (the activation side of the fp8 Linear; also the weights' one-off
+//                       conversion): shared exponent floor(log2 amax) - 8 per 32 columns, elements rounded to
+//                       nearest even and saturated at 448
+//   engram_wkv_mx    -- kv = A * W^T with v_mfma_scale_f32_32x32x64_f8f6f4 (the block scales applied by the
+//                       matrix core), fp32 accumulation, one bf16 rounding
+//
+// Scale layout (both operands): uint8 [K/128][rows4][4], rows4 = rows rounded up to a multiple of 4; byte
+// [s][r][b] scales row r's columns 128 s + 32 b .. +32.  A 128-column slab of a 256-row tile then has its
+// scales in one contiguous kilobyte, loaded with the slab by one 16-byte-per-lane direct-to-LDS load.
+//
+// Design (gfx950): the bf16 projection's persistent design (wkv.hip) with fp8 slabs -- 256 x 256 tiles, eight
+// waves (two per SIMD, loader waves 0-3 issue every slab load, storer waves 4-7 every store), slabs of 128
+// fp8 columns (128-byte rows, the same XOR swizzle as the bf16 slabs of 64 columns) in two stages, XCD-grouped
+// tile order.  A stage holds 66 KB (A and W slabs and their scales), so the epilogue exchange is 16 KB and
+// runs in eight rounds of 32 tokens x 128 outputs per wave pair.  Each wave: 128 tokens x 64 outputs = 4 x 2
+// MFMA blocks of 32x32 (K 64 per MFMA: two per slab).  Lane l of a 32x32x64 fragment holds row l % 32: in
+// its first 16 bytes columns 16h .. 16h + 15 and in its last 16 bytes columns 32 + 16h .. 32 + 16h + 15 of
+// the step (h = l / 32); the scale operand of lane half h scales the step's 32-column block h of the row (the
+// first 16 bytes of both halves, or the last 16) -- measured on gfx950.  Each lane's slab scale word (byte b:
+// block b of the slab) is shifted right by 8 h, and k-step s takes byte 2 s.
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+
+namespace engram {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 256, BN = 256;
+constexpr int kSlabCols = 128;              // fp8 columns (= bytes) per slab row
+constexpr int kMxBlock = 32;                // columns per E8M0 scale
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kOpBytes = 256 * kSlabCols;   // one operand's slab: 32 KB
+constexpr int kScBytes = 256 * 4;           // its scales: 1 KB
+constexpr int kStageBytes = 2 * kOpBytes + 2 * kScBytes;
+constexpr int kExBytes = 64 * 256;          // epilogue exchange: 64 token rows x 128 outputs (bf16)
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+constexpr int kCUs = 256;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+struct MxArgs {
+    const uint8_t* a;    // [M, K] e4m3
+    const uint8_t* as;   // [K/128][M4][4] e8m0
+    const uint8_t* w;    // [N, K] e4m3
+    const uint8_t* ws;   // [K/128][N4][4] e8m0
+    uint16_t* kv;        // [M, ld_out] bf16
+    int64_t M;
+    int N, K;
+    int64_t M4, N4;      // rows of the scale layouts (multiples of 4)
+    int tiles_m, tiles_n;
+    int64_t ld_out;
+};
+
+// pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
+__device__ inline void tile_coords(const MxArgs& p, int pid, int& tm, int& tn) {
+    const int n = p.tiles_m * p.tiles_n;
+    const int xcd = pid % kXcds, idx = pid / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    const int logical = xcd * per + min(xcd, rem) + idx;
+    const int in_group = kGroupM * p.tiles_n;
+    const int group = logical / in_group;
+    const int first_m = group * kGroupM;
+    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int r = logical - group * in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int G = gridDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const bool loader = wave < 4;
+    const int KT = p.K / kSlabCols;
+    const int row_bytes = p.K;
+
+    auto sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto sync_epi = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        sync();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- slab loads (loader waves): wave w fills rows [64w, 64w+64) of the A and of the W slab, 8 rows per
+    // instruction, lane l at slot (l & 7) of row base + 8q + (l >> 3), fetching the piece the swizzle puts
+    // there; wave 0 also loads the A slab's scales (1 KB), wave 1 the W slab's.  Rows past M or N fall outside
+    // their resource and read as zero.
+    const int ld_r = lane >> 3, ld_slot = lane & 7;
+    const uint32_t vo_piece = static_cast<uint32_t>(ld_r * row_bytes + ((ld_slot ^ (ld_r >> 1)) << 4));
+    const uint32_t vo_rows = vo_piece + static_cast<uint32_t>(wave * 64 * row_bytes);
+    struct SlabRsrc {
+        __amdgpu_buffer_rsrc_t ra, rw, rs;
+        uint32_t k0b;
+    };
+    auto slab_rsrc = [&](int pid, int kt, bool live) {
+        int tm, tn;
+        tile_coords(p, pid, tm, tn);
+        const int64_t m0 = static_cast<int64_t>(tm) * BM;
+        const int n0 = tn * BN;
+        const int a_bytes = live ? static_cast<int>(min<int64_t>(BM, p.M - m0)) * row_bytes : 0;
+        const int w_bytes = live ? min(BN, p.N - n0) * row_bytes : 0;
+        SlabRsrc r;
+        r.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * p.K), 0, a_bytes, kBufferWord3);
+        r.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w + static_cast<int64_t>(n0) * p.K), 0, w_bytes,
+                                                 kBufferWord3);
+        // slab kt's scales of the tile's 256 rows: bytes [(kt * rows4 + row0) * 4, +1024) of the layout (wave 0:
+        // the A side, wave 1: the W side)
+        const uint8_t* sbase = wave == 0 ? p.as : p.ws;
+        const int64_t rows4 = wave == 0 ? p.M4 : p.N4;
+        const int64_t row0 = wave == 0 ? m0 : n0;
+        const int valid = live ? static_cast<int>(min<int64_t>(256, rows4 - row0)) * 4 : 0;
+        r.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase + (static_cast<int64_t>(kt) * rows4 + row0) * 4),
+                                                 0, valid, kBufferWord3);
+        r.k0b = static_cast<uint32_t>(kt * kSlabCols);
+        return r;
+    };
+    // part q (0..7) of a slab's loads: rows 8q..8q+7 of the wave's A and W rows (2 loads); part 0 of waves 0
+    // and 1 also the scales (1 load)
+    auto issue_part = [&](const SlabRsrc& r, int stage, int q) {
+        uint8_t* st = lds + stage * kStageBytes;
+        const uint32_t flip = (q & 1) ? (4u << 4) : 0u;
+        const uint32_t qrows = static_cast<uint32_t>(q * 8 * row_bytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ra, st + (wave * 64 + q * 8) * 128, 16, (vo_rows ^ flip) + qrows,
+                                                 r.k0b, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rw, st + kOpBytes + (wave * 64 + q * 8) * 128, 16,
+                                                 (vo_rows ^ flip) + qrows, r.k0b, 0, 0);
+        if (q == 0 && wave < 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rs, st + 2 * kOpBytes + wave * kScBytes, 16,
+                                                     static_cast<uint32_t>(lane * 16), 0, 0, 0);
+    };
+    auto issue_slab = [&](int pid, int kt, int stage, bool live) {
+        const SlabRsrc r = slab_rsrc(pid, kt, live);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) issue_part(r, stage, q);
+    };
+
+    // ---- fragments: lane reads row (lane % 32) of a 32-row block, for k-step s (columns 64s .. 64s + 63):
+    // bytes 0-15 of the fragment hold columns 64s + 16h .. +15 and bytes 16-31 columns 64s + 32 + 16h .. +15
+    // (h = lane / 32), i.e. pieces 4s + h and 4s + 2 + h, each at its swizzled slot.  So the first 16 bytes
+    // of both lane halves form the step's first 32-column block and the last 16 bytes its second: the scale
+    // operand of lane half h is the row's scale of block 2s + h.
+    const int h = lane >> 5;
+    const int g = (lane >> 1) & 7;  // swizzle key of the lane's rows (blocks start at multiples of 16 rows)
+    const int a_row = (wm * 128 + (lane & 31)) * 128;
+    const int w_row = kOpBytes + (wn * 64 + (lane & 31)) * 128;
+    auto read_piece = [&](int stage, int s, int row_off) -> i32x8 {
+        const uint8_t* base = lds + stage * kStageBytes + row_off;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(base + (((4 * s + h) ^ g) << 4));
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(base + (((4 * s + 2 + h) ^ g) << 4));
+        return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    };
+    auto read_a = [&](int stage, int s, int i) { return read_piece(stage, s, a_row + i * 32 * 128); };
+    auto read_w = [&](int stage, int s, int j) { return read_piece(stage, s, w_row + j * 32 * 128); };
+    // the slab's scale words of the lane's rows (raw); shift_scales then moves the lane's K half of k-step 0 /
+    // k-step 1 into byte 0 / byte 2
+    auto read_scales = [&](int stage, uint32_t* sa, uint32_t* sw) {
+        const uint8_t* base = lds + stage * kStageBytes + 2 * kOpBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(base + (wm * 128 + i * 32 + (lane & 31)) * 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sw[j] = *reinterpret_cast<const uint32_t*>(base + kScBytes + (wn * 64 + j * 32 + (lane & 31)) * 4);
+    };
+    auto shift_scales = [&](uint32_t* sa, uint32_t* sw) {
+        const int sh = 8 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] >>= sh;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sw[j] >>= sh;
+    };
+
+    // ---- epilogue: 8 rounds (4 token blocks x 2 column halves); in round (i, hf) the waves of column half hf
+    // (wn >> 1 == hf) put tokens 32i..32i+31 x their 64 outputs into the exchange (64 rows of 256 B, row
+    // 32 wm + t, 16-byte pieces XOR-swizzled by row), then the storer waves write 16 rows each with full-line,
+    // non-temporal 16-byte stores
+    uint8_t* ex = lds + 2 * kStageBytes;
+    auto epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
+        const int l = lane_id();
+        const int key = l & 15;
+        const uint32_t wbase = static_cast<uint32_t>((wm * 32 + (l & 31)) * 256 + (l >> 5) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if ((wn >> 1) == hf) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int chunk = (wn & 1) * 8 + 4 * j + gq;
+                            const u32x2 v = {pack_bf16(acc[i][j][4 * gq + 0], acc[i][j][4 * gq + 1]),
+                                             pack_bf16(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
+                            *reinterpret_cast<u32x2*>(ex + wbase + ((chunk ^ key) << 4)) = v;
+                        }
+                }
+                sync_epi();
+                if (!loader) {
+                    const int s = wave - 4;
+                    const int ls = lane_id();
+                    const int chunk = ls & 15;
+                    const int ncol = n0 + hf * 128 + chunk * 8;
+#pragma unroll
+                    for (int ins = 0; ins < 4; ++ins) {
+                        const int rr = 16 * s + 4 * ins + (ls >> 4);  // exchange row: token half rr / 32
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(ex + rr * 256 + ((chunk ^ (rr & 15)) << 4));
+                        const int64_t m = m0 + (rr >> 5) * 128 + 32 * i + (rr & 31);
+                        if (m < p.M && ncol < p.N)
+                            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + ncol));
+                    }
+                }
+                sync_epi();
+            }
+        }
+    };
+
+    if (static_cast<int>(blockIdx.x) >= tiles) return;
+    const int my_tiles = (tiles - 1 - static_cast<int>(blockIdx.x)) / G + 1;
+    const int total = my_tiles * KT;  // slabs of this workgroup
+    // the slab stream of this workgroup: slab number n -> (tile pid, k slab)
+    auto slab_pid = [&](int n) { return static_cast<int>(blockIdx.x) + (n / KT) * G; };
+
+    // One k-step: acc[i][j] += (W fragment j) x (A fragment i) scaled by byte kSel of the lane's scale words,
+    // in W-fragment-major order; each fragment is reloaded, for k-step `ns` of stage `nst`, right after its last
+    // use here (one set of 48 fragment registers; every reload is issued three or more MFMAs before its use).
+    // Each MFMA with its reloads and `extra(u)` (u = 0..7: a share of the slab loads) is one scheduling unit.
+    auto kstep = [&](auto sel_tag, auto zero_tag, f32x16 (&acc)[4][2], i32x8 (&fa)[4], i32x8 (&fw)[2],
+                     const uint32_t* sa, const uint32_t* sw, int nst, int ns, auto&& extra) {
+        constexpr int kSel = decltype(sel_tag)::value;
+        constexpr bool kZero = decltype(zero_tag)::value;
+        const f32x16 z = {};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0], fa[i], kZero ? z : acc[i][0], 0, 0,
+                                                                        kSel, sw[0], kSel, sa[i]);
+            if (i == 3) fw[0] = read_w(nst, ns, 0);
+            extra(i);
+            asm volatile("" ::: "memory");  // keeps the unit's LDS reads and loads in the unit
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1], fa[i], kZero ? z : acc[i][1], 0, 0,
+                                                                        kSel, sw[1], kSel, sa[i]);
+            fa[i] = read_a(nst, ns, i);
+            if (i == 3) fw[1] = read_w(nst, ns, 1);
+            extra(4 + i);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto no_extra = [](int) {};
+
+    auto run = [&](auto loader_tag) {
+        constexpr bool kLoader = decltype(loader_tag)::value;
+        if (kLoader) {
+            issue_slab(slab_pid(0), 0, 0, true);
+            issue_slab(slab_pid(1 < total ? 1 : 0), 1 % KT, 1, 1 < total);
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        }
+        sync();
+        f32x16 acc[4][2];
+        i32x8 fa[4], fw[2];
+        uint32_t sa[4], sw[2];
+        int stage = 0;
+        int n = 0;  // slab number in this workgroup's stream
+        read_scales(0, sa, sw);
+        shift_scales(sa, sw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = read_a(0, 0, i);
+        fw[0] = read_w(0, 0, 0);
+        fw[1] = read_w(0, 0, 1);
+        for (int t = 0; t < my_tiles; ++t) {
+            const int pid = static_cast<int>(blockIdx.x) + t * G;
+            int tm, tn;
+            tile_coords(p, pid, tm, tn);
+            const int64_t m0 = static_cast<int64_t>(tm) * BM;
+            const int n0 = tn * BN;
+            for (int kt = 0; kt < KT; ++kt, ++n) {
+                // k-step 0 of the slab (its fragments and scales already in registers), reloading k-step 1's
+                if (kt == 0)
+                    kstep(std::integral_constant<int, 0>{}, std::true_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra);
+                else
+                    kstep(std::integral_constant<int, 0>{}, std::false_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra);
+                // the next slab has landed (the loaders waited for it) and this stage is read out: publish one
+                // stage, refill the other with the slab after next
+                if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+                sync();
+                // k-step 1, reloading k-step 0 of the next slab (and its scales) from the other stage; the loaders
+                // spread the slab after next over its MFMAs
+                uint32_t sa_n[4], sw_n[2];
+                const int nst = stage ^ 1;
+                if (kLoader) {
+                    const int nn = n + 2;
+                    const SlabRsrc r = slab_rsrc(slab_pid(nn < total ? nn : 0), nn % KT, nn < total);
+                    const int st = stage;
+                    kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
+                        if (u == 0) read_scales(nst, sa_n, sw_n);  // (past the last slab: stale, unused)
+                        issue_part(r, st, u);
+                    });
+                } else {
+                    kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
+                        if (u == 0) read_scales(nst, sa_n, sw_n);
+                    });
+                }
+                shift_scales(sa_n, sw_n);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) sw[j] = sw_n[j];
+                stage ^= 1;
+            }
+            epilogue(acc, m0, n0);
+        }
+        // loads issued past this workgroup's last slab (empty resources) still write LDS: let them land
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    };
+    if (loader)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+}
+
+// ---- OCP MX quantisation of bf16 rows (one wave per 32-column block group) ----
+// A thread owns 8 consecutive columns (one 16-byte load); the 4 threads of a 32-column block reduce their
+// amax with two lane swaps.  The shared exponent floor(log2 amax) - 8 is read off amax's fp32 exponent field
+// (amax is a bf16 value, so it is normal or a bf16 subnormal, which fp32 holds exactly); the scaled element
+// x * 2^-e is formed exactly by ldexp and rounded to E4M3 (nearest even, saturated at 448) from its bits.
+__device__ inline uint32_t e4m3_sat_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float m = fabsf(v);
+    if (m >= 448.0f) return sign | 0x7Eu;
+    if (m < 0.015625f) {  // below 2^-6: multiples of 2^-9
+        const float n = __builtin_rintf(m * 512.0f);  // exact product; rint rounds half to even
+        return sign | static_cast<uint32_t>(n);
+    }
+    const uint32_t mu = __float_as_uint(m);
+    const int e = static_cast<int>(mu >> 23) - 127;          // floor(log2 m), in [-6, 8]
+    const uint32_t mant = mu & 0x7FFFFFu;
+    // keep 3 mantissa bits, round the other 20 to nearest even
+    uint32_t q = (mant >> 20) | 8u;                          // 8..15
+    const uint32_t rest = mant & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ++q;
+    int ee = e;
+    if (q == 16u) {
+        q = 8u;
+        ++ee;
+    }
+    if (ee > 8 || (ee == 8 && q > 14u)) return sign | 0x7Eu;
+    return sign | (static_cast<uint32_t>(ee + 7) << 3) | (q - 8u);
+}
+
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* x, int64_t rows, int K, int64_t rows4,
+                                                      uint8_t* q, uint8_t* scale) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int per_row = K / 8;
+    const int64_t r = gid / per_row;
+    const int c8 = static_cast<int>(gid - r * per_row);  // 8-column group
+    const bool ok = r < rows;
+    u32x4 v = {0, 0, 0, 0};
+    if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + r * K) + c8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    // the 4 threads of a block are lanes 4b .. 4b+3 of the wave (K / 8 is a multiple of 4)
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    int shared = -127;
+    if (amax > 0.f) {
+        const uint32_t au = __float_as_uint(amax);
+        const int ef = static_cast<int>(au >> 23);
+        const int fl = ef != 0 ? ef - 127 : 31 - __builtin_clz(au & 0x7FFFFFu) - 149;  // floor(log2 amax)
+        shared = max(-127, min(127, fl - 8));
+    }
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i >> 2] |= e4m3_sat_rne(__builtin_ldexpf(f[i], -shared)) << (8 * (i & 3));
+    if (!ok) return;
+    *reinterpret_cast<u32x2*>(q + r * K + 8 * c8) = u32x2{packed[0], packed[1]};
+    if ((c8 & 3) == 0) {
+        const int b = c8 / 4;  // the 32-column block
+        scale[((static_cast<int64_t>(b / 4) * rows4 + r) * 4) + (b & 3)] = static_cast<uint8_t>(shared + 127);
+    }
+}
+
+}  // namespace
+}  // namespace engram
+
+using namespace engram;
+
+extern "C" int64_t engram_mx_scale_bytes(int64_t rows, int32_t K) {
+    if (rows < 0 || K < kSlabCols || K % kSlabCols != 0) return -1;
+    return (K / kSlabCols) * ((rows + 3) / 4 * 4) * 4;
+}
+
+extern "C" int engram_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* q, uint8_t* scale, void* stream) {
+    const char* what = "engram_mx_quant";
+    if (rows < 0) return fail(ENGRAM_EINVAL, "%s: rows < 0", what);
+    if (K < kSlabCols || K % kSlabCols != 0) return fail(ENGRAM_EINVAL, "%s: K=%d must be a positive multiple of %d", what, K, kSlabCols);
+    if (rows == 0) return ENGRAM_OK;
+    if (!x || !q || !scale) return fail(ENGRAM_EINVAL, "%s: null pointer", what);
+    if (!aligned(x, 16) || !aligned(q, 8)) return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
+    const int64_t threads = rows * (K / 8);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many rows", what);
+    hipLaunchKernelGGL(mx_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, as_stream(stream), x, rows, K,
+                       (rows + 3) / 4 * 4, q, scale);
+    return check_launch(what);
+}
+
+extern "C" int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                             uint16_t* kv, int64_t T, int32_t K, int32_t Nout, void* stream) {
+    const char* what = "engram_wkv_mx";
+    if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", what);
+    if (K < kSlabCols || K % kSlabCols != 0) return fail(ENGRAM_EINVAL, "%s: K=%d must be a positive multiple of %d", what, K, kSlabCols);
+    if (Nout < 8 || Nout % 8 != 0) return fail(ENGRAM_EINVAL, "%s: Nout=%d must be a positive multiple of 8", what, Nout);
+    if (T == 0) return ENGRAM_OK;
+    if (!a || !a_scale || !w || !w_scale || !kv) return fail(ENGRAM_EINVAL, "%s: null pointer", what);
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_scale, 16) || !aligned(w_scale, 16) || !aligned(kv, 16))
+        return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
+    MxArgs p = {};
+    p.a = a;
+    p.as = a_scale;
+    p.w = w;
+    p.ws = w_scale;
+    p.kv = kv;
+    p.M = T;
+    p.N = Nout;
+    p.K = K;
+    p.M4 = (T + 3) / 4 * 4;
+    p.N4 = (static_cast<int64_t>(Nout) + 3) / 4 * 4;
+    p.ld_out = Nout;
+    const int64_t tiles_m = (T + BM - 1) / BM;
+    p.tiles_n = (Nout + BN - 1) / BN;
+    if (tiles_m * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
+    p.tiles_m = static_cast<int>(tiles_m);
+    const int64_t tiles = tiles_m * p.tiles_n;
+    const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
+    hipLaunchKernelGGL(wkv_mx_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    return check_launch(what);
+}

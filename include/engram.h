@@ -29,6 +29,11 @@
  *                             one launch
  *   engram_wkv_gate_layers -- engram_wkv_gate for every layer in one launch
  *
+ * the fp8 block-scaled (OCP MX) form of the `wkv` Linear:
+ *
+ *   engram_mx_quant        -- bf16 rows to MX fp8 (E4M3 + an E8M0 scale per 32 columns)
+ *   engram_wkv_mx          -- the projection on MX fp8 operands
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every array argument is a DEVICE pointer (memory the caller allocated on
@@ -353,6 +358,57 @@ int engram_wkv_gate_layers(int32_t layers, const uint16_t* const* a, const uint1
                            const uint16_t* const* k_weight, float eps, uint16_t* const* value, int64_t ld_value,
                            float* const* dot, void* workspace, int64_t workspace_bytes, int64_t T, int32_t K,
                            int32_t hc, int32_t dim, void* stream);
+
+/*
+ * The fp8 block-scaled form of the `wkv` Linear (stack-hashes page: the released
+ * config's "dtype": "fp8" and Engram.__init__'s `wkv`; the pages name the fp8
+ * Linear without showing it).  Operands are in the OCP microscaling (MX) fp8
+ * format: float8_e4m3fn elements, and for every 32 consecutive columns of a
+ * row one E8M0 scale byte s meaning 2^(s-127) -- the block-32 / E8M0 format
+ * the pages use for the indexer's quantised activations.
+ *
+ * MX scale layout of this library: uint8 [K/128][rows4][4], rows4 = rows
+ * rounded up to a multiple of 4; byte [c][r][b] is the scale of row r,
+ * columns 128c + 32b .. 128c + 32b + 31 (engram_mx_scale_bytes gives the size;
+ * bytes of the padding rows are never written and never affect an output).
+ */
+
+/* Bytes of an MX scale array for `rows` rows of K columns, or -1 if K is not a
+ * positive multiple of 128. */
+int64_t engram_mx_scale_bytes(int64_t rows, int32_t K);
+
+/*
+ * engram_mx_quant -- bf16 rows to MX fp8 by the OCP MX rule: for each row and
+ * 32-column block with largest magnitude amax, e = floor(log2 amax) - 8 (8 being
+ * E4M3's largest exponent), kept in [-127, 127] (-127 for an all-zero block);
+ * scale = e + 127; q = x * 2^-e rounded to the nearest E4M3FN value, ties to even,
+ * magnitudes past 448 saturated to 448, the sign kept (so -0 gives 0x80).  The
+ * activation side of the fp8 Linear (its bf16 input, the gathered rows), and the
+ * one-off conversion of bf16 weights.
+ *
+ * x      uint16 [rows, K] bf16 bits, finite values; 16-byte aligned
+ * q      uint8 [rows, K], out; 8-byte aligned
+ * scale  uint8, engram_mx_scale_bytes(rows, K) bytes in the layout above, out
+ * Limits: rows >= 0; K >= 128 and K % 128 == 0.
+ */
+int engram_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* q, uint8_t* scale, void* stream);
+
+/*
+ * engram_wkv_mx -- the projection on MX fp8 operands:
+ *   kv[t,o] = bf16( sum over 32-column blocks b of
+ *                   2^(a_scale[t,b]-127) * 2^(w_scale[o,b]-127) * sum_{k in b} e4m3(a[t,k]) * e4m3(w[o,k]) )
+ * with fp32 accumulation and one bf16 rounding (round to nearest even).
+ *
+ * a        uint8 [T, K] E4M3FN bytes; 16-byte aligned
+ * a_scale  MX scales of a (T rows), layout above; 16-byte aligned
+ * w        uint8 [Nout, K] E4M3FN bytes; 16-byte aligned
+ * w_scale  MX scales of w (Nout rows); 16-byte aligned
+ * kv       uint16 [T, Nout] bf16 bits, out: the hc keys then the value, as engram_wkv;
+ *          16-byte aligned
+ * Limits: T >= 0; K >= 128 and K % 128 == 0; Nout >= 8 and Nout % 8 == 0.
+ */
+int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                  uint16_t* kv, int64_t T, int32_t K, int32_t Nout, void* stream);
 
 /*
  * engram_wkv_gate_layers_noalloc -- engram_wkv_gate_layers without a workspace

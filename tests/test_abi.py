@@ -285,3 +285,21 @@ def test_wkv_gate_layers_noalloc_validation(kw, status, msg):
     assert g.NOALLOC_SCRATCH_BYTES == 16 << 20
     # 2 layers x 4369 tokens fit
     assert 2 * g.lib().engram_wkv_gate_workspace_bytes(4369, 4, 5120) <= g.NOALLOC_SCRATCH_BYTES
+
+
+def test_mx_validation():
+    L = g.lib()
+    assert L.engram_mx_scale_bytes(10, 256) == 2 * 12 * 4
+    assert L.engram_mx_scale_bytes(0, 128) == 0
+    assert L.engram_mx_scale_bytes(10, 192) == -1 and L.engram_mx_scale_bytes(10, 0) == -1
+    assert L.engram_mx_quant(FAKE, 10, 192, FAKE, FAKE, None) == 1 and "K=192" in _err()
+    assert L.engram_mx_quant(FAKE, -1, 128, FAKE, FAKE, None) == 1 and "rows" in _err()
+    assert L.engram_mx_quant(None, 10, 128, FAKE, FAKE, None) == 1 and "null" in _err()
+    assert L.engram_mx_quant(ctypes.c_void_p(0x100008), 10, 128, FAKE, FAKE, None) == 1 and "misaligned" in _err()
+    assert L.engram_mx_quant(None, 0, 128, None, None, None) == 0
+    assert L.engram_wkv_mx(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 64, 256, None) == 1 and "K=64" in _err()
+    assert L.engram_wkv_mx(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 128, 12, None) == 1 and "Nout=12" in _err()
+    assert L.engram_wkv_mx(FAKE, None, FAKE, FAKE, FAKE, 10, 128, 256, None) == 1 and "null" in _err()
+    assert L.engram_wkv_mx(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, 10, 128, 256, None) == 1
+    assert "misaligned" in _err()
+    assert L.engram_wkv_mx(None, None, None, None, None, 0, 128, 256, None) == 0

@@ -1,0 +1,122 @@
+"""The fp8 block-scaled (OCP MX) form of the `wkv` Linear on the GPU (released
+config's "dtype": "fp8", stack-hashes page), against the oracle:
+engram_mx_quant bit for bit (elements and E8M0 scales, in the library's scale
+layout); engram_wkv_mx within the projection's bar on ragged shapes, on
+extreme scales, and at the workloads' shapes on sampled tokens."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_close, bf16_tensor, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _scales_rowmajor(scale_dev, rows, K):
+    """[K/128, rows4, 4] (the library's layout) -> [rows, K/32] (the oracle's)."""
+    s = scale_dev.cpu().numpy().reshape(K // 128, -1, 4)
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(-1, K // 32)[:rows])
+
+
+def _scales_tiled(scale_rowmajor, K, device):
+    import torch
+
+    rows = scale_rowmajor.shape[0]
+    rows4 = (rows + 3) // 4 * 4
+    t = np.zeros((rows4, K // 32), np.uint8)
+    t[:rows] = scale_rowmajor
+    t = np.ascontiguousarray(t.reshape(rows4, K // 128, 4).transpose(1, 0, 2))
+    return torch.from_numpy(t).to(device)
+
+
+def _assert_close_cancelling(kv, a_q, a_s, w_q, w_s, what):
+    """The projection's bar plus an allowance for operands whose products cancel: the fp8 matrix core sums its
+    products more coarsely than IEEE fp32 -- measured on gfx950, |error| <= 2^-13.3 * sum_k |a_k w_k| on uniform
+    E4M3 codes of both signs (2^-19.3 on quantised normal rows), about three times the fp32 recursive-summation
+    bound K * 2^-24 -- so each output may also differ by 2^-12 times the sum of its products' magnitudes."""
+    mag = np.abs(oracle.mx_dequant(a_q, a_s)) @ np.abs(oracle.mx_dequant(w_q, w_s)).T
+    assert_close(oracle.bf16_bits_to_float(bits(kv)), oracle.wkv_mx_matmul(a_q, a_s, w_q, w_s),
+                 atol=1e-3 + 2.0 ** -12 * mag, what=what)
+
+
+def _bf16_rows(rng, rows, K, spread=30):
+    x = rng.normal(size=(rows, K)) * np.exp2(rng.integers(-spread, spread, size=(rows, 1)))
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (5, 256), (257, 1536), (1000, 6144), (3, 384)])
+def test_mx_quant_matches_the_oracle(gpu_device, rows, K):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(rows * 7 + K)
+    x = _bf16_rows(rng, rows, K)
+    if rows >= 3:
+        x[0, :32] = 0.0                       # an all-zero block
+        x[0, 5] = -0.0
+        x[1, 32:64] = 480.0 * 2.0 ** -20      # a saturating block
+        x[1, 40] = -3.0 * 2.0 ** -20
+        x[2, :32] = 2.0 ** -133               # the smallest bf16 subnormal
+        x[2, 64:96] = rng.normal(size=32) * 2.0 ** 120
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    x_bits = xb.view(torch.int16).numpy().view(np.uint16)
+    q, sc = g.engram_mx_quant(xb.to(gpu_device))
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.mx_quant(x_bits)
+    np.testing.assert_array_equal(q.cpu().numpy(), want_q)
+    np.testing.assert_array_equal(_scales_rowmajor(sc, rows, K), want_s)
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 128, 8), (37, 256, 264), (255, 128, 256), (257, 1536, 1280),
+                                   (600, 384, 520), (1000, 1536, 25600), (4173, 1536, 2048), (300, 6144, 512)])
+def test_wkv_mx_matches_the_oracle(gpu_device, T, K, N):
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(T + K * 3 + N * 7)
+    a_bits = bits(torch.from_numpy(_bf16_rows(rng, T, K, spread=4)).to(torch.bfloat16))
+    w_bits = bits(torch.from_numpy((rng.normal(size=(N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16))
+    a_q, a_s = oracle.mx_quant(a_bits)
+    w_q, w_s = oracle.mx_quant(w_bits)
+    kv = g.engram_wkv_mx(torch.from_numpy(a_q).to(gpu_device), _scales_tiled(a_s, K, gpu_device),
+                         torch.from_numpy(w_q).to(gpu_device), _scales_tiled(w_s, K, gpu_device))
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 1000 else np.unique(np.r_[0, 255, 256, T - 1, rng.integers(0, T, 300)])
+    want = oracle.wkv_mx_matmul(a_q[rows], a_s[rows], w_q, w_s)
+    assert_close(oracle.bf16_bits_to_float(bits(kv)[rows]), want, what=f"wkv_mx {T}x{K}x{N}")
+
+
+def test_wkv_mx_extreme_scales_and_the_quantiser_chain(gpu_device):
+    """Scales near both ends of the E8M0 range (products still in fp32 range), and the device quantiser feeding
+    the device projection: equal to the oracle's chain."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(99)
+    T, K, N = 300, 512, 768
+    a_q = rng.integers(0, 0x7E, size=(T, K)).astype(np.uint8) | (rng.integers(0, 2, (T, K)) << 7).astype(np.uint8)
+    w_q = rng.integers(0, 0x7E, size=(N, K)).astype(np.uint8) | (rng.integers(0, 2, (N, K)) << 7).astype(np.uint8)
+    # per block b: every token's scale 2^(c_b - 127) with c_b up to 2^60 away from 1, every weight row's
+    # 2^(254 - c_b + d - 127), |d| <= 8: the operands' scales span 2^-60 .. 2^60, their products 2^-8 .. 2^8
+    c = rng.integers(127 - 60, 127 + 60, size=K // 32)
+    a_s = np.repeat(c[None, :], T, axis=0).astype(np.uint8)
+    w_s = (254 - c[None, :] + rng.integers(-8, 9, size=(N, K // 32))).astype(np.uint8)
+    kv = g.engram_wkv_mx(torch.from_numpy(a_q).to(gpu_device), _scales_tiled(a_s, K, gpu_device),
+                         torch.from_numpy(w_q).to(gpu_device), _scales_tiled(w_s, K, gpu_device))
+    torch.cuda.synchronize()
+    _assert_close_cancelling(kv, a_q, a_s, w_q, w_s, "wkv_mx codes")
+    # the chain: bf16 rows -> device quantiser -> device projection
+    x = torch.from_numpy(_bf16_rows(rng, T, K, spread=10)).to(torch.bfloat16)
+    wb = torch.from_numpy((rng.normal(size=(N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    aq, asc = g.engram_mx_quant(x.to(gpu_device))
+    wq, wsc = g.engram_mx_quant(wb.to(gpu_device))
+    kv = g.engram_wkv_mx(aq, asc, wq, wsc)
+    torch.cuda.synchronize()
+    oa_q, oa_s = oracle.mx_quant(bits(x))
+    ow_q, ow_s = oracle.mx_quant(bits(wb))
+    np.testing.assert_array_equal(aq.cpu().numpy(), oa_q)
+    np.testing.assert_array_equal(_scales_rowmajor(asc, T, K), oa_s)
+    _assert_close_cancelling(kv, oa_q, oa_s, ow_q, ow_s, "chain")
