@@ -18,8 +18,8 @@ import dataclasses
 from typing import List, Optional
 
 from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
-               engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_wkv, engram_wkv_gate,
-               engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes)
+               engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_mx_quant, engram_wkv,
+               engram_wkv_gate, engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes, engram_wkv_mx)
 
 
 @dataclasses.dataclass
@@ -47,6 +47,8 @@ class LayerWeights:
     block_size: int
     row_start: int = 0
     packed: "Optional[torch.Tensor]" = None  # uint8 [R, 2*D]: the same table as one record per row (engram_pack_table)
+    # the wkv weight in the fp8 block-scaled (OCP MX) form: (E4M3 bytes [Nout, K], E8M0 scales), for fp8=True
+    wkv_mx: "Optional[tuple]" = None
 
 
 class EngramForward:
@@ -137,6 +139,30 @@ class EngramForward:
                 hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
         return a
 
+    def layer_fp8(self, e: int, hash_ids, x, events=None, packed=False, a=None):
+        """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e with the fp8 block-scaled projection:
+        the gathered rows quantised to MX fp8 (engram_mx_quant), engram_wkv_mx against the layer's MX weights,
+        then engram_gate_dot."""
+        import torch
+
+        lw = self.layers[e]
+        if lw.wkv_mx is None:
+            raise ValueError(f"layer {e} has no fp8 (MX) projection weights")
+        T = hash_ids.shape[0] * hash_ids.shape[1]
+        dev = hash_ids.device
+        if a is None:
+            a = self.gather(e, hash_ids, events, packed)
+        K = a.numel() // T
+        aq = self._buf(("a_mx", e), (T, K), torch.uint8, dev)
+        asc = self._buf(("a_mx_scale", e), (K // 128, (T + 3) // 4 * 4, 4), torch.uint8, dev)
+        self._timed(events, "mx_quant", lambda: engram_mx_quant(a.view(T, K), q=aq, scale=asc))
+        kv = self._buf(("kv", e), (T, lw.wkv.shape[0]), torch.bfloat16, dev)
+        self._timed(events, "wkv_mx", lambda: engram_wkv_mx(aq, asc, lw.wkv_mx[0], lw.wkv_mx[1], out=kv))
+        x3 = x.reshape(T, x.shape[-2], x.shape[-1])
+        dot = self._buf(("dot", e), (T, x3.shape[1]), torch.float32, dev)
+        self._timed(events, "gate_dot", lambda: engram_gate_dot(x3, kv, lw.q_weight, lw.k_weight, self.eps, out=dot))
+        return a, kv, dot
+
     def layer(self, e: int, hash_ids, x, events=None, token_mask=None, output=False, fused=False, packed=False,
               a=None):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e for x [T, hc, dim]
@@ -179,18 +205,23 @@ class EngramForward:
         return a, kv, dot
 
     def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False,
-             packed=False, hash_gather=False, all_layers=False):
+             packed=False, hash_gather=False, all_layers=False, fp8=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
         (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
         With `hash_gather`, the hash and every layer's packed gather are one launch; with `all_layers`
         (fused only), every layer's projection and gate pre-activation are one launch (their tiles share
-        the CUs).
+        the CUs); with `fp8`, the projection is the fp8 block-scaled form (layer_fp8; pre-activations only).
         `events`: optional dict that collects (start, end) timing events per entry point."""
         if hash_gather:
             ids, rows = self.hash_gather(input_ids, start_pos, token_mask, events)
         else:
             ids, rows = self.hash(input_ids, start_pos, token_mask, events), [None] * self.E
+        if fp8:
+            if output or fused or all_layers:
+                raise ValueError("the fp8 projection runs unfused, up to the pre-activation")
+            return [self.layer_fp8(e, ids, xs[e] if isinstance(xs, (list, tuple)) else xs, events, packed,
+                                   rows[e])[-1] for e in range(self.E)]
         if all_layers:
             if not fused:
                 raise ValueError("all_layers needs the fused projection")

@@ -32,11 +32,13 @@ class Workload:
 
 
 def build(cfg: EngramConfig, device="cuda", x_steps: int = 1, full_range: bool = False,
-          n_layers: Optional[int] = None, packed: bool = False) -> Workload:
-    """`packed`: also give every layer its table in the packed layout (engram_pack_table)."""
+          n_layers: Optional[int] = None, packed: bool = False, fp8: bool = False) -> Workload:
+    """`packed`: also give every layer its table in the packed layout (engram_pack_table); `fp8`: also its wkv
+    weight in the fp8 block-scaled form (engram_mx_quant of the bf16 weight: the stand-in for released fp8
+    weights)."""
     import torch
 
-    from gram_hash_embedding_amd import engram_pack_table
+    from gram_hash_embedding_amd import engram_mx_quant, engram_pack_table
     from gram_hash_embedding_amd.forward import EngramForward, HashState, LayerWeights
 
     hi = hash_inputs(cfg, full_range_multipliers=full_range)
@@ -56,8 +58,10 @@ def build(cfg: EngramConfig, device="cuda", x_steps: int = 1, full_range: bool =
         w, s = synth_device.device_table(table_seed(cfg, e), rows[e], cfg.head_dim, cfg.block_size, device)
         q, k = qk_weights(cfg, e, device=device)
         pk = engram_pack_table(w, s, cfg.block_size) if packed else None
-        layers.append(LayerWeights(weight=w, scale=s, wkv=wkv_weight(cfg, e, device=device), q_weight=q,
-                                   k_weight=k, block_size=cfg.block_size, packed=pk))
+        wkv = wkv_weight(cfg, e, device=device)
+        wmx = engram_mx_quant(wkv) if fp8 and cfg.K % 128 == 0 else None
+        layers.append(LayerWeights(weight=w, scale=s, wkv=wkv, q_weight=q, k_weight=k, block_size=cfg.block_size,
+                                   packed=pk, wkv_mx=wmx))
     fwd = EngramForward(state, layers, cfg.eps)
     ids = torch.from_numpy(hi.input_ids).to(device)
     mask = None if hi.token_mask is None else torch.from_numpy(hi.token_mask).to(device)
