@@ -46,6 +46,7 @@ def lib():
         L.oracle_wkv.argtypes = [p, p, p, i64, i32, i32]
         L.oracle_gate_dot.argtypes = [p, p, i64, p, p, ctypes.c_double, p, i64, i32, i32]
         L.oracle_gate_output.argtypes = [p, p, i64, p, p, p, p, i64, i32, i32]
+        L.oracle_gather_dequant_fmt.argtypes = [p, i32, i64, i64, i32, p, p, i32, i64, i64, i32, i32, p, p, p]
         L.oracle_mx_quant.argtypes = [p, i64, i32, i32, p, p]
         L.oracle_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, i32]
         L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
@@ -60,7 +61,7 @@ def lib():
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.oracle_set_num_threads.restype = None
         for f in (L.oracle_hash, L.oracle_gather_dequant, L.oracle_wkv, L.oracle_gate_dot, L.oracle_gate_output,
-                  L.oracle_mx_quant, L.oracle_wkv_mx):
+                  L.oracle_mx_quant, L.oracle_wkv_mx, L.oracle_gather_dequant_fmt):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -120,6 +121,32 @@ def gather_dequant(hash_ids, weight, scale, row_start=0, block_size=32, n_cols=N
     rc = lib().oracle_gather_dequant(_ptr(ids), T, stride, C, _ptr(w), _ptr(s), R, row_start, D, block_size,
                                      _ptr(out), _ptr(raw), _ptr(rsc))
     _check(rc, "oracle_gather_dequant")
+    return (out, raw, rsc) if want_raw else out
+
+
+SCALE_FORMATS = {"fp32": 0, "e8m0": 1, "e4m3": 2}
+
+
+def gather_dequant_fmt(hash_ids, weight, scale, scale_format="fp32", row_start=0, block_size=32, n_cols=None,
+                       want_raw=False):
+    """gather_dequant with the block scales as float32 (`scale` float32 [R, D/blk]) or one-byte E8M0 / E4M3
+    (`scale` uint8 [R, D/blk]), and int64 or int32 ids [T, stride] -> bf16 bits uint16 [T, C, D] (and, with
+    want_raw, the gathered bytes and the gathered scale elements as stored)."""
+    ids = np.ascontiguousarray(hash_ids)
+    if ids.dtype not in (np.int64, np.int32):
+        raise ValueError("ids must be int64 or int32")
+    T, stride = ids.shape
+    C = stride if n_cols is None else n_cols
+    fmt = SCALE_FORMATS[scale_format]
+    w = _c(weight, np.uint8)
+    s = _c(scale, np.float32 if fmt == 0 else np.uint8)
+    R, D = w.shape
+    out = np.empty((T, C, D), dtype=np.uint16)
+    raw = np.empty((T, C, D), dtype=np.uint8) if want_raw else None
+    rsc = np.empty((T, C, D // block_size), dtype=s.dtype) if want_raw else None
+    rc = lib().oracle_gather_dequant_fmt(_ptr(ids), ids.dtype.itemsize, T, stride, C, _ptr(w), _ptr(s), fmt, R,
+                                         row_start, D, block_size, _ptr(out), _ptr(raw), _ptr(rsc))
+    _check(rc, "oracle_gather_dequant_fmt")
     return (out, raw, rsc) if want_raw else out
 
 

@@ -170,6 +170,51 @@ int oracle_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_s
     return ORACLE_OK;
 }
 
+/* The same gather and dequant with the table's block scales in one of the formats `scale_dtype` may name
+ * (the stack-hashes page leaves it open): 0 = float32, 1 = E8M0 (one byte, 2^(s-127), 0xFF NaN), 2 =
+ * float8_e4m3fn (one byte); `scales.float()` is the decoded value, and the dequant is again the fp32
+ * product, then bf16.  Ids are int64 (id_bytes 8) or int32 (id_bytes 4).  out_scale (optional) receives
+ * the gathered scale elements as stored (4 or 1 bytes each). */
+int oracle_gather_dequant_fmt(const void* hash_ids, int id_bytes, int64_t T, int64_t id_token_stride, int C,
+                              const uint8_t* weight, const void* scale, int scale_format, int64_t R,
+                              int64_t row_start, int D, int blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                              void* out_scale) {
+    if (T < 0 || C < 1 || D < 1 || blk < 1 || D % blk != 0 || R < 1) return ORACLE_EINVAL;
+    if ((id_bytes != 4 && id_bytes != 8) || scale_format < 0 || scale_format > 2) return ORACLE_EINVAL;
+    const int S = D / blk;
+    const int sbytes = scale_format == 0 ? 4 : 1;
+    const int64_t vocab_end = row_start + R;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int c = 0; c < C; ++c) {
+            const int64_t at = t * id_token_stride + c;
+            const int64_t idx = id_bytes == 8 ? ((const int64_t*)hash_ids)[at] : (int64_t)((const int32_t*)hash_ids)[at];
+            const int masked = idx < row_start || idx >= vocab_end;
+            const int64_t local = masked ? 0 : idx - row_start;
+            const uint8_t* w = weight + local * D;
+            const int64_t o = (t * C + c);
+            for (int j = 0; j < D; ++j) {
+                const int64_t si = local * S + j / blk;
+                float sv;
+                if (scale_format == 0)
+                    sv = ((const float*)scale)[si];
+                else if (scale_format == 1)
+                    sv = (float)oracle_e8m0_decode(((const uint8_t*)scale)[si]);
+                else
+                    sv = oracle_e4m3fn_decode(((const uint8_t*)scale)[si]);
+                /* fp32 product (one rounding) then bf16 (a second rounding) */
+                const float prod = oracle_e4m3fn_decode(w[j]) * sv;
+                out_bf16[o * D + j] = masked ? (uint16_t)0 : oracle_bf16_rne(prod);
+                if (out_fp8) out_fp8[o * D + j] = w[j];
+            }
+            if (out_scale)
+                memcpy((uint8_t*)out_scale + o * S * sbytes, (const uint8_t*)scale + local * S * sbytes,
+                       (size_t)(S * sbytes));
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* step 4: wkv projection                                                    */
 /* ------------------------------------------------------------------------ */

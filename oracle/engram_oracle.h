@@ -33,6 +33,14 @@ int oracle_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_s
                           const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
                           int D, int blk, uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale);
 
+/* The same with the block scales as float32 (scale_format 0), E8M0 (1) or
+ * float8_e4m3fn (2) bytes, and int64 (id_bytes 8) or int32 (4) ids; out_scale
+ * receives the gathered scale elements as stored. */
+int oracle_gather_dequant_fmt(const void* hash_ids, int id_bytes, int64_t T, int64_t id_token_stride, int C,
+                              const uint8_t* weight, const void* scale, int scale_format, int64_t R,
+                              int64_t row_start, int D, int blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                              void* out_scale);
+
 /* wkv: kv[t,o] = sum_k a[t,k] w[o,k] in double (a [T,K], w [Nout,K] bf16 bits). */
 int oracle_wkv(const uint16_t* a, const uint16_t* w, double* kv, int64_t T, int K, int Nout);
 

@@ -95,6 +95,15 @@ static void drive_gather(void) {
     EXPECT(oracle_gather_dequant(ids, T, STRIDE, C, w, sc, R, 10, D, BLK, out, NULL, NULL) == 0);
     EXPECT(oracle_gather_dequant(ids, 0, STRIDE, C, w, sc, R, 0, D, BLK, out, NULL, NULL) == 0);
     EXPECT(oracle_gather_dequant(ids, T, STRIDE, C, w, sc, R, 0, D, 24, out, NULL, NULL) == ORACLE_EINVAL);
+    /* the one-byte scale formats and int32 ids */
+    uint8_t sc8[R * (D / 16)], rsc8[T * C * (D / 16)];
+    int32_t ids32[T * STRIDE];
+    for (int i = 0; i < R * (D / 16); ++i) sc8[i] = (uint8_t)next_u64();
+    for (int i = 0; i < T * STRIDE; ++i) ids32[i] = (int32_t)(ids[i] > INT32_MAX || ids[i] < INT32_MIN ? -1 : ids[i]);
+    EXPECT(oracle_gather_dequant_fmt(ids32, 4, T, STRIDE, C, w, sc8, 1, R, 10, D, 32, out, raw, rsc8) == 0);
+    EXPECT(oracle_gather_dequant_fmt(ids, 8, T, STRIDE, C, w, sc8, 2, R, 10, D, 16, out, raw, rsc8) == 0);
+    EXPECT(oracle_gather_dequant_fmt(ids, 8, T, STRIDE, C, w, sc, 0, R, 10, D, 32, out, raw, rsc) == 0);
+    EXPECT(oracle_gather_dequant_fmt(ids, 2, T, STRIDE, C, w, sc, 0, R, 10, D, 32, out, raw, rsc) == ORACLE_EINVAL);
     for (int b = 0; b < 256; ++b) {
         const float v = oracle_e4m3fn_decode((uint8_t)b);
         EXPECT(isnan(v) == ((b & 0x7F) == 0x7F));

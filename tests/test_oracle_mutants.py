@@ -17,9 +17,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "engram_oracle.c")
 
-HASH, DEQ, WKV_GATE, OUT, MX = ("tests/test_oracle_hash.py", "tests/test_oracle_dequant.py",
-                                "tests/test_oracle_wkv_gate.py", "tests/test_oracle_gate_output.py",
-                                "tests/test_oracle_mx.py")
+HASH, DEQ, WKV_GATE, OUT, MX, FMT = ("tests/test_oracle_hash.py", "tests/test_oracle_dequant.py",
+                                     "tests/test_oracle_wkv_gate.py", "tests/test_oracle_gate_output.py",
+                                     "tests/test_oracle_mx.py", "tests/test_oracle_scale_formats.py")
 
 # name -> (text in the oracle, planted replacement, pin file that must fail)
 MUTANTS = {
@@ -61,6 +61,13 @@ MUTANTS = {
                         "oracle_e4m3fn_encode_sat(ldexp(fabs(oracle_bf16_to_double(xb[k])), -shared))", MX),
     "mx_subnormal_quantum": ("const int n = (int)round_half_even(m / ldexp(1.0, -9));",
                              "const int n = (int)round_half_even(m / ldexp(1.0, -8));", MX),
+    "fmt_e4m3_scale_read_as_e8m0": ("sv = oracle_e4m3fn_decode(((const uint8_t*)scale)[si]);",
+                                    "sv = (float)oracle_e8m0_decode(((const uint8_t*)scale)[si]);", FMT),
+    "fmt_int32_ids_as_int16": ("(int64_t)((const int32_t*)hash_ids)[at]", "(int64_t)((const int16_t*)hash_ids)[at]",
+                               FMT),
+    "fmt_scale_in_double": ("const float prod = oracle_e4m3fn_decode(w[j]) * sv;",
+                            "const float prod = (float)((double)oracle_e4m3fn_decode(w[j]) * (double)sv + 0x1p-40);",
+                            FMT),
     "wkv_mx_first_block_scale": ("acc += oracle_e8m0_decode(a_s[t * nb + b])", "acc += oracle_e8m0_decode(a_s[t * nb])",
                                  MX),
 }
