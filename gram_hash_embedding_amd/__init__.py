@@ -10,6 +10,7 @@ an exception is raised.
     engram_hash            -- n-gram hash ids (+ compressed-id cache update)
     engram_hash_gather_packed -- engram_hash and every layer's packed gather + dequant in one launch
     engram_gather_dequant  -- fp8 row gather + block-scale dequant -> bf16
+    engram_gather_dequant_fmt -- the same with E8M0 / E4M3 block scales and int32 or int64 ids
     engram_pack_table      -- the table's rows and scales in one record per row (one-off layout conversion)
     engram_gather_dequant_packed -- engram_gather_dequant on a packed table (same output, fewer lines fetched)
     engram_wkv             -- kv = A @ W^T on bf16 matrix cores
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, p, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         L.engram_hash.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p, p]
+        L.engram_hash_i32.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32, i64, i64, p, p]
+        L.engram_gather_dequant_fmt.argtypes = [p, i32, i64, i64, i32, p, p, i32, i64, i64, i32, i32, p, p, p, p]
         L.engram_hash_gather_packed.argtypes = [p, i64, i64, i64, p, p, i64, p, i64, i64, p, p, p, i32, i32, i32,
                                                 i64, i64, p, p, p, p, i32, i32, p, p]
         L.engram_gather_dequant.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p, p]
@@ -69,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.engram_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
-        for f in (L.engram_hash, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
+        for f in (L.engram_hash, L.engram_hash_i32, L.engram_gather_dequant_fmt, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
                   L.engram_wkv_gate_layers, L.engram_wkv_gate_layers_noalloc, L.engram_mx_quant, L.engram_wkv_mx,
                   L.engram_abi_version):
@@ -111,16 +114,18 @@ def _dev(t, name, dtype, ndim=None):
 
 
 def engram_hash(input_ids, start_pos, token_mask, token_map, cache, multipliers, primes, offsets, pad_id,
-                dead=-1, out=None, stream=None):
-    """Hash ids int64 [B, L, E, (N-1)*H]; `cache` (int64 [cache_B, cache_L]) is updated in place."""
+                dead=-1, out=None, stream=None, int32_ids=False):
+    """Hash ids int64 [B, L, E, (N-1)*H] (int32 with `int32_ids`: engram_hash_i32, ids outside [0, 2^31) as -1);
+    `cache` (int64 [cache_B, cache_L]) is updated in place."""
     import torch
 
     B, L = input_ids.shape
     E, N = multipliers.shape
     H = primes.shape[2]
     C = (N - 1) * H
+    id_dtype = torch.int32 if int32_ids else torch.int64
     if out is None:
-        out = torch.empty((B, L, E, C), dtype=torch.int64, device=input_ids.device)
+        out = torch.empty((B, L, E, C), dtype=id_dtype, device=input_ids.device)
     if tuple(out.shape) != (B, L, E, C):
         raise ValueError("out has the wrong shape")
     if tuple(primes.shape) != (E, N - 1, H) or tuple(offsets.shape) != (E, C):
@@ -132,13 +137,14 @@ def engram_hash(input_ids, start_pos, token_mask, token_map, cache, multipliers,
         if token_mask.dtype == torch.bool:
             token_mask = token_mask.view(torch.uint8)
         mask_p = _dev(token_mask, "token_mask", torch.uint8, 2)
-    _check(lib().engram_hash(
+    fn = lib().engram_hash_i32 if int32_ids else lib().engram_hash
+    _check(fn(
         _dev(input_ids, "input_ids", torch.int64, 2), B, L, int(start_pos), mask_p,
         _dev(token_map, "token_map", torch.int64, 1), token_map.numel(),
         _dev(cache, "cache", torch.int64, 2), cache.shape[0], cache.shape[1],
         _dev(multipliers, "multipliers", torch.int64, 2), _dev(primes, "primes", torch.int64, 3),
         _dev(offsets, "offsets", torch.int64, 2), E, N, H, int(pad_id), int(dead),
-        _dev(out, "out", torch.int64, 4), _stream(stream)))
+        _dev(out, "out", id_dtype, 4), _stream(stream)))
     return out
 
 
@@ -206,9 +212,9 @@ def _gather_ids(hash_ids, n_cols, layer):
         raise ValueError("hash_ids must be [B, L, E, C] or [T, C]")
     if n_cols is not None:
         C = n_cols
-    if not hash_ids.is_contiguous() or hash_ids.dtype != torch.int64 or not hash_ids.is_cuda:
-        raise ValueError("hash_ids must be a contiguous int64 GPU tensor")
-    return T, C, stride, ctypes.c_void_p(hash_ids.data_ptr() + 8 * base)
+    if not hash_ids.is_contiguous() or hash_ids.dtype not in (torch.int64, torch.int32) or not hash_ids.is_cuda:
+        raise ValueError("hash_ids must be a contiguous int64 (or int32) GPU tensor")
+    return T, C, stride, ctypes.c_void_p(hash_ids.data_ptr() + hash_ids.element_size() * base)
 
 
 def _raw_outputs(out_fp8, out_scale, T, C, D, block_size):
@@ -289,6 +295,45 @@ def engram_gather_dequant(hash_ids, weight, scale, block_size=32, row_start=0, n
     _check(lib().engram_gather_dequant(
         ids_ptr, T, stride, C, _dev(weight, "weight", torch.uint8, 2), _dev(scale, "scale", torch.float32, 2),
         R, int(row_start), D, int(block_size), _dev(out, "out", torch.bfloat16), p8, ps, _stream(stream)))
+    return out
+
+
+SCALE_FORMATS = {"fp32": 0, "e8m0": 1, "e4m3": 2}
+
+
+def engram_gather_dequant_fmt(hash_ids, weight, scale, scale_format="fp32", block_size=32, row_start=0, n_cols=None,
+                              layer=0, out=None, out_fp8=None, out_scale=None, stream=None):
+    """engram_gather_dequant with int64 or int32 ids and the block scales as float32 (`scale` float32 [R, D/blk])
+    or one-byte E8M0 / float8_e4m3fn (`scale` uint8, float8_e8m0fnu or float8_e4m3fn [R, D/blk])."""
+    import torch
+
+    fmt = SCALE_FORMATS[scale_format]
+    T, C, stride, ids_ptr = _gather_ids(hash_ids, n_cols, layer)
+    if weight.dtype == torch.float8_e4m3fn:
+        weight = weight.view(torch.uint8)
+    if scale.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        scale = scale.view(torch.uint8)
+    R, D = weight.shape
+    if tuple(scale.shape) != (R, D // block_size):
+        raise ValueError("scale must be [R, D/block_size]")
+    sdt = torch.float32 if fmt == 0 else torch.uint8
+    if out is None:
+        out = torch.empty((T, C, D), dtype=torch.bfloat16, device=hash_ids.device)
+    if out.numel() != T * C * D:
+        raise ValueError("out has the wrong size")
+    p8 = ps = None
+    if out_fp8 is not None:
+        if out_fp8.numel() != T * C * D:
+            raise ValueError("out_fp8 must hold T*C*D bytes")
+        p8 = _dev(out_fp8, "out_fp8", torch.uint8)
+    if out_scale is not None:
+        if out_scale.numel() != T * C * (D // block_size):
+            raise ValueError("out_scale must hold T*C*(D/block_size) elements")
+        ps = _dev(out_scale, "out_scale", sdt)
+    _check(lib().engram_gather_dequant_fmt(
+        ids_ptr, hash_ids.element_size(), T, stride, C, _dev(weight, "weight", torch.uint8, 2),
+        _dev(scale, "scale", sdt, 2), fmt, R, int(row_start), D, int(block_size), _dev(out, "out", torch.bfloat16),
+        p8, ps, _stream(stream)))
     return out
 
 
@@ -570,6 +615,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
            "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_layers_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "engram_wkv_gate_workspace_bytes", "engram_mx_quant", "engram_wkv_mx", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate_workspace_bytes", "engram_gather_dequant_fmt", "SCALE_FORMATS", "engram_mx_quant", "engram_wkv_mx", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

@@ -35,20 +35,33 @@ namespace {
 constexpr int kThreads = 256;
 
 struct GatherArgs {
-    const int64_t* ids;
+    const void* ids;        // int64 (or, with IdT = int32_t, int32) [T, stride]
     int64_t stride;
     int64_t W;  // rows to produce = T * C
     int C;
     const uint8_t* weight;  // [R, D] fp8, or the packed table [R, 2D]
-    const float* scale;     // [R, D/blk] fp32 (unused for a packed table)
+    const void* scale;      // [R, D/blk]: fp32, or one-byte E8M0 / E4M3 (unused for a packed table)
     int64_t R, row_start;
     int blk;
     uint16_t* out;
     uint8_t* out_fp8;
-    float* out_scale;
+    void* out_scale;        // the gathered scale elements as stored, or null
 };
 
-template <int D, int U, bool kPacked>
+// Block scale formats of the table: 32-bit float, E8M0 (2^(s-127); 0xFF NaN) and float8_e4m3fn.
+constexpr int kScaleF32 = 0, kScaleE8M0 = 1, kScaleE4M3 = 2;
+
+// One-byte scale -> fp32 (exact): E8M0 as the exponent field (0 is the fp32 subnormal 2^-127), E4M3 through
+// the fp8 convert (OCP E4M3FN on gfx950).
+template <int SF>
+__device__ inline float decode_scale(uint32_t s) {
+    if constexpr (SF == kScaleE8M0)
+        return __uint_as_float(s == 0 ? 0x00400000u : (s == 0xFFu ? 0x7FC00000u : s << 23));
+    else
+        return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(s), 0);
+}
+
+template <int D, int U, bool kPacked, int SF = kScaleF32, typename IdT = int64_t>
 __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) {
     constexpr int LPR = D / 16;              // lanes per row
     constexpr int RPS = kThreads / LPR;      // rows per step of the block
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
                 t = w / a.C;
                 c = w - t * a.C;
             }
-            id = __builtin_nontemporal_load(a.ids + t * a.stride + c);
+            id = __builtin_nontemporal_load(static_cast<const IdT*>(a.ids) + t * a.stride + c);
         }
         const int64_t local = id - a.row_start;
         ok[u] = live[u] && local >= 0 && local < a.R;
@@ -85,6 +98,7 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
 
     u32x4 v[U];
     float sc[U];
+    uint32_t sraw[U];  // the stored scale element
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (kPacked) {
@@ -93,7 +107,12 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
             sc[u] = reinterpret_cast<const float*>(rec + D)[sidx];
         } else {
             v[u] = *reinterpret_cast<const u32x4*>(a.weight + row[u] * D + lane_in_row * 16);
-            sc[u] = a.scale[row[u] * S + sidx];
+            if constexpr (SF == kScaleF32) {
+                sc[u] = static_cast<const float*>(a.scale)[row[u] * S + sidx];
+            } else {
+                sraw[u] = static_cast<const uint8_t*>(a.scale)[row[u] * S + sidx];
+                sc[u] = decode_scale<SF>(sraw[u]);
+            }
         }
     }
 
@@ -112,19 +131,35 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
         __builtin_nontemporal_store(o0, dst);
         __builtin_nontemporal_store(o1, dst + 1);
         if (a.out_fp8) *reinterpret_cast<u32x4*>(a.out_fp8 + w * D + lane_in_row * 16) = v[u];
-        if (a.out_scale && (lane_in_row * 16) % a.blk == 0) a.out_scale[w * S + sidx] = sc[u];
+        if (a.out_scale && (lane_in_row * 16) % a.blk == 0) {
+            if constexpr (SF == kScaleF32)
+                static_cast<float*>(a.out_scale)[w * S + sidx] = sc[u];
+            else
+                static_cast<uint8_t*>(a.out_scale)[w * S + sidx] = static_cast<uint8_t>(sraw[u]);
+        }
     }
 }
 
-template <int D, bool kPacked>
-int launch(const GatherArgs& a, hipStream_t stream) {
+template <int D, bool kPacked, int SF = kScaleF32, typename IdT = int64_t>
+int launch(const GatherArgs& a, hipStream_t stream, const char* name) {
     constexpr int U = 1;
     constexpr int rows_per_block = (kThreads / (D / 16)) * U;
     const int64_t blocks = (a.W + rows_per_block - 1) / rows_per_block;
-    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "engram_gather_dequant: too many rows");
-    hipLaunchKernelGGL((gather_dequant_kernel<D, U, kPacked>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
-    return check_launch(kPacked ? "engram_gather_dequant_packed" : "engram_gather_dequant");
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many rows", name);
+    hipLaunchKernelGGL((gather_dequant_kernel<D, U, kPacked, SF, IdT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
+    return check_launch(name);
+}
+
+// the two-tensor gather for a scale format and id type (D dispatched here)
+template <int SF, typename IdT>
+int launch_fmt(const GatherArgs& a, int D, hipStream_t s, const char* name) {
+    switch (D) {
+        case 32: return launch<32, false, SF, IdT>(a, s, name);
+        case 64: return launch<64, false, SF, IdT>(a, s, name);
+        case 128: return launch<128, false, SF, IdT>(a, s, name);
+        default: return launch<256, false, SF, IdT>(a, s, name);
+    }
 }
 
 // One thread per 16-byte piece of the packed table: pieces [0, D/16) of a record are the row, the rest its
@@ -157,9 +192,11 @@ __global__ __launch_bounds__(kThreads) void pack_table_kernel(const uint8_t* wei
 using namespace engram;
 
 namespace {
-int gather_entry(const char* name, bool packed, const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
-                 const uint8_t* weight, const float* scale, int64_t R, int64_t row_start, int32_t D, int32_t blk,
-                 uint16_t* out_bf16, uint8_t* out_fp8, float* out_scale, void* stream) {
+// scale_format: 0 fp32, 1 E8M0, 2 E4M3 (two-tensor tables only); id_bytes 8 or 4
+int gather_entry(const char* name, bool packed, const void* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                 const uint8_t* weight, const void* scale, int64_t R, int64_t row_start, int32_t D, int32_t blk,
+                 uint16_t* out_bf16, uint8_t* out_fp8, void* out_scale, void* stream, int scale_format = 0,
+                 int id_bytes = 8) {
     if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", name);
     if (C < 1 || C > 1024) return fail(ENGRAM_EINVAL, "%s: C=%d outside [1, 1024]", name, C);
     if (id_token_stride < C) return fail(ENGRAM_EINVAL, "%s: id_token_stride < C", name);
@@ -170,8 +207,9 @@ int gather_entry(const char* name, bool packed, const int64_t* hash_ids, int64_t
     if (R < 1) return fail(ENGRAM_EINVAL, "%s: R < 1", name);
     if (T == 0) return ENGRAM_OK;
     if (!hash_ids || !weight || (!packed && !scale) || !out_bf16) return fail(ENGRAM_EINVAL, "%s: null pointer", name);
-    if (!aligned(hash_ids, 8) || !aligned(weight, packed ? 2 * D : 16) || (!packed && !aligned(scale, 4)) ||
-        !aligned(out_bf16, 16) || (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, 4)))
+    const int sbytes = scale_format == 0 ? 4 : 1;
+    if (!aligned(hash_ids, id_bytes) || !aligned(weight, packed ? 2 * D : 16) || (!packed && !aligned(scale, sbytes)) ||
+        !aligned(out_bf16, 16) || (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, sbytes)))
         return fail(ENGRAM_EINVAL, "%s: misaligned pointer", name);
 
     GatherArgs a;
@@ -188,12 +226,22 @@ int gather_entry(const char* name, bool packed, const int64_t* hash_ids, int64_t
     a.out_fp8 = out_fp8;
     a.out_scale = out_scale;
     hipStream_t s = as_stream(stream);
-    switch (D) {
-        case 32: return packed ? launch<32, true>(a, s) : launch<32, false>(a, s);
-        case 64: return packed ? launch<64, true>(a, s) : launch<64, false>(a, s);
-        case 128: return packed ? launch<128, true>(a, s) : launch<128, false>(a, s);
-        default: return packed ? launch<256, true>(a, s) : launch<256, false>(a, s);
+    if (packed) {
+        switch (D) {
+            case 32: return launch<32, true>(a, s, name);
+            case 64: return launch<64, true>(a, s, name);
+            case 128: return launch<128, true>(a, s, name);
+            default: return launch<256, true>(a, s, name);
+        }
     }
+    if (id_bytes == 4) {
+        if (scale_format == kScaleE8M0) return launch_fmt<kScaleE8M0, int32_t>(a, D, s, name);
+        if (scale_format == kScaleE4M3) return launch_fmt<kScaleE4M3, int32_t>(a, D, s, name);
+        return launch_fmt<kScaleF32, int32_t>(a, D, s, name);
+    }
+    if (scale_format == kScaleE8M0) return launch_fmt<kScaleE8M0, int64_t>(a, D, s, name);
+    if (scale_format == kScaleE4M3) return launch_fmt<kScaleE4M3, int64_t>(a, D, s, name);
+    return launch_fmt<kScaleF32, int64_t>(a, D, s, name);
 }
 }  // namespace
 
@@ -203,6 +251,18 @@ extern "C" int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t
                                      float* out_scale, void* stream) {
     return gather_entry("engram_gather_dequant", false, hash_ids, T, id_token_stride, C, weight, scale, R, row_start,
                         D, blk, out_bf16, out_fp8, out_scale, stream);
+}
+
+extern "C" int engram_gather_dequant_fmt(const void* hash_ids, int32_t id_bytes, int64_t T, int64_t id_token_stride,
+                                         int32_t C, const uint8_t* weight, const void* scale, int32_t scale_format,
+                                         int64_t R, int64_t row_start, int32_t D, int32_t blk, uint16_t* out_bf16,
+                                         uint8_t* out_fp8, void* out_scale, void* stream) {
+    const char* name = "engram_gather_dequant_fmt";
+    if (id_bytes != 4 && id_bytes != 8) return fail(ENGRAM_EINVAL, "%s: id_bytes=%d not 4 or 8", name, id_bytes);
+    if (scale_format < kScaleF32 || scale_format > kScaleE4M3)
+        return fail(ENGRAM_EINVAL, "%s: scale_format=%d not 0 (fp32), 1 (E8M0) or 2 (E4M3)", name, scale_format);
+    return gather_entry(name, false, hash_ids, T, id_token_stride, C, weight, scale, R, row_start, D, blk, out_bf16,
+                        out_fp8, out_scale, stream, scale_format, id_bytes);
 }
 
 extern "C" int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,

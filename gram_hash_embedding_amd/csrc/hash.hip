@@ -63,6 +63,7 @@ struct HashArgs {
     int E, N, H, C;
     int tile;  // tokens per workgroup (a power of two, at most kTileTokens)
     int64_t* out;  // may be null when the rows are gathered
+    int32_t* out32;  // the ids as int32 (ids outside [0, 2^31) stored as -1), or null
 };
 
 // Phase 3 of the fused call: per layer e, its packed table [R, 2D] and its rows [T, C, D] out.
@@ -165,8 +166,10 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a, GatherSide g
     const int total = ntok * EC;
     int64_t* out = a.out != nullptr ? a.out + tile0 * EC : nullptr;
     int64_t* ids = roll + static_cast<int64_t>(a.tile) * a.E * NR;
+    int32_t* out32 = a.out32 != nullptr ? a.out32 + tile0 * EC : nullptr;
     auto put = [&](int idx, int64_t id) {
         if (out != nullptr) out[idx] = id;
+        if (out32 != nullptr) out32[idx] = (id >= 0 && id <= 0x7FFFFFFF) ? static_cast<int32_t>(id) : -1;
         if (D > 0) ids[idx] = id;
     };
     if (EC <= kThreads) {
@@ -263,7 +266,7 @@ int hash_entry(const char* name, const int64_t* input_ids, int64_t B, int64_t L,
                const uint8_t* token_mask, const int64_t* token_map, int64_t vocab, int64_t* cache, int64_t cache_B,
                int64_t cache_L, const int64_t* multipliers, const int64_t* primes, const int64_t* offsets, int32_t E,
                int32_t N, int32_t H, int64_t pad_id, int64_t dead, int64_t* hash_ids, int D, const GatherSide* gs,
-               void* stream) {
+               void* stream, int32_t* hash_ids32 = nullptr) {
     if (B < 0 || L < 0 || start_pos < 0) return fail(ENGRAM_EINVAL, "%s: negative B, L or start_pos", name);
     if (N < 2 || N > kMaxN) return fail(ENGRAM_EINVAL, "%s: N=%d outside [2, %d]", name, N, kMaxN);
     if (E < 1 || E > kMaxE) return fail(ENGRAM_EINVAL, "%s: E=%d outside [1, %d]", name, E, kMaxE);
@@ -276,8 +279,9 @@ int hash_entry(const char* name, const int64_t* input_ids, int64_t B, int64_t L,
                     (long long)(start_pos + L), (long long)cache_B, (long long)cache_L);
     const int64_t T = B * L;
     if (T == 0) return ENGRAM_OK;
-    if (!input_ids || !token_map || !cache || !multipliers || !primes || !offsets || (!hash_ids && !gs))
+    if (!input_ids || !token_map || !cache || !multipliers || !primes || !offsets || (!hash_ids && !hash_ids32 && !gs))
         return fail(ENGRAM_EINVAL, "%s: null required pointer", name);
+    if (!aligned(hash_ids32, 4)) return fail(ENGRAM_EINVAL, "%s: int32 ids not 4-byte aligned", name);
     for (const void* p : {(const void*)input_ids, (const void*)token_map, (const void*)cache,
                           (const void*)multipliers, (const void*)primes, (const void*)offsets,
                           (const void*)hash_ids})
@@ -303,6 +307,7 @@ int hash_entry(const char* name, const int64_t* input_ids, int64_t B, int64_t L,
     a.H = H;
     a.C = (N - 1) * H;
     a.out = hash_ids;
+    a.out32 = hash_ids32;
     // A small call (a 256-token decode step) is spread over the CUs, down to one token per workgroup: its
     // time is the dependent memory round trips plus the id arithmetic, which then runs on many CUs.  With
     // the gather, a tile's ids must also fit the LDS beside the running values (at most 32 KB of ids).
@@ -337,6 +342,18 @@ extern "C" int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64
                            int64_t* hash_ids, void* stream) {
     return hash_entry("engram_hash", input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B,
                       cache_L, multipliers, primes, offsets, E, N, H, pad_id, dead, hash_ids, 0, nullptr, stream);
+}
+
+extern "C" int engram_hash_i32(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                               const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                               int64_t* cache, int64_t cache_B, int64_t cache_L,
+                               const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                               int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                               int32_t* hash_ids, void* stream) {
+    if (B * L > 0 && !hash_ids) return fail(ENGRAM_EINVAL, "engram_hash_i32: null required pointer");
+    return hash_entry("engram_hash_i32", input_ids, B, L, start_pos, token_mask, token_map, vocab, cache, cache_B,
+                      cache_L, multipliers, primes, offsets, E, N, H, pad_id, dead, nullptr, 0, nullptr, stream,
+                      hash_ids);
 }
 
 extern "C" int engram_hash_gather_packed(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,

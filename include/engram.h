@@ -27,6 +27,9 @@
  *   engram_hash_gather_packed
  *                          -- engram_hash and every layer's packed gather in
  *                             one launch
+ *   engram_hash_i32, engram_gather_dequant_fmt
+ *                          -- int32 ids, and the table's block scales as E8M0
+ *                             or float8_e4m3fn bytes
  *   engram_wkv_gate_layers -- engram_wkv_gate for every layer in one launch
  *
  * the fp8 block-scaled (OCP MX) form of the `wkv` Linear:
@@ -118,6 +121,20 @@ int engram_hash(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_po
                 int64_t* hash_ids, void* stream);
 
 /*
+ * engram_hash_i32 -- engram_hash with int32 ids: hash_ids int32 [B, L, E,
+ * (N-1)*H], out, 4-byte aligned; an id outside [0, 2^31) is stored as -1 (so
+ * every gather treats it as outside its rows).  Half the id bytes of
+ * engram_hash for the released tables, whose ids are all below 384,016,682.
+ * Everything else as engram_hash.
+ */
+int engram_hash_i32(const int64_t* input_ids, int64_t B, int64_t L, int64_t start_pos,
+                    const uint8_t* token_mask, const int64_t* token_map, int64_t vocab,
+                    int64_t* cache, int64_t cache_B, int64_t cache_L,
+                    const int64_t* multipliers, const int64_t* primes, const int64_t* offsets,
+                    int32_t E, int32_t N, int32_t H, int64_t pad_id, int64_t dead,
+                    int32_t* hash_ids, void* stream);
+
+/*
  * engram_gather_dequant -- fetch and dequantise the fp8 rows of one layer's
  * hash ids (stack-hashes page: ParallelEngramEmbedding.forward, one rank's
  * rows [row_start, row_start + R)).
@@ -145,6 +162,28 @@ int engram_gather_dequant(const int64_t* hash_ids, int64_t T, int64_t id_token_s
                           const uint8_t* weight, const float* scale, int64_t R, int64_t row_start,
                           int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
                           float* out_scale, void* stream);
+
+/*
+ * engram_gather_dequant_fmt -- engram_gather_dequant with the table's block
+ * scales in another `scale_dtype` (stack-hashes page: ParallelEngramEmbedding's
+ * `scale` and `scales.float()`; the page names the dtype but does not fix it)
+ * and with int32 or int64 ids.  Scale formats: 0 = float32 [R, D/blk] (exactly
+ * engram_gather_dequant); 1 = E8M0 bytes [R, D/blk], scale 2^(s-127) (0xFF NaN),
+ * the pages' indexer format (blocks of 32); 2 = float8_e4m3fn bytes [R, D/blk],
+ * the pages' compressed-KV format (blocks of 16).  The dequant is unchanged: the
+ * decoded scale (exact in fp32) times the decoded fp8 value rounded to fp32,
+ * then to bf16, both to nearest even.
+ *
+ * hash_ids   int64 (id_bytes 8, 8-byte aligned) or int32 (id_bytes 4, 4-byte aligned)
+ *            [T, id_token_stride], first C columns used (engram_hash or engram_hash_i32)
+ * scale      [R, D/blk] elements of the format; float32 4-byte aligned
+ * out_scale  [T, C, D/blk] elements of the format, the gathered scales as stored, or NULL
+ * Other arguments, limits and errors: as engram_gather_dequant.
+ */
+int engram_gather_dequant_fmt(const void* hash_ids, int32_t id_bytes, int64_t T, int64_t id_token_stride,
+                              int32_t C, const uint8_t* weight, const void* scale, int32_t scale_format, int64_t R,
+                              int64_t row_start, int32_t D, int32_t blk, uint16_t* out_bf16, uint8_t* out_fp8,
+                              void* out_scale, void* stream);
 
 /*
  * engram_pack_table -- copy one layer's table (the pages' two tensors: the

@@ -434,6 +434,21 @@ def compact_table(ids: np.ndarray, n_rows: int, seed: int, head_dim: int, block_
     return w, s, remap.reshape(np.shape(ids))
 
 
+def scale_bytes(scale_f32: np.ndarray, fmt: str) -> np.ndarray:
+    """The one-byte block scales of a table whose scales are stored as E8M0 or float8_e4m3fn, as a bit-level
+    function of the seeded float32 scales of the same rows (exponent uniform in {-8..-3}, 23 random mantissa
+    bits): E8M0 keeps the float32 exponent byte (a power of two in [2^-8, 2^-3]); E4M3 takes exponent field
+    (biased exponent - 117), in 2..7, and the top three mantissa bits: the scale times 8 truncated to E4M3
+    (values in [2^-5, 2))."""
+    bits = np.ascontiguousarray(scale_f32, dtype=np.float32).view(np.uint32)
+    e = (bits >> np.uint32(23)) & np.uint32(0xFF)
+    if fmt == "e8m0":
+        return e.astype(np.uint8)
+    if fmt == "e4m3":
+        return (((e - np.uint32(117)) << np.uint32(3)) | ((bits >> np.uint32(20)) & np.uint32(7))).astype(np.uint8)
+    raise ValueError(fmt)
+
+
 def table_rows_alloc(cfg: EngramConfig) -> list:
     return list(cfg.rows_alloc[: cfg.n_layers])
 

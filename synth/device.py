@@ -71,4 +71,17 @@ def device_table(seed: int, rows: int, head_dim: int, block_size: int, device="c
     return w, s
 
 
-__all__ = ["build", "lib", "fill_table", "device_table", "LIB_PATH", "np"]
+def device_scale_bytes(scale_f32, fmt: str):
+    """synth.scale_bytes on a device float32 scale tensor (the same bit-level definition, as torch integer ops)."""
+    import torch
+
+    bits = scale_f32.contiguous().view(torch.int32)
+    e = (bits >> 23) & 0xFF
+    if fmt == "e8m0":
+        return e.to(torch.uint8)
+    if fmt == "e4m3":
+        return (((e - 117) << 3) | ((bits >> 20) & 7)).to(torch.uint8)
+    raise ValueError(fmt)
+
+
+__all__ = ["build", "lib", "fill_table", "device_table", "device_scale_bytes", "LIB_PATH", "np"]

@@ -303,3 +303,24 @@ def test_mx_validation():
     assert L.engram_wkv_mx(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, 10, 128, 256, None) == 1
     assert "misaligned" in _err()
     assert L.engram_wkv_mx(None, None, None, None, None, 0, 128, 256, None) == 0
+
+
+def test_formats_validation():
+    L = g.lib()
+    args = lambda **kw: dict(dict(ids=FAKE, idb=8, T=10, stride=24, C=24, w=FAKE, s=FAKE, fmt=1, R=100, rs=0, D=64,
+                                  blk=32, out=FAKE, o8=None, os=None), **kw)
+    call = lambda a: L.engram_gather_dequant_fmt(a["ids"], a["idb"], a["T"], a["stride"], a["C"], a["w"], a["s"],
+                                                 a["fmt"], a["R"], a["rs"], a["D"], a["blk"], a["out"], a["o8"],
+                                                 a["os"], None)
+    assert call(args(idb=2)) == 1 and "id_bytes" in _err()
+    assert call(args(fmt=3)) == 1 and "scale_format" in _err()
+    assert call(args(blk=24)) == 1 and "blk" in _err()
+    assert call(args(ids=ctypes.c_void_p(0x100004))) == 1 and "misaligned" in _err()  # int64 ids need 8 bytes
+    assert call(args(s=None)) == 1 and "null" in _err()
+    assert call(args(T=0, ids=None, w=None, s=None, out=None)) == 0
+    assert L.engram_hash_i32(FAKE, 1, 64, 0, None, FAKE, 10, FAKE, 1, 64, FAKE, FAKE, FAKE, 1, 4, 2, 2, -1, None,
+                             None) == 1
+    assert "null" in _err()
+    assert L.engram_hash_i32(FAKE, 1, 64, 0, None, FAKE, 10, FAKE, 1, 64, FAKE, FAKE, FAKE, 1, 4, 2, 2, -1,
+                             ctypes.c_void_p(0x100002), None) == 1
+    assert "aligned" in _err()

@@ -78,3 +78,21 @@ def test_configs_are_consistent():
         assert c.head_dim % c.block_size == 0
         assert c.n_out == c.dim * 5 and c.K == c.n_hash_cols * c.head_dim
     assert synth.CONFIGS[3].K == 1536 and synth.CONFIGS[3].n_out == 25600
+
+
+def test_scale_bytes_definition():
+    """The one-byte scale stand-ins: E8M0 is the float32 scale's exponent byte, E4M3 the scale times 8 truncated
+    to three mantissa bits (a normal code in [2^-5, 2))."""
+    import torch
+
+    w, s = synth.table_rows(123, np.arange(5000), 64, 16)
+    e8 = synth.scale_bytes(s, "e8m0")
+    np.testing.assert_array_equal(torch.from_numpy(e8).view(torch.float8_e8m0fnu).float().numpy(),
+                                  np.exp2(np.floor(np.log2(s))))
+    e4 = synth.scale_bytes(s, "e4m3")
+    v = torch.from_numpy(e4).view(torch.float8_e4m3fn).float().numpy()
+    assert (v >= 2.0 ** -5).all() and (v < 2.0).all()
+    # the scale times 8, truncated to three mantissa bits
+    x = s.astype(np.float64) * 8
+    q = np.exp2(np.floor(np.log2(x)) - 3)
+    np.testing.assert_array_equal(v, np.floor(x / q) * q)
