@@ -276,7 +276,9 @@ struct SlabCursor {
 // was a matrix-core bubble, measured at ~20 % of the main loop).  A wave's vmcnt counts its loads and
 // stores together and the slab barrier must wait for the loads, so the roles stay split: loaders never
 // have stores outstanding, storers never wait for slab loads.
-template <bool kGate, int NI>
+// kOneSlab: K is a single slab (K = 64; fused launches only), a tile loop of its own so that the other
+// instances do not carry its registers.
+template <bool kGate, int NI, bool kOneSlab = false>
 __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
     constexpr int kBM = 64 * NI;               // tokens per tile
     constexpr int kABytes = kBM * BK * 2;      // the A slab: kBM rows x 128 B
@@ -782,7 +784,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
                 // the exchange region is free until the epilogue: fetch the stream rows of round 0 now
                 if (!kLoader) dma_x(m0, n0, 0, ex, std::true_type{});
                 int free_stage = stage;
-                if (KT == 1) {
+                if constexpr (kOneSlab) {
                     slab(std::true_type{}, std::true_type{}, m0, n0);
                 } else {
                     slab(std::false_type{}, std::true_type{}, m0, n0);
@@ -1021,6 +1023,12 @@ int launch_main(WkvArgs& p, int64_t T, int layers, hipStream_t stream, const cha
     const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
     if (ni == 2 && tiles > kCUs) return fail(ENGRAM_EINVAL, "%s: one-tile launch with %lld tiles", what, (long long)tiles);
+    if constexpr (kGate) {
+        if (p.K == BK) {
+            hipLaunchKernelGGL((wkv_kernel<true, 4, true>), dim3(grid), dim3(kMainThreads), 0, stream, p);
+            return check_launch(what);
+        }
+    }
     if (ni == 2)
         hipLaunchKernelGGL((wkv_kernel<kGate, 2>), dim3(grid), dim3(kMainThreads), 0, stream, p);
     else
