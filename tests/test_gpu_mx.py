@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import assert_close, bf16_tensor, bits
+import synth
+from tests.gpu_util import assert_close, bf16_tensor, bits, compact_rows, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -29,14 +30,16 @@ def _scales_tiled(scale_rowmajor, K, device):
     return torch.from_numpy(t).to(device)
 
 
-def _assert_close_cancelling(kv, a_q, a_s, w_q, w_s, what):
+def _assert_close_cancelling(kv, a_q, a_s, w_q, w_s, what, kv_bits=None):
     """The projection's bar plus an allowance for operands whose products cancel: the fp8 matrix core sums its
     products more coarsely than IEEE fp32 -- measured on gfx950, |error| <= 2^-13.3 * sum_k |a_k w_k| on uniform
     E4M3 codes of both signs (2^-19.3 on quantised normal rows), about three times the fp32 recursive-summation
     bound K * 2^-24 -- so each output may also differ by 2^-12 times the sum of its products' magnitudes."""
     mag = np.abs(oracle.mx_dequant(a_q, a_s)) @ np.abs(oracle.mx_dequant(w_q, w_s)).T
-    assert_close(oracle.bf16_bits_to_float(bits(kv)), oracle.wkv_mx_matmul(a_q, a_s, w_q, w_s),
+    want = oracle.wkv_mx_matmul(a_q, a_s, w_q, w_s)
+    assert_close(oracle.bf16_bits_to_float(bits(kv) if kv_bits is None else kv_bits), want,
                  atol=1e-3 + 2.0 ** -12 * mag, what=what)
+    return want
 
 
 def _bf16_rows(rng, rows, K, spread=30):
@@ -120,3 +123,53 @@ def test_wkv_mx_extreme_scales_and_the_quantiser_chain(gpu_device):
     np.testing.assert_array_equal(aq.cpu().numpy(), oa_q)
     np.testing.assert_array_equal(_scales_rowmajor(asc, T, K), oa_s)
     _assert_close_cancelling(kv, oa_q, oa_s, ow_q, ow_s, "chain")
+
+
+@pytest.mark.parametrize("cfg_index,n_sample", [(2, 8192), (3, 4096)])
+def test_fp8_pipeline(gpu_device, cfg_index, n_sample):
+    """The fp8 path at workload sizes, launched as the benchmark launches it (EngramForward.step(fp8=True):
+    the gathered rows quantised by engram_mx_quant, engram_wkv_mx against the layer's MX weights,
+    engram_gate_dot): the MX operands bit-exact against the oracle's quantiser (of the oracle's gathered rows
+    and of the bf16 weights), kv within the fp8 bar and the dot within the gate bar of the oracle's chain (and
+    of the oracle fed the device's kv).  Every token of the mid prefill (both layers); at the long prefill
+    4,096 sampled tokens with the first, last and a random token of every 256-token M tile."""
+    import torch
+
+    import synth.workload as sw
+
+    cfg = synth.CONFIGS[cfg_index]
+    wl = sw.build(cfg, device=gpu_device, packed=True, fp8=True)
+    dots = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, packed=True, fp8=True)
+    torch.cuda.synchronize()
+    hi = wl.host
+    B, L = hi.input_ids.shape
+    T, C, D, blk, K = cfg.tokens, cfg.n_hash_cols, cfg.head_dim, cfg.block_size, cfg.K
+    ids = oracle.hash(hi.input_ids, 0, hi.token_mask, hi.token_map, np.zeros((B, L), np.int64), hi.multipliers,
+                      hi.primes, hi.offsets, cfg.pad_id, synth.DEAD)
+    sample = sample_tokens(T, n_sample, cfg_index + 100, L=L, mask=hi.token_mask)
+    sidx = torch.from_numpy(sample).to(gpu_device)
+    x_bits = bits(wl.x[0].view(T, cfg.hc_mult, cfg.dim)[sidx])
+    for e in range(cfg.n_layers):
+        lw = wl.fwd.layers[e]
+        lid = ids.reshape(T, cfg.n_layers, C)[sample, e]
+        cw, cs, remap = compact_rows(lid, cfg.rows_alloc[e], synth.table_seed(cfg, e), D, blk)
+        a_want = oracle.gather_dequant(remap, cw, cs, block_size=blk).reshape(len(sample), C * D)
+        aq_want, as_want = oracle.mx_quant(a_want)
+        np.testing.assert_array_equal(wl.fwd._bufs[("a_mx", e)].view(T, K)[sidx].cpu().numpy(), aq_want,
+                                      err_msg=f"MX elements of the gathered rows, layer {e}")
+        np.testing.assert_array_equal(_scales_rowmajor(wl.fwd._bufs[("a_mx_scale", e)], T, K)[sample], as_want,
+                                      err_msg=f"MX scales of the gathered rows, layer {e}")
+        wq_want, ws_want = oracle.mx_quant(bits(lw.wkv))
+        N = wq_want.shape[0]
+        np.testing.assert_array_equal(lw.wkv_mx[0].cpu().numpy(), wq_want, err_msg=f"MX weights, layer {e}")
+        np.testing.assert_array_equal(_scales_rowmajor(lw.wkv_mx[1], N, K), ws_want, err_msg=f"MX weight scales {e}")
+        kv_got = bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])
+        kv_want = _assert_close_cancelling(None, aq_want, as_want, wq_want, ws_want, f"kv (fp8) layer {e}",
+                                           kv_bits=kv_got)
+        kv_want_bits = torch.from_numpy(kv_want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        q_bits, k_bits = bits(lw.q_weight), bits(lw.k_weight)
+        dot_got = dots[e].view(T, -1)[sidx].cpu().numpy()
+        assert_close(dot_got, oracle.gate_dot(x_bits, kv_want_bits, q_bits, k_bits, cfg.eps), what=f"dot (fp8) {e}")
+        assert_close(dot_got, oracle.gate_dot(x_bits, kv_got, q_bits, k_bits, cfg.eps), rtol=1e-3, atol=1e-4,
+                     what=f"dot (fp8, device kv) layer {e}")
+        del kv_want, kv_want_bits
