@@ -349,36 +349,12 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
         run(std::false_type{});
 }
 
-// ---- OCP MX quantisation of bf16 rows (one wave per 32-column block group) ----
+// ---- OCP MX quantisation of bf16 rows ----
 // A thread owns 8 consecutive columns (one 16-byte load); the 4 threads of a 32-column block reduce their
 // amax with two lane swaps.  The shared exponent floor(log2 amax) - 8 is read off amax's fp32 exponent field
 // (amax is a bf16 value, so it is normal or a bf16 subnormal, which fp32 holds exactly); the scaled element
-// x * 2^-e is formed exactly by ldexp and rounded to E4M3 (nearest even, saturated at 448) from its bits.
-__device__ inline uint32_t e4m3_sat_rne(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float m = fabsf(v);
-    if (m >= 448.0f) return sign | 0x7Eu;
-    if (m < 0.015625f) {  // below 2^-6: multiples of 2^-9
-        const float n = __builtin_rintf(m * 512.0f);  // exact product; rint rounds half to even
-        return sign | static_cast<uint32_t>(n);
-    }
-    const uint32_t mu = __float_as_uint(m);
-    const int e = static_cast<int>(mu >> 23) - 127;          // floor(log2 m), in [-6, 8]
-    const uint32_t mant = mu & 0x7FFFFFu;
-    // keep 3 mantissa bits, round the other 20 to nearest even
-    uint32_t q = (mant >> 20) | 8u;                          // 8..15
-    const uint32_t rest = mant & 0xFFFFFu;
-    if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ++q;
-    int ee = e;
-    if (q == 16u) {
-        q = 8u;
-        ++ee;
-    }
-    if (ee > 8 || (ee == 8 && q > 14u)) return sign | 0x7Eu;
-    return sign | (static_cast<uint32_t>(ee + 7) << 3) | (q - 8u);
-}
-
+// x * 2^-e is formed exactly by ldexp, clamped to +-448 and rounded to E4M3 (nearest even) by the
+// hardware conversion.
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* x, int64_t rows, int K, int64_t rows4,
                                                       uint8_t* q, uint8_t* scale) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -407,9 +383,18 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* x, int64_
         const int fl = ef != 0 ? ef - 127 : 31 - __builtin_clz(au & 0x7FFFFFu) - 149;  // floor(log2 amax)
         shared = max(-127, min(127, fl - 8));
     }
-    uint32_t packed[2] = {0, 0};
+    // x 2^-shared is exact (a power of two; results below fp32's normal range round to 0 in E4M3 either way);
+    // clamped to +-448 it converts without overflow, rounded to nearest even by v_cvt_pk_fp8_f32 (OCP E4M3 on
+    // gfx950, subnormals included) -- the saturating conversion
+    float g[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i >> 2] |= e4m3_sat_rne(__builtin_ldexpf(f[i], -shared)) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) g[i] = __builtin_amdgcn_fmed3f(__builtin_ldexpf(f[i], -shared), -448.0f, 448.0f);
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(g[4 * h], g[4 * h + 1], 0, false);
+        packed[h] = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(g[4 * h + 2], g[4 * h + 3], lo, true));
+    }
     if (!ok) return;
     *reinterpret_cast<u32x2*>(q + r * K + 8 * c8) = u32x2{packed[0], packed[1]};
     if ((c8 & 3) == 0) {
