@@ -324,3 +324,27 @@ def test_formats_validation():
     assert L.engram_hash_i32(FAKE, 1, 64, 0, None, FAKE, 10, FAKE, 1, 64, FAKE, FAKE, FAKE, 1, 4, 2, 2, -1,
                              ctypes.c_void_p(0x100002), None) == 1
     assert "aligned" in _err()
+
+
+def test_probe_library_exports_and_validates():
+    """libengram_probe.so (the measured ceilings) loads without a GPU, exports what include/engram_probe.h
+    declares, and rejects bad arguments on the host before any launch."""
+    from gram_hash_embedding_amd import build as engram_build
+
+    text = open(os.path.join(ROOT, "include", "engram_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(engram_probe_\w+)\s*\(", text)))
+    assert set(names) == {"engram_probe_mfma", "engram_probe_read", "engram_probe_copy", "engram_probe_read_grid"}
+    L = ctypes.CDLL(engram_build.PROBE_LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    L.engram_probe_mfma.argtypes = [ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+    L.engram_probe_read.argtypes = [P, ctypes.c_int64, P, P]
+    L.engram_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
+    assert L.engram_probe_read_grid() > 0
+    assert L.engram_probe_mfma(2, FAKE, FAKE, 256, 8, 10, None) != 0   # unknown kind
+    assert L.engram_probe_mfma(0, FAKE, FAKE, 256, 9, 10, None) != 0   # more than 8 waves
+    assert L.engram_probe_mfma(0, None, FAKE, 256, 8, 10, None) != 0
+    assert L.engram_probe_read(FAKE, 24, FAKE, None) != 0              # not a multiple of 16
+    assert L.engram_probe_read(ctypes.c_void_p(0x100008), 32, FAKE, None) != 0  # misaligned
+    assert L.engram_probe_copy(FAKE, None, 32, None) != 0
