@@ -201,54 +201,57 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a, GatherSide g
         }
     }
     if constexpr (D > 0) {
-        // Phase 3: D/16 lanes per row (one 16-byte piece each), rows (token, layer, column) of the tile in
-        // order, kUnroll rows per lane in flight.  A row outside its layer's [row_start, row_start + R) is
-        // zero; the record's scales sit after its D bytes.
+        // Phase 3: D/16 lanes per row (one 16-byte piece each); layer by layer, the layer's rows (token,
+        // column) of the tile in order, kUnroll rows per lane in flight.  A row outside its layer's
+        // [row_start, row_start + R) is zero; the record's scales sit after its D bytes.
         constexpr int LPR = D / 16;
         constexpr int RPP = kThreads / LPR;  // rows per pass
         constexpr int kUnroll = kGatherUnroll;
         __syncthreads();
         const int lr = tid % LPR;
         const int sidx = (lr * 16) / gs.blk;
-        for (int r0 = tid / LPR; r0 < total; r0 += RPP * kUnroll) {
-            u32x4 v[kUnroll];
-            float sc[kUnroll];
-            bool ok[kUnroll];
-            uint16_t* dst[kUnroll];
+        const int rows = ntok * a.C;  // one layer's rows of the tile: row r = (token r / C, column r % C)
+        // consecutive rows of a lane are RPP apart: (RPP / C, RPP % C) in (token, column), one carry
+        const int step_i = RPP / a.C, step_c = RPP - step_i * a.C;
+        for (int e = 0; e < a.E; ++e) {
+            // the layer's arguments, read with a wave-uniform index from the kernel arguments
+            const uint8_t* table = gs.table[e];
+            const int64_t R = gs.R[e], rs = gs.row_start[e];
+            uint16_t* o = gs.out[e];
+            for (int r0 = tid / LPR; r0 < rows; r0 += RPP * kUnroll) {
+                u32x4 v[kUnroll];
+                float sc[kUnroll];
+                bool ok[kUnroll];
+                uint16_t* dst[kUnroll];
+                int i = r0 / a.C;
+                int c = r0 - i * a.C;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int r = r0 + u * RPP;
-                const bool live = r < total;
-                const int i = live ? r / EC : 0;
-                const int pc = live ? r - i * EC : 0;
-                const int e = pc / a.C;
-                const int c = pc - e * a.C;
-                const uint8_t* table = gs.table[0];
-                int64_t R = gs.R[0], rs = gs.row_start[0];
-                uint16_t* o = gs.out[0];
-#pragma unroll
-                for (int k = 1; k < kMaxE; ++k)  // select the layer's arguments (no dynamic indexing)
-                    if (e == k) {
-                        table = gs.table[k];
-                        R = gs.R[k];
-                        rs = gs.row_start[k];
-                        o = gs.out[k];
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int r = r0 + u * RPP;
+                    const bool live = r < rows;
+                    const int ri = i * EC + e * a.C + c;  // the id's place in the tile's [token, layer, column]
+                    const int64_t local = (live ? ids[ri] : rs) - rs;
+                    ok[u] = live && local >= 0 && local < R;
+                    const uint8_t* rec = table + (ok[u] ? local : 0) * (2 * D);
+                    v[u] = *reinterpret_cast<const u32x4*>(rec + lr * 16);
+                    sc[u] = reinterpret_cast<const float*>(rec + D)[sidx];
+                    dst[u] = live ? o + ((tile0 + i) * a.C + c) * D + lr * 16 : nullptr;
+                    i += step_i;
+                    c += step_c;
+                    if (c >= a.C) {
+                        c -= a.C;
+                        ++i;
                     }
-                const int64_t local = (live ? ids[r] : rs) - rs;
-                ok[u] = live && local >= 0 && local < R;
-                const uint8_t* rec = table + (ok[u] ? local : 0) * (2 * D);
-                v[u] = *reinterpret_cast<const u32x4*>(rec + lr * 16);
-                sc[u] = reinterpret_cast<const float*>(rec + D)[sidx];
-                dst[u] = live ? o + ((tile0 + i) * a.C + c) * D + lr * 16 : nullptr;
-            }
+                }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                if (dst[u] == nullptr) continue;
-                u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
-                if (ok[u]) dequant16(v[u], sc[u], o0, o1);
-                u32x4* d = reinterpret_cast<u32x4*>(dst[u]);
-                __builtin_nontemporal_store(o0, d);
-                __builtin_nontemporal_store(o1, d + 1);
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (dst[u] == nullptr) continue;
+                    u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+                    if (ok[u]) dequant16(v[u], sc[u], o0, o1);
+                    u32x4* d = reinterpret_cast<u32x4*>(dst[u]);
+                    __builtin_nontemporal_store(o0, d);
+                    __builtin_nontemporal_store(o1, d + 1);
+                }
             }
         }
     }
