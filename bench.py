@@ -336,6 +336,9 @@ def measure_workload(cfg, args, dev, peaks, full: bool) -> dict:
     if fp8:
         # the fp8 block-scaled projection (gathered rows quantised to MX fp8, engram_wkv_mx, engram_gate_dot)
         runs.append(("fp8_unfused", False, False, main_packed, False, False, True))
+        # and fused (engram_wkv_mx_gate: keys reduced in the projection), where K allows it
+        if cfg.K >= 384:
+            runs.append(("fp8_fused", True, False, main_packed, False, False, True))
     for name, fused, output, packed, hg, al, f8 in runs:
         sec, ev = loop(fused, output, packed, hg, al, f8)
         paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
@@ -442,8 +445,10 @@ def measure_workload(cfg, args, dev, peaks, full: bool) -> dict:
             byts = layers * (W_bytes + T_launch * algo["wkv_gate_bytes"])
             w["GB/s"] = round(byts / (w["avg_us"] * 1e3), 1)
             w["frac_hbm"] = round(w["GB/s"] / PEAK_HBM_GBS, 4)
-    if "wkv_mx" in kern:
-        w = kern["wkv_mx"]
+    for name in ("wkv_mx", "wkv_mx_gate"):  # the fp8 projection, alone and fused with the gate (finalize included)
+        if name not in kern:
+            continue
+        w = kern[name]
         w["TFLOP/s"] = round(T_launch * algo["wkv_flops"] / (w["avg_us"] * 1e6), 1)
         w["frac_fp8_mfma"] = round(w["TFLOP/s"] / PEAK_FP8_TFLOPS, 4)
         if peaks:

@@ -22,6 +22,7 @@ an exception is raised.
     engram_gate_residual   -- gate, token mask and residual add from a given dot
     engram_mx_quant        -- bf16 rows -> OCP MX fp8 (E4M3 + E8M0 scale per 32 columns)
     engram_wkv_mx          -- the wkv projection on MX fp8 operands (fp8 matrix cores with block scales)
+    engram_wkv_mx_gate     -- engram_wkv_mx fused with the gate dot (keys reduced in the projection)
 """
 from __future__ import annotations
 
@@ -70,12 +71,13 @@ def lib() -> ctypes.CDLL:
         L.engram_mx_scale_bytes.restype = i64
         L.engram_mx_quant.argtypes = [p, i64, i32, p, p, p]
         L.engram_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, p]
+        L.engram_wkv_mx_gate.argtypes = [p, p, p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
         L.engram_wkv_gate_workspace_bytes.restype = i64
         for f in (L.engram_hash, L.engram_hash_i32, L.engram_gather_dequant_fmt, L.engram_hash_gather_packed, L.engram_gather_dequant, L.engram_gather_dequant_packed, L.engram_pack_table,
                   L.engram_wkv, L.engram_gate_dot, L.engram_gate_output, L.engram_wkv_gate, L.engram_gate_residual,
                   L.engram_wkv_gate_layers, L.engram_wkv_gate_layers_noalloc, L.engram_mx_quant, L.engram_wkv_mx,
-                  L.engram_abi_version):
+                  L.engram_wkv_mx_gate, L.engram_abi_version):
             f.restype = ctypes.c_int
         L.engram_status_string.argtypes = [ctypes.c_int]
         L.engram_status_string.restype = ctypes.c_char_p
@@ -470,6 +472,50 @@ def engram_wkv_gate_workspace_bytes(T: int, hc: int, dim: int) -> int:
     return n
 
 
+def engram_wkv_mx_gate(a, a_scale, w, w_scale, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None,
+                       stream=None):
+    """(value bf16 [T, dim], dot float32 [T, hc]) from MX fp8 operands a (uint8 [T, K]) and w (uint8
+    [(hc+1)*dim, K]) with their scales, and the stream x bf16 [T, hc, dim] (or [B, L, hc, dim]); `value`,
+    `dot` and `workspace` as engram_wkv_gate."""
+    import torch
+
+    if a.dtype == torch.float8_e4m3fn:
+        a = a.view(torch.uint8)
+    if w.dtype == torch.float8_e4m3fn:
+        w = w.view(torch.uint8)
+    x3 = x.reshape(-1, x.shape[-2], x.shape[-1])
+    T, hc, dim = x3.shape
+    if a.dim() != 2 or a.shape[0] != T:
+        raise ValueError("a must be [T, K]")
+    K = a.shape[1]
+    if tuple(w.shape) != ((hc + 1) * dim, K):
+        raise ValueError("w must be [(hc+1)*dim, K]")
+    if a_scale.numel() != engram_mx_scale_bytes(T, K) or w_scale.numel() != engram_mx_scale_bytes(w.shape[0], K):
+        raise ValueError("a_scale / w_scale must be MX scale arrays of a and w")
+    if tuple(q_weight.shape) != (hc, dim) or tuple(k_weight.shape) != (hc, dim):
+        raise ValueError("q_weight and k_weight must be [hc, dim]")
+    if value is None:
+        value = torch.empty((T, dim), dtype=torch.bfloat16, device=a.device)
+    if value.dim() != 2 or value.shape[0] != T or value.shape[1] < dim or value.stride(1) != 1:
+        raise ValueError("value must be [T, >= dim] with unit column stride")
+    if value.dtype != torch.bfloat16 or not value.is_cuda:
+        raise TypeError("value must be a bf16 GPU tensor")
+    if dot is None:
+        dot = torch.empty((T, hc), dtype=torch.float32, device=a.device)
+    if tuple(dot.shape) != (T, hc):
+        raise ValueError("dot must be [T, hc]")
+    need = engram_wkv_gate_workspace_bytes(T, hc, dim)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    _check(lib().engram_wkv_mx_gate(
+        _dev(a, "a", torch.uint8, 2), _dev(a_scale, "a_scale", torch.uint8), _dev(w, "w", torch.uint8, 2),
+        _dev(w_scale, "w_scale", torch.uint8), _dev(x3, "x", torch.bfloat16, 3),
+        _dev(q_weight, "q_weight", torch.bfloat16, 2), _dev(k_weight, "k_weight", torch.bfloat16, 2), float(eps),
+        ctypes.c_void_p(value.data_ptr()), value.stride(0), _dev(dot, "dot", torch.float32),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), T, K, hc, dim, _stream(stream)))
+    return value, dot
+
+
 def engram_wkv_gate(a, w, x, q_weight, k_weight, eps, value=None, dot=None, workspace=None, stream=None):
     """(value bf16 [T, dim], dot float32 [T, hc]) from a bf16 [T, K], w bf16 [(hc+1)*dim, K] and the stream
     x bf16 [T, hc, dim] (or [B, L, hc, dim]).  `value` may be a [T, ld >= dim] row-strided view whose first
@@ -615,6 +661,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
            "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_layers_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "engram_wkv_gate_workspace_bytes", "engram_gather_dequant_fmt", "SCALE_FORMATS", "engram_mx_quant", "engram_wkv_mx", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate_workspace_bytes", "engram_gather_dequant_fmt", "SCALE_FORMATS", "engram_mx_quant", "engram_wkv_mx", "engram_wkv_mx_gate", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

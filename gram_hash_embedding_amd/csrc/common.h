@@ -21,4 +21,10 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // 16-byte vector of 32-bit words: the unit of every wide global access.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// The second launch of a fused projection + gate (wkv.hip): per (token, copy), the per-128-column partial sums
+// [hc][dim/128][3][T] of each of `layers` layers (layer e's at part + e * part_stride floats) added in slice
+// order, then dot = sum(h w key) * rsqrt(mean h^2 + eps) * rsqrt(mean key^2 + eps) * dim^-1/2.
+int launch_gate_finalize(const float* part, int64_t part_stride, float* const* dot, int layers, int64_t T, int hc,
+                         int dim, float eps, hipStream_t stream, const char* what);
+
 }  // namespace engram

@@ -999,6 +999,31 @@ __global__ __launch_bounds__(256) void gate_finalize_split_kernel(FinArgs f) {
 }
 
 }  // namespace
+
+int launch_gate_finalize(const float* part, int64_t part_stride, float* const* dot, int layers, int64_t T, int hc,
+                         int dim, float eps, hipStream_t stream, const char* what) {
+    const int64_t blocks = (T * hc + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tokens", what);
+    FinArgs f = {};
+    f.part = part;
+    f.part_stride = part_stride;
+    for (int e = 0; e < layers; ++e) f.dot[e] = dot[e];
+    f.M = T;
+    f.hc = hc;
+    f.slices = dim / 128;
+    f.eps = eps;
+    f.inv_dim = 1.0f / static_cast<float>(dim);
+    f.rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
+    if (blocks * layers < kCUs && f.slices <= kFinGroups * kFinPer) {  // few pairs: one memory latency per pair
+        const int64_t split_blocks = static_cast<int64_t>(hc) * ((T + 31) / 32);
+        hipLaunchKernelGGL(gate_finalize_split_kernel, dim3(static_cast<unsigned>(split_blocks), layers), dim3(256),
+                           0, stream, f);
+    } else {
+        hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks), layers), dim3(256), 0, stream, f);
+    }
+    return check_launch(what);
+}
+
 }  // namespace engram
 
 using namespace engram;
@@ -1139,7 +1164,6 @@ int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const
     if (!static_scratch && !aligned(workspace, 16)) return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
     const int Nout = (hc + 1) * dim;
     WkvArgs p = {};
-    FinArgs f = {};
     for (int e = 0; e < layers; ++e) {
         if (!a[e] || !w[e] || !x[e] || !q_weight[e] || !k_weight[e] || !value[e] || !dot[e])
             return fail(ENGRAM_EINVAL, "%s: layer %d: null pointer", what, e);
@@ -1160,7 +1184,6 @@ int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const
         L.q = q_weight[e];
         L.k = k_weight[e];
         L.part = static_cast<float*>(workspace) + e * (per_layer / static_cast<int64_t>(sizeof(float)));
-        f.dot[e] = dot[e];
     }
     p.M = T;
     p.N = Nout;
@@ -1172,25 +1195,8 @@ int wkv_gate_entry(const char* what, int layers, const uint16_t* const* a, const
     p.tiles_n = Nout / BN;
     int rc = launch_main<true>(p, T, layers, as_stream(stream), what);
     if (rc != ENGRAM_OK) return rc;
-    const int64_t blocks = (T * hc + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tokens", what);
-    f.part = static_cast<const float*>(workspace);
-    f.part_stride = per_layer / static_cast<int64_t>(sizeof(float));
-    f.M = T;
-    f.hc = hc;
-    f.slices = dim / 128;
-    f.eps = eps;
-    f.inv_dim = 1.0f / static_cast<float>(dim);
-    f.rsqrt_dim = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(dim)));
-    if (blocks * layers < kCUs && f.slices <= kFinGroups * kFinPer) {  // few pairs: one memory latency per pair
-        const int64_t split_blocks = static_cast<int64_t>(hc) * ((T + 31) / 32);
-        hipLaunchKernelGGL(gate_finalize_split_kernel, dim3(static_cast<unsigned>(split_blocks), layers), dim3(256),
-                           0, as_stream(stream), f);
-    } else {
-        hipLaunchKernelGGL(gate_finalize_kernel, dim3(static_cast<unsigned>(blocks), layers), dim3(256), 0,
-                           as_stream(stream), f);
-    }
-    return check_launch(what);
+    return launch_gate_finalize(static_cast<const float*>(workspace), per_layer / static_cast<int64_t>(sizeof(float)),
+                                dot, layers, T, hc, dim, eps, as_stream(stream), what);
 }
 
 }  // namespace

@@ -48,6 +48,8 @@ constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;             // cache-policy operand of a global load: streamed past L2
+constexpr int kXArea = 32 * 128;            // fused gate: a wave's stream rows of one round (32 tokens x 64 bf16)
 constexpr int kWaitLgkmcnt0 = 0xC07F;
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
@@ -62,6 +64,12 @@ struct MxArgs {
     int64_t M4, N4;      // rows of the scale layouts (multiples of 4)
     int tiles_m, tiles_n;
     int64_t ld_out;
+    // the fused gate (kGate): every tile's columns are key columns, reduced against the stream, not stored
+    const uint16_t* x;   // [M, hc, dim] bf16
+    const uint16_t* q;   // [hc, dim] bf16
+    const uint16_t* k;   // [hc, dim] bf16
+    float* part;         // [hc][dim/128][3][M] fp32: per 128-column slice pair sum(h w key), sum(key^2), sum(h^2)
+    int hc, dim;
 };
 
 // pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
@@ -86,7 +94,25 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
+__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 (RNE) in one instruction, opaque to the compiler so that it keeps the pair
+__device__ inline uint32_t cvt_pk_bf16(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+
+// c + a.lo * b.lo + a.hi * b.hi over packed bf16 pairs, fp32 accumulation
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// kGate: the fused projection + gate pre-activation over the key columns only (every tile is reduced against
+// the stream in its epilogue instead of stored; the value columns are a plain launch of their own).
+template <bool kGate>
+__device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
     const int tiles = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
@@ -242,6 +268,142 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
         }
     };
 
+    // ---- fused gate epilogue of a key tile (kGate): the product is not stored.  The tile's 256 columns lie in
+    // one copy c; wave (wm, wn) owns the 64-column slice (n0 - c dim) / 64 + wn of that copy and tokens
+    // [128 wm, +128).  Lane l holds, in round i < 4, token 32i + l%32 and 32 of the slice's columns (4
+    // consecutive ones per (j, gq), as the MFMA leaves them).  Each accumulator is rounded to bf16 (the product
+    // is a bf16 tensor before it is used) and reduced against the stream's matching element: sum(h w key),
+    // sum(key^2), sum(h^2) over the lane's columns, then over the two lane halves.  A key tile's last two slabs
+    // issue nothing (the next tile's first two slabs are held back), so both stages are free once its last
+    // slab's barrier has passed: there each wave fetches the stream rows of its four rounds with direct-to-LDS
+    // loads -- round r in stage st (r < 2) or st ^ 1, at (r & 1) * 32 KB, the wave's 4 KB area: row t is token
+    // 32 r + t of the wave's 128, 16-byte piece q at slot q ^ ((t >> 1) & 7) -- and waits only for its own loads.
+    // Loader waves hand their sums to their SIMD partner (storer wave w + 4: the same tokens, the slice 128
+    // columns to the right), which adds them to its own and stores one value per (copy, pair of slices, token).
+    auto own_wait = [&](auto n_tag) {  // this wave's own loads down to n outstanding; LDS reads stay after it
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(decltype(n_tag)::value));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto lds_fence = [&]() {  // this wave's LDS reads are done
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0, int st) {
+        const int l = lane_id();
+        const int c = n0 / p.dim;
+        const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice inside copy c
+        auto round_base = [&](int r) { return lds + (r < 2 ? st : st ^ 1) * kStageBytes + (r & 1) * 8 * kXArea; };
+        // q * k (exact in fp32) for the lane's 32 columns, loaded before the stream rows so that waiting for them
+        // leaves the rows in flight
+        const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
+        u32x2 qv[2][4], kv[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                qv[j][gq] = *reinterpret_cast<const u32x2*>(qrow + 32 * j + 8 * gq);
+                kv[j][gq] = *reinterpret_cast<const u32x2*>(krow + 32 * j + 8 * gq);
+            }
+        const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
+        const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + col0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int ins = 0; ins < 4; ++ins) {
+                const int rr = 8 * ins + (l >> 3);
+                const int piece = (l & 7) ^ ((rr >> 1) & 7);
+                const int64_t t = min<int64_t>(m0 + wm * 128 + 32 * r + rr, p.M - 1);  // past M: unused
+                __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece,
+                                                 round_base(r) + wave * kXArea + ins * 1024, 16, 0, kNonTemporal);
+            }
+        float wgt[2][4][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                wgt[j][gq][0] = lo_bf16(qv[j][gq][0]) * lo_bf16(kv[j][gq][0]);
+                wgt[j][gq][1] = hi_bf16(qv[j][gq][0]) * hi_bf16(kv[j][gq][0]);
+                wgt[j][gq][2] = lo_bf16(qv[j][gq][1]) * lo_bf16(kv[j][gq][1]);
+                wgt[j][gq][3] = hi_bf16(qv[j][gq][1]) * hi_bf16(kv[j][gq][1]);
+            }
+        float res[4][3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i == 0) own_wait(std::integral_constant<int, 12>{});  // round i landed; the later rounds may fly
+            if (i == 1) own_wait(std::integral_constant<int, 8>{});
+            if (i == 2) own_wait(std::integral_constant<int, 4>{});
+            if (i == 3) own_wait(std::integral_constant<int, 0>{});
+            const uint8_t* xl = round_base(i) + wave * kXArea;
+            u32x2 xr[2][4];
+            {
+                const int rr = l & 31, hx = l >> 5;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq)
+                        xr[j][gq] = *reinterpret_cast<const u32x2*>(
+                            xl + rr * 128 + (((4 * j + gq) ^ ((rr >> 1) & 7)) << 4) + hx * 8);
+            }
+            float hwk = 0.f, kk = 0.f, hh = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const uint32_t k01 = cvt_pk_bf16(acc[i][j][4 * gq + 0], acc[i][j][4 * gq + 1]);
+                    const uint32_t k23 = cvt_pk_bf16(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+                    const float key[4] = {lo_bf16(k01), hi_bf16(k01), lo_bf16(k23), hi_bf16(k23)};
+                    const float h[4] = {lo_bf16(xr[j][gq][0]), hi_bf16(xr[j][gq][0]), lo_bf16(xr[j][gq][1]),
+                                        hi_bf16(xr[j][gq][1])};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hwk += h[r] * wgt[j][gq][r] * key[r];
+                    kk = dot2_bf16(k01, k01, kk);
+                    kk = dot2_bf16(k23, k23, kk);
+                    hh = dot2_bf16(xr[j][gq][0], xr[j][gq][0], hh);
+                    hh = dot2_bf16(xr[j][gq][1], xr[j][gq][1], hh);
+                }
+            res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
+            res[i][1] = kk + __shfl_xor(kk, 32, 64);
+            res[i][2] = hh + __shfl_xor(hh, 32, 64);
+        }
+        // hand-over: a loader wave leaves its sums in its own area of round 3 (read out above); its SIMD partner
+        // adds them to its own and stores both
+        uint8_t* const hand = round_base(3);
+        if (loader) {
+            lds_fence();
+            if (l < 32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        reinterpret_cast<float*>(hand + wave * kXArea)[(i * 3 + q) * 32 + l] = res[i][q];
+            }
+        }
+        sync_epi();
+        if (!loader && l < 32) {
+            // the storer adds its partner's sums (slice wn - 2 of the tile) to its own (slice wn): one value per
+            // (copy, 128-column slice pair, token), always summed in this order
+            const float* partner = reinterpret_cast<const float*>(hand + (wave - 4) * kXArea);
+            const int64_t tbase = m0 + wm * 128 + l;
+            const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
+            float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = tbase + 32 * i;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const float v = res[i][q] + partner[(i * 3 + q) * 32 + l];
+                    if (t < p.M) __builtin_nontemporal_store(v, out + q * p.M + t);
+                }
+            }
+        }
+        sync_epi();  // the partner's sums and every round's rows are read before the stages are refilled
+    };
+
     if (static_cast<int>(blockIdx.x) >= tiles) return;
     const int my_tiles = (tiles - 1 - static_cast<int>(blockIdx.x)) / G + 1;
     const int total = my_tiles * KT;  // slabs of this workgroup
@@ -252,16 +414,18 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
     // in W-fragment-major order; each fragment is reloaded, for k-step `ns` of stage `nst`, right after its last
     // use here (one set of 48 fragment registers; every reload is issued three or more MFMAs before its use).
     // Each MFMA with its reloads and `extra(u)` (u = 0..7: a share of the slab loads) is one scheduling unit.
+    // kReload false (the last slab of a fused key tile): no reloads, the fragments are dead after the k-step.
     auto kstep = [&](auto sel_tag, auto zero_tag, f32x16 (&acc)[4][2], i32x8 (&fa)[4], i32x8 (&fw)[2],
-                     const uint32_t* sa, const uint32_t* sw, int nst, int ns, auto&& extra) {
+                     const uint32_t* sa, const uint32_t* sw, int nst, int ns, auto&& extra, auto reload_tag) {
         constexpr int kSel = decltype(sel_tag)::value;
         constexpr bool kZero = decltype(zero_tag)::value;
+        constexpr bool kReload = decltype(reload_tag)::value;
         const f32x16 z = {};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0], fa[i], kZero ? z : acc[i][0], 0, 0,
                                                                         kSel, sw[0], kSel, sa[i]);
-            if (i == 3) fw[0] = read_w(nst, ns, 0);
+            if (kReload && i == 3) fw[0] = read_w(nst, ns, 0);
             extra(i);
             asm volatile("" ::: "memory");  // keeps the unit's LDS reads and loads in the unit
             __builtin_amdgcn_sched_barrier(0);
@@ -270,8 +434,8 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
         for (int i = 0; i < 4; ++i) {
             acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1], fa[i], kZero ? z : acc[i][1], 0, 0,
                                                                         kSel, sw[1], kSel, sa[i]);
-            fa[i] = read_a(nst, ns, i);
-            if (i == 3) fw[1] = read_w(nst, ns, 1);
+            if (kReload) fa[i] = read_a(nst, ns, i);
+            if (kReload && i == 3) fw[1] = read_w(nst, ns, 1);
             extra(4 + i);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
@@ -298,47 +462,121 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
         for (int i = 0; i < 4; ++i) fa[i] = read_a(0, 0, i);
         fw[0] = read_w(0, 0, 0);
         fw[1] = read_w(0, 0, 1);
-        for (int t = 0; t < my_tiles; ++t) {
-            const int pid = static_cast<int>(blockIdx.x) + t * G;
-            int tm, tn;
-            tile_coords(p, pid, tm, tn);
-            const int64_t m0 = static_cast<int64_t>(tm) * BM;
-            const int n0 = tn * BN;
-            for (int kt = 0; kt < KT; ++kt, ++n) {
-                // k-step 0 of the slab (its fragments and scales already in registers), reloading k-step 1's
-                if (kt == 0)
-                    kstep(std::integral_constant<int, 0>{}, std::true_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra);
-                else
-                    kstep(std::integral_constant<int, 0>{}, std::false_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra);
-                // the next slab has landed (the loaders waited for it) and this stage is read out: publish one
-                // stage, refill the other with the slab after next
+        if constexpr (!kGate) {
+            for (int t = 0; t < my_tiles; ++t) {
+                const int pid = static_cast<int>(blockIdx.x) + t * G;
+                int tm, tn;
+                tile_coords(p, pid, tm, tn);
+                const int64_t m0 = static_cast<int64_t>(tm) * BM;
+                const int n0 = tn * BN;
+                for (int kt = 0; kt < KT; ++kt, ++n) {
+                    // k-step 0 of the slab (its fragments and scales already in registers), reloading k-step 1's
+                    if (kt == 0)
+                        kstep(std::integral_constant<int, 0>{}, std::true_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra, std::true_type{});
+                    else
+                        kstep(std::integral_constant<int, 0>{}, std::false_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra, std::true_type{});
+                    // the next slab has landed (the loaders waited for it) and this stage is read out: publish one
+                    // stage, refill the other with the slab after next
+                    if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+                    sync();
+                    // k-step 1, reloading k-step 0 of the next slab (and its scales) from the other stage; the loaders
+                    // spread the slab after next over its MFMAs
+                    uint32_t sa_n[4], sw_n[2];
+                    const int nst = stage ^ 1;
+                    if (kLoader) {
+                        const int nn = n + 2;
+                        const SlabRsrc r = slab_rsrc(slab_pid(nn < total ? nn : 0), nn % KT, nn < total);
+                        const int st = stage;
+                        kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
+                            if (u == 0) read_scales(nst, sa_n, sw_n);  // (past the last slab: stale, unused)
+                            issue_part(r, st, u);
+                        }, std::true_type{});
+                    } else {
+                        kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
+                            if (u == 0) read_scales(nst, sa_n, sw_n);
+                        }, std::true_type{});
+                    }
+                    shift_scales(sa_n, sw_n);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) sw[j] = sw_n[j];
+                    stage ^= 1;
+                }
+                epilogue(acc, m0, n0);
+            }
+        } else {
+            // One slab: k-step 0, the barrier, k-step 1.  kIssue false: the loaders issue nothing (the held-back
+            // slabs of a key tile's end); kReload false: the tile's last slab, no fragments are reloaded.
+            // kFirst: the tile's first slab (zero C operand: the accumulators are dead between tiles)
+            auto slab = [&](auto first_tag, auto issue_tag, auto reload_tag) {
+                constexpr bool kIssue = decltype(issue_tag)::value;
+                constexpr bool kReload = decltype(reload_tag)::value;
+                kstep(std::integral_constant<int, 0>{}, first_tag, acc, fa, fw, sa, sw, stage, 1, no_extra,
+                      std::true_type{});
                 if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
                 sync();
-                // k-step 1, reloading k-step 0 of the next slab (and its scales) from the other stage; the loaders
-                // spread the slab after next over its MFMAs
                 uint32_t sa_n[4], sw_n[2];
                 const int nst = stage ^ 1;
-                if (kLoader) {
+                if constexpr (!kReload) {
+                    kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, no_extra,
+                          std::false_type{});
+                } else if (kLoader && kIssue) {
                     const int nn = n + 2;
                     const SlabRsrc r = slab_rsrc(slab_pid(nn < total ? nn : 0), nn % KT, nn < total);
                     const int st = stage;
                     kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
                         if (u == 0) read_scales(nst, sa_n, sw_n);  // (past the last slab: stale, unused)
                         issue_part(r, st, u);
-                    });
+                    }, std::true_type{});
                 } else {
                     kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
                         if (u == 0) read_scales(nst, sa_n, sw_n);
-                    });
+                    }, std::true_type{});
                 }
-                shift_scales(sa_n, sw_n);
+                if constexpr (kReload) {
+                    shift_scales(sa_n, sw_n);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
+                    for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) sw[j] = sw_n[j];
+                    for (int j = 0; j < 2; ++j) sw[j] = sw_n[j];
+                }
                 stage ^= 1;
+                ++n;
+            };
+            for (int t = 0; t < my_tiles; ++t) {
+                const int pid = static_cast<int>(blockIdx.x) + t * G;
+                int tm, tn;
+                tile_coords(p, pid, tm, tn);
+                const int64_t m0 = static_cast<int64_t>(tm) * BM;
+                const int n0 = tn * BN;
+                using T_ = std::true_type;
+                using F_ = std::false_type;
+                // a key tile (KT >= 3): its last two slabs hold back the next tile's first two
+                slab(T_{}, T_{}, T_{});
+                for (int kt = 1; kt < KT - 2; ++kt) slab(F_{}, T_{}, T_{});
+                slab(F_{}, F_{}, T_{});
+                const int st = stage;  // the last slab's stage
+                slab(F_{}, F_{}, F_{});
+                gate_epilogue(acc, m0, n0, st);
+                // the held-back slabs n and n + 1 of the stream (past the workgroup's last: empty issues) into the
+                // two stages; the first must land before its fragments are read, the second may still fly
+                if (kLoader) {
+                    issue_slab(slab_pid(n < total ? n : 0), n % KT, stage, n < total);
+                    issue_slab(slab_pid(n + 1 < total ? n + 1 : 0), (n + 1) % KT, stage ^ 1, n + 1 < total);
+                    if (wave < 2)
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt(17));  // (waves 0 and 1 also load a slab's scales)
+                    else
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+                }
+                sync();
+                read_scales(stage, sa, sw);
+                shift_scales(sa, sw);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fa[i] = read_a(stage, 0, i);
+                fw[0] = read_w(stage, 0, 0);
+                fw[1] = read_w(stage, 0, 1);
             }
-            epilogue(acc, m0, n0);
         }
         // loads issued past this workgroup's last slab (empty resources) still write LDS: let them land
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
@@ -348,6 +586,9 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) {
     else
         run(std::false_type{});
 }
+
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) { wkv_mx_body<false>(p); }
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_gate_kernel(MxArgs p) { wkv_mx_body<true>(p); }
 
 // ---- OCP MX quantisation of bf16 rows ----
 // A thread owns 8 consecutive columns (one 16-byte load); the 4 threads of a 32-column block reduce their
@@ -458,4 +699,82 @@ extern "C" int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uin
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
     hipLaunchKernelGGL(wkv_mx_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
     return check_launch(what);
+}
+
+extern "C" int engram_wkv_mx_gate(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                                  const uint16_t* x, const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                                  uint16_t* value, int64_t ld_value, float* dot, void* workspace,
+                                  int64_t workspace_bytes, int64_t T, int32_t K, int32_t hc, int32_t dim,
+                                  void* stream) {
+    const char* what = "engram_wkv_mx_gate";
+    if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", what);
+    if (K < 3 * kSlabCols || K % kSlabCols != 0)
+        return fail(ENGRAM_EINVAL, "%s: K=%d must be a multiple of %d, at least %d", what, K, kSlabCols, 3 * kSlabCols);
+    if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "%s: hc=%d outside [1, 64]", what, hc);
+    if (dim < 256 || dim % 256 != 0)
+        return fail(ENGRAM_EINVAL, "%s: dim=%d must be a positive multiple of 256", what, dim);
+    if (ld_value < dim || ld_value % 8 != 0)
+        return fail(ENGRAM_EINVAL, "%s: ld_value=%lld must be >= dim and a multiple of 8", what, (long long)ld_value);
+    const int64_t need = engram_wkv_gate_workspace_bytes(T, hc, dim);
+    if (workspace_bytes < need)
+        return fail(ENGRAM_ERANGE, "%s: workspace of %lld bytes, %lld needed", what, (long long)workspace_bytes,
+                    (long long)need);
+    if (T == 0) return ENGRAM_OK;
+    if (!a || !a_scale || !w || !w_scale || !x || !q_weight || !k_weight || !value || !dot || !workspace)
+        return fail(ENGRAM_EINVAL, "%s: null pointer", what);
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_scale, 16) || !aligned(w_scale, 16) || !aligned(x, 16) ||
+        !aligned(q_weight, 16) || !aligned(k_weight, 16) || !aligned(value, 16) || !aligned(dot, 4) ||
+        !aligned(workspace, 16))
+        return fail(ENGRAM_EINVAL, "%s: misaligned pointer", what);
+    const int Nout = (hc + 1) * dim;
+    const int64_t tiles_m = (T + BM - 1) / BM;
+    if (tiles_m * (Nout / BN) > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
+    // launch 1: the hc * dim key rows of w, reduced against the stream (every tile a key tile)
+    MxArgs p = {};
+    p.a = a;
+    p.as = a_scale;
+    p.w = w;
+    p.ws = w_scale;
+    p.M = T;
+    p.N = hc * dim;
+    p.K = K;
+    p.M4 = (T + 3) / 4 * 4;
+    p.N4 = Nout;  // w's scale rows (Nout is a multiple of 256)
+    p.x = x;
+    p.q = q_weight;
+    p.k = k_weight;
+    p.part = static_cast<float*>(workspace);
+    p.hc = hc;
+    p.dim = dim;
+    p.tiles_m = static_cast<int>(tiles_m);
+    p.tiles_n = p.N / BN;
+    int64_t tiles = tiles_m * p.tiles_n;
+    hipLaunchKernelGGL(wkv_mx_gate_kernel, dim3(static_cast<unsigned>(tiles < kCUs ? tiles : kCUs)), dim3(kThreads),
+                       0, as_stream(stream), p);
+    int rc = check_launch(what);
+    if (rc != ENGRAM_OK) return rc;
+    // launch 2: the dim value rows of w (rows hc * dim on; their scales sit at that row of every 128-column block
+    // of the scale layout, whose row count stays Nout), stored into `value`
+    MxArgs v = {};
+    v.a = a;
+    v.as = a_scale;
+    v.w = w + static_cast<int64_t>(hc) * dim * K;
+    v.ws = w_scale + static_cast<int64_t>(hc) * dim * 4;
+    v.kv = value;
+    v.M = T;
+    v.N = dim;
+    v.K = K;
+    v.M4 = p.M4;
+    v.N4 = Nout;
+    v.ld_out = ld_value;
+    v.tiles_m = p.tiles_m;
+    v.tiles_n = dim / BN;
+    tiles = tiles_m * v.tiles_n;
+    hipLaunchKernelGGL(wkv_mx_kernel, dim3(static_cast<unsigned>(tiles < kCUs ? tiles : kCUs)), dim3(kThreads),
+                       0, as_stream(stream), v);
+    rc = check_launch(what);
+    if (rc != ENGRAM_OK) return rc;
+    float* dots[1] = {dot};
+    return launch_gate_finalize(static_cast<const float*>(workspace), 0, dots, 1, T, hc, dim, eps, as_stream(stream),
+                                what);
 }

@@ -19,7 +19,8 @@ from typing import List, Optional
 
 from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
                engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_mx_quant, engram_wkv,
-               engram_wkv_gate, engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes, engram_wkv_mx)
+               engram_wkv_gate, engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes, engram_wkv_mx,
+               engram_wkv_mx_gate)
 
 
 @dataclasses.dataclass
@@ -139,10 +140,10 @@ class EngramForward:
                 hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
         return a
 
-    def layer_fp8(self, e: int, hash_ids, x, events=None, packed=False, a=None):
+    def layer_fp8(self, e: int, hash_ids, x, events=None, packed=False, a=None, fused=False):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e with the fp8 block-scaled projection:
         the gathered rows quantised to MX fp8 (engram_mx_quant), engram_wkv_mx against the layer's MX weights,
-        then engram_gate_dot."""
+        then engram_gate_dot; with `fused`, (a, value bf16 [T, dim], dot) from engram_wkv_mx_gate instead."""
         import torch
 
         lw = self.layers[e]
@@ -156,6 +157,16 @@ class EngramForward:
         aq = self._buf(("a_mx", e), (T, K), torch.uint8, dev)
         asc = self._buf(("a_mx_scale", e), (K // 128, (T + 3) // 4 * 4, 4), torch.uint8, dev)
         self._timed(events, "mx_quant", lambda: engram_mx_quant(a.view(T, K), q=aq, scale=asc))
+        if fused:
+            x3 = x.reshape(T, x.shape[-2], x.shape[-1])
+            hc, dim = x3.shape[1], x3.shape[2]
+            value = self._buf(("value", e), (T, dim), torch.bfloat16, dev)
+            dot = self._buf(("dot", e), (T, hc), torch.float32, dev)
+            ws = self._buf("workspace", (engram_wkv_gate_workspace_bytes(T, hc, dim),), torch.uint8, dev)
+            self._timed(events, "wkv_mx_gate", lambda: engram_wkv_mx_gate(
+                aq, asc, lw.wkv_mx[0], lw.wkv_mx[1], x3, lw.q_weight, lw.k_weight, self.eps, value=value, dot=dot,
+                workspace=ws))
+            return a, value, dot
         kv = self._buf(("kv", e), (T, lw.wkv.shape[0]), torch.bfloat16, dev)
         self._timed(events, "wkv_mx", lambda: engram_wkv_mx(aq, asc, lw.wkv_mx[0], lw.wkv_mx[1], out=kv))
         x3 = x.reshape(T, x.shape[-2], x.shape[-1])
@@ -211,17 +222,18 @@ class EngramForward:
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
         With `hash_gather`, the hash and every layer's packed gather are one launch; with `all_layers`
         (fused only), every layer's projection and gate pre-activation are one launch (their tiles share
-        the CUs); with `fp8`, the projection is the fp8 block-scaled form (layer_fp8; pre-activations only).
+        the CUs); with `fp8`, the projection is the fp8 block-scaled form (layer_fp8, fused or not; pre-activations
+        only).
         `events`: optional dict that collects (start, end) timing events per entry point."""
         if hash_gather:
             ids, rows = self.hash_gather(input_ids, start_pos, token_mask, events)
         else:
             ids, rows = self.hash(input_ids, start_pos, token_mask, events), [None] * self.E
         if fp8:
-            if output or fused or all_layers:
-                raise ValueError("the fp8 projection runs unfused, up to the pre-activation")
+            if output or all_layers:
+                raise ValueError("the fp8 projection runs up to the pre-activation, one launch per layer")
             return [self.layer_fp8(e, ids, xs[e] if isinstance(xs, (list, tuple)) else xs, events, packed,
-                                   rows[e])[-1] for e in range(self.E)]
+                                   rows[e], fused=fused)[-1] for e in range(self.E)]
         if all_layers:
             if not fused:
                 raise ValueError("all_layers needs the fused projection")

@@ -450,6 +450,33 @@ int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, co
                   uint16_t* kv, int64_t T, int32_t K, int32_t Nout, void* stream);
 
 /*
+ * engram_wkv_mx_gate -- engram_wkv_mx fused with the gate dot, as engram_wkv_gate
+ * is for the bf16 projection (stack-hashes page, Engram.forward: `kv`, its
+ * key/value split, `rstd`, `dot`, with the released config's fp8 `Linear`): the
+ * key columns of the product are rounded to bf16 and reduced against the stream
+ * inside the projection, never written; the value columns are stored.
+ *
+ *   kv       = engram_wkv_mx(a, w), Nout = (hc+1)*dim
+ *   value    = kv[:, hc*dim : (hc+1)*dim]                       -> value
+ *   dot[t,c] = as engram_gate_dot, with key = kv[t, c*dim : (c+1)*dim]  -> dot
+ * The value columns equal engram_wkv_mx's bit for bit; the dot equals
+ * engram_gate_dot on engram_wkv_mx's kv up to the order of its fp32 sums (per 128
+ * columns in the projection, then added in slice order by a second kernel).
+ *
+ * a, a_scale, w, w_scale  as engram_wkv_mx, w having (hc+1)*dim rows
+ * x, q_weight, k_weight, eps, value, ld_value, dot  as engram_wkv_gate
+ * workspace  at least engram_wkv_gate_workspace_bytes(T, hc, dim) bytes, 16-byte
+ *            aligned, caller-owned scratch (no initialisation needed)
+ * Limits: T >= 0; K >= 384 and K % 128 == 0; 1 <= hc <= 64; dim >= 256 and
+ * dim % 256 == 0; ld_value >= dim, ld_value % 8 == 0.  Too small a workspace ->
+ * ENGRAM_ERANGE.
+ */
+int engram_wkv_mx_gate(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                       const uint16_t* x, const uint16_t* q_weight, const uint16_t* k_weight, float eps,
+                       uint16_t* value, int64_t ld_value, float* dot, void* workspace, int64_t workspace_bytes,
+                       int64_t T, int32_t K, int32_t hc, int32_t dim, void* stream);
+
+/*
  * engram_wkv_gate_layers_noalloc -- engram_wkv_gate_layers without a workspace
  * argument, for callers that cannot allocate device memory: code recorded
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -348,3 +348,23 @@ def test_probe_library_exports_and_validates():
     assert L.engram_probe_read(FAKE, 24, FAKE, None) != 0              # not a multiple of 16
     assert L.engram_probe_read(ctypes.c_void_p(0x100008), 32, FAKE, None) != 0  # misaligned
     assert L.engram_probe_copy(FAKE, None, 32, None) != 0
+
+
+def test_mx_gate_validation():
+    L = g.lib()
+    need = L.engram_wkv_gate_workspace_bytes(10, 4, 256)
+    args = lambda **kw: dict(dict(a=FAKE, as_=FAKE, w=FAKE, ws=FAKE, x=FAKE, q=FAKE, k=FAKE, value=FAKE, ld=256,
+                                  dot=FAKE, ws_buf=FAKE, ws_bytes=need, T=10, K=384, hc=4, dim=256), **kw)
+    call = lambda a: L.engram_wkv_mx_gate(a["a"], a["as_"], a["w"], a["ws"], a["x"], a["q"], a["k"], 1e-20,
+                                          a["value"], a["ld"], a["dot"], a["ws_buf"], a["ws_bytes"], a["T"], a["K"],
+                                          a["hc"], a["dim"], None)
+    assert call(args(K=256)) == 1 and "K=256" in _err()  # at least three 128-column slabs
+    assert call(args(K=400)) == 1 and "K=400" in _err()
+    assert call(args(hc=0)) == 1 and "hc=0" in _err()
+    assert call(args(dim=320)) == 1 and "dim=320" in _err()
+    assert call(args(ld=128)) == 1 and "ld_value" in _err()
+    assert call(args(ws_bytes=need - 4)) == 2 and "workspace" in _err()
+    assert call(args(x=None)) == 1 and "null" in _err()
+    assert call(args(dot=ctypes.c_void_p(0x100002))) == 1 and "misaligned" in _err()
+    assert call(args(T=0, a=None, as_=None, w=None, ws=None, x=None, q=None, k=None, value=None, dot=None,
+                     ws_buf=None, ws_bytes=0)) == 0

@@ -173,3 +173,85 @@ def test_fp8_pipeline(gpu_device, cfg_index, n_sample):
         assert_close(dot_got, oracle.gate_dot(x_bits, kv_got, q_bits, k_bits, cfg.eps), rtol=1e-3, atol=1e-4,
                      what=f"dot (fp8, device kv) layer {e}")
         del kv_want, kv_want_bits
+    # the fused fp8 projection + gate (engram_wkv_mx_gate) as the benchmark runs it: value columns bit for bit
+    # those of the unfused kv above, the dot within the fp32 summation-order bar of the unfused one
+    kv_cols = [bits(wl.fwd._bufs[("kv", e)].view(T, -1)[sidx])[:, cfg.hc_mult * cfg.dim:] for e in range(cfg.n_layers)]
+    dots_u = [dots[e].view(T, -1)[sidx].cpu().numpy() for e in range(cfg.n_layers)]
+    dots_f = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, packed=True, fp8=True, fused=True)
+    torch.cuda.synchronize()
+    for e in range(cfg.n_layers):
+        np.testing.assert_array_equal(bits(wl.fwd._bufs[("value", e)].view(T, -1)[sidx]), kv_cols[e],
+                                      err_msg=f"fused fp8 value columns, layer {e}")
+        assert_close(dots_f[e].view(T, -1)[sidx].cpu().numpy(), dots_u[e], rtol=1e-3, atol=1e-4,
+                     what=f"fused fp8 dot, layer {e}")
+
+
+# (T, K, hc, dim): ragged token counts, one token, grids of more tiles than CUs (several key tiles per workgroup,
+# so held-back slabs and the next tile's restart run many times), K from the smallest the fused form takes
+# (three slabs) to the workloads', the workloads' dim with its 80 key column tiles
+MX_GATE_SHAPES = [(300, 384, 2, 256), (257, 1536, 4, 512), (1, 512, 1, 256), (1000, 1536, 4, 5120),
+                  (3000, 768, 3, 768), (9000, 384, 4, 1024)]
+
+
+@pytest.mark.parametrize("T,K,hc,dim", MX_GATE_SHAPES)
+def test_wkv_mx_gate_matches_the_unfused_path_and_the_oracle(gpu_device, T, K, hc, dim):
+    """engram_wkv_mx_gate against engram_wkv_mx + engram_gate_dot on the same MX operands: the value columns bit
+    for bit, the dot within the fp32 summation-order bar; the dot against the oracle's chain (the exact product
+    of the dequantised operands, rounded to bf16, then the gate) on sampled tokens; run-to-run identical."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    rng = np.random.default_rng(T * 3 + K + hc * 100 + dim)
+    N = (hc + 1) * dim
+    a = torch.from_numpy(_bf16_rows(rng, T, K, spread=6)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.normal(size=(N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    x = torch.from_numpy(rng.normal(size=(T, hc, dim)).astype(np.float32)).to(torch.bfloat16).to(gpu_device)
+    q = torch.from_numpy((1 + 0.1 * rng.normal(size=(hc, dim))).astype(np.float32)).to(torch.bfloat16).to(gpu_device)
+    k = torch.from_numpy((1 + 0.1 * rng.normal(size=(hc, dim))).astype(np.float32)).to(torch.bfloat16).to(gpu_device)
+    eps = 1e-20
+    aq, asc = g.engram_mx_quant(a.to(gpu_device))
+    wq, wsc = g.engram_mx_quant(w.to(gpu_device))
+    value, dot = g.engram_wkv_mx_gate(aq, asc, wq, wsc, x, q, k, eps)
+    kv = g.engram_wkv_mx(aq, asc, wq, wsc)
+    dot_u = g.engram_gate_dot(x, kv, q, k, eps)
+    value2, dot2 = g.engram_wkv_mx_gate(aq, asc, wq, wsc, x, q, k, eps)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(value), bits(kv)[:, hc * dim:], err_msg="value columns")
+    assert_close(dot.cpu().numpy(), dot_u.cpu().numpy(), rtol=1e-3, atol=1e-4, what="dot vs the unfused path")
+    np.testing.assert_array_equal(bits(value2), bits(value))
+    np.testing.assert_array_equal(dot2.cpu().numpy().view(np.uint32), dot.cpu().numpy().view(np.uint32))
+    sample = sample_tokens(T, min(T, 384), T + K)
+    x_bits = bits(x)[sample]
+    q_bits, k_bits = bits(q), bits(k)
+    # the fused gate arithmetic against the oracle's, both on the device's keys (engram_wkv_mx's, which the fused
+    # kernel forms with the same MFMAs in the same order): the isolating bar
+    dot_dev = oracle.gate_dot(x_bits, bits(kv)[sample], q_bits, k_bits, eps)
+    assert_close(dot.cpu().numpy()[sample], dot_dev, rtol=1e-3, atol=1e-4, what="dot vs the oracle on the device kv")
+    # end to end: the oracle's exact product of the dequantised operands, rounded to bf16, then the gate; the
+    # bar adds the fp8 matrix core's accumulation error (2^-12 sum|a w| per key element) carried through the gate
+    a_q, a_s = aq.cpu().numpy()[sample], _scales_rowmajor(asc, T, K)[sample]
+    w_q, w_s = wq.cpu().numpy(), _scales_rowmajor(wsc, N, K)
+    kv_o = oracle.wkv_mx_matmul(a_q, a_s, w_q, w_s)
+    kv_o_bits = torch.from_numpy(kv_o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    dot_o = oracle.gate_dot(x_bits, kv_o_bits, q_bits, k_bits, eps)
+    extra = _gate_bound_of_key_error(x_bits, kv_o_bits,
+                                     2.0 ** -12 * (np.abs(oracle.mx_dequant(a_q, a_s)) @ np.abs(oracle.mx_dequant(w_q, w_s)).T),
+                                     q_bits, k_bits, eps)
+    assert_close(dot.cpu().numpy()[sample], dot_o, atol=1e-3 + extra, what="dot vs the oracle")
+
+
+def _gate_bound_of_key_error(x_bits, kv_bits, key_err, q_bits, k_bits, eps):
+    """A bound on how far the gate pre-activation moves when every key element moves by at most key_err
+    [n, Nout] (first order): dot = S rh rk dim^-1/2 with S = sum(h w key), rk = (mean key^2 + eps)^-1/2, so
+    |d dot| <= dim^-1/2 rh (rk sum|h w| |d key| + |S| rk^3 mean(|key| |d key|))."""
+    hc, dim = q_bits.shape
+    n = x_bits.shape[0]
+    h = oracle.bf16_bits_to_float(x_bits).astype(np.float64).reshape(n, hc, dim)
+    key = oracle.bf16_bits_to_float(kv_bits[:, :hc * dim]).astype(np.float64).reshape(n, hc, dim)
+    dk = key_err[:, :hc * dim].reshape(n, hc, dim)
+    w = (oracle.bf16_bits_to_float(q_bits).astype(np.float64) * oracle.bf16_bits_to_float(k_bits).astype(np.float64))
+    rh = 1.0 / np.sqrt((h * h).mean(-1) + eps)
+    rk = 1.0 / np.sqrt((key * key).mean(-1) + eps)
+    S = (h * w * key).sum(-1)
+    return dim ** -0.5 * rh * (rk * (np.abs(h * w) * dk).sum(-1) + np.abs(S) * rk ** 3 * (np.abs(key) * dk).mean(-1))
