@@ -88,6 +88,14 @@ __device__ inline void tile_coords(const MxArgs& p, int pid, int& tm, int& tn) {
 }
 
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+// The lane's index formed where it is used: opaque, so the compiler neither hoists it nor keeps what is derived
+// from it live across the slab loop.  With every VGPR taken such loop-invariant values are spilled, and the
+// reload of one waits (vmcnt is in order) for every load in flight, the slab just issued included.
+__device__ inline int lane_here() {
+    int v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -181,7 +189,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                                                  (vo_rows ^ flip) + qrows, r.k0b, 0, 0);
         if (q == 0 && wave < 2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rs, st + 2 * kOpBytes + wave * kScBytes, 16,
-                                                     static_cast<uint32_t>(lane * 16), 0, 0, 0);
+                                                     static_cast<uint32_t>(lane_here() * 16), 0, 0, 0);
     };
     auto issue_slab = [&](int pid, int kt, int stage, bool live) {
         const SlabRsrc r = slab_rsrc(pid, kt, live);
@@ -209,12 +217,12 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
     // the slab's scale words of the lane's rows (raw); shift_scales then moves the lane's K half of k-step 0 /
     // k-step 1 into byte 0 / byte 2
     auto read_scales = [&](int stage, uint32_t* sa, uint32_t* sw) {
-        const uint8_t* base = lds + stage * kStageBytes + 2 * kOpBytes;
+        const uint8_t* base = lds + stage * kStageBytes + 2 * kOpBytes + (lane_here() & 31) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(base + (wm * 128 + i * 32 + (lane & 31)) * 4);
+        for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(base + (wm * 128 + i * 32) * 4);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            sw[j] = *reinterpret_cast<const uint32_t*>(base + kScBytes + (wn * 64 + j * 32 + (lane & 31)) * 4);
+            sw[j] = *reinterpret_cast<const uint32_t*>(base + kScBytes + (wn * 64 + j * 32) * 4);
     };
     auto shift_scales = [&](uint32_t* sa, uint32_t* sw) {
         const int sh = 8 * h;
@@ -273,13 +281,15 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
     // [128 wm, +128).  Lane l holds, in round i < 4, token 32i + l%32 and 32 of the slice's columns (4
     // consecutive ones per (j, gq), as the MFMA leaves them).  Each accumulator is rounded to bf16 (the product
     // is a bf16 tensor before it is used) and reduced against the stream's matching element: sum(h w key),
-    // sum(key^2), sum(h^2) over the lane's columns, then over the two lane halves.  A key tile's last two slabs
-    // issue nothing (the next tile's first two slabs are held back), so both stages are free once its last
-    // slab's barrier has passed: there each wave fetches the stream rows of its four rounds with direct-to-LDS
-    // loads -- round r in stage st (r < 2) or st ^ 1, at (r & 1) * 32 KB, the wave's 4 KB area: row t is token
-    // 32 r + t of the wave's 128, 16-byte piece q at slot q ^ ((t >> 1) & 7) -- and waits only for its own loads.
-    // Loader waves hand their sums to their SIMD partner (storer wave w + 4: the same tokens, the slice 128
-    // columns to the right), which adds them to its own and stores one value per (copy, pair of slices, token).
+    // sum(key^2), sum(h^2) over the lane's columns, then over the two lane halves.  The stream rows come in by
+    // direct-to-LDS loads that the tile's last two slabs issue (they hold back the next tile's first two, so
+    // each stage is free from the barrier of the slab that read it last): the second-to-last slab fetches the
+    // slice's q and k elements and rounds 2 and 3 into its own stage, the last slab rounds 0 and 1 into its
+    // own, st.  Round r: stage st (r < 2) or st ^ 1, at (r & 1) * 32 KB, the wave's 4 KB area; row t is token
+    // 32 r + t of the wave's 128, 16-byte piece q at slot q ^ ((t >> 1) & 7).  Each wave waits only for its own
+    // loads.  Loader waves hand their sums to their SIMD partner (storer wave w + 4: the same tokens, the slice
+    // 128 columns to the right), which adds them to its own and stores one value per (copy, pair of slices,
+    // token).
     auto own_wait = [&](auto n_tag) {  // this wave's own loads down to n outstanding; LDS reads stay after it
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(decltype(n_tag)::value));
@@ -292,53 +302,66 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto round_base = [&](int r, int st) { return lds + (r < 2 ? st : st ^ 1) * kStageBytes + (r & 1) * 8 * kXArea; };
+    // The stream rows of this wave's 128 tokens and 64 columns through a buffer resource based at token
+    // m0 + 128 wm, column n0 + 64 wn of x ([M, hc dim] bf16; the key columns n0 + 64 wn .. +63 of copy c are
+    // x's columns of the same numbers): tokens past M fall outside it and read as zero.  Lane l loads row l / 8
+    // of an 8-row group, the 16-byte piece its slot l % 8 holds under the swizzle: x_voff, flipped by 64 bytes
+    // for odd groups (the swizzle key of group g's rows is 4 g + l / 16, mod 8).
+    const uint32_t x_row_bytes = static_cast<uint32_t>(p.hc * p.dim * 2);  // < 2^24
+    const uint32_t x_voff = (lane >> 3) * x_row_bytes + (((lane & 7) ^ (lane >> 4)) << 4);
+    auto x_rsrc = [&](int64_t m0, int n0) {
+        const int64_t t0 = m0 + wm * 128;
+        const int64_t rows = min<int64_t>(128, p.M - t0);
+        const int64_t col = n0 + wn * 64;
+        const int bytes = rows > 0 ? static_cast<int>(rows * x_row_bytes - 2 * col) : 0;  // < 2^31
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + t0 * (x_row_bytes / 2) + col), 0, bytes,
+                                                 kBufferWord3);
+    };
+    // load `ins` (0..3) of round r: rows 8 ins .. 8 ins + 7 of the round's 32 tokens (the whole offset in the
+    // range-checked VGPR operand; the host keeps 128 rows of x under 2^31 bytes)
+    auto dma_piece = [&](__amdgpu_buffer_rsrc_t xr, int r, int ins, int st) {
+        uint32_t v = x_voff;
+        asm volatile("" : "+v"(v));  // formed here, not hoisted out of the tile loop as 8 live registers
+        const uint32_t voff = ((ins & 1) ? (v ^ 64u) : v) + static_cast<uint32_t>(32 * r + 8 * ins) * x_row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, round_base(r, st) + wave * kXArea + ins * 1024, 16, voff, 0, 0,
+                                                 kNonTemporal);
+    };
+    // the slice's 64 q and 64 k elements into the wave's 512 bytes of the exchange area (unused by the fused
+    // kernel): q column j at byte 2 j, k column j at 256 + 2 j; two loads of 4 bytes a lane whose upper 32
+    // lanes fall outside their 128-byte resource
+    auto dma_qk = [&](int n0, int which) {
+        const uint16_t* src = (which == 0 ? p.q : p.k) + (n0 + wn * 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, 128, kBufferWord3),
+            ex + wave * 512 + which * 256, 4, static_cast<uint32_t>(lane * 4), 0, 0, 0);
+    };
+    // The accumulators of a key tile whose last two slabs issued, in this order, the q and k loads and rounds 2
+    // and 3 (10 loads), then rounds 0 and 1 (8 loads): rounds 2 and 3 are reduced first.
     auto gate_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0, int st) {
         const int l = lane_id();
         const int c = n0 / p.dim;
-        const int col0 = n0 - c * p.dim + wn * 64;  // this wave's slice inside copy c
-        auto round_base = [&](int r) { return lds + (r < 2 ? st : st ^ 1) * kStageBytes + (r & 1) * 8 * kXArea; };
-        // q * k (exact in fp32) for the lane's 32 columns, loaded before the stream rows so that waiting for them
-        // leaves the rows in flight
-        const uint16_t* qrow = p.q + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
-        const uint16_t* krow = p.k + static_cast<int64_t>(c) * p.dim + col0 + 4 * (l >> 5);
-        u32x2 qv[2][4], kv[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                qv[j][gq] = *reinterpret_cast<const u32x2*>(qrow + 32 * j + 8 * gq);
-                kv[j][gq] = *reinterpret_cast<const u32x2*>(krow + 32 * j + 8 * gq);
-            }
-        const int64_t xstride = static_cast<int64_t>(p.hc) * p.dim;  // elements per token of x
-        const uint16_t* xs = p.x + static_cast<int64_t>(c) * p.dim + col0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int ins = 0; ins < 4; ++ins) {
-                const int rr = 8 * ins + (l >> 3);
-                const int piece = (l & 7) ^ ((rr >> 1) & 7);
-                const int64_t t = min<int64_t>(m0 + wm * 128 + 32 * r + rr, p.M - 1);  // past M: unused
-                __builtin_amdgcn_global_load_lds(xs + t * xstride + 8 * piece,
-                                                 round_base(r) + wave * kXArea + ins * 1024, 16, 0, kNonTemporal);
-            }
+        own_wait(std::integral_constant<int, 8>{});  // q, k and rounds 2 and 3 (rounds 0 and 1 may fly)
+        // q * k (exact in fp32) for the lane's 32 columns
         float wgt[2][4][4];
+        {
+            const uint8_t* qk = ex + wave * 512 + 8 * (l >> 5);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                wgt[j][gq][0] = lo_bf16(qv[j][gq][0]) * lo_bf16(kv[j][gq][0]);
-                wgt[j][gq][1] = hi_bf16(qv[j][gq][0]) * hi_bf16(kv[j][gq][0]);
-                wgt[j][gq][2] = lo_bf16(qv[j][gq][1]) * lo_bf16(kv[j][gq][1]);
-                wgt[j][gq][3] = hi_bf16(qv[j][gq][1]) * hi_bf16(kv[j][gq][1]);
-            }
+                for (int gq = 0; gq < 4; ++gq) {
+                    const u32x2 qv = *reinterpret_cast<const u32x2*>(qk + 2 * (32 * j + 8 * gq));
+                    const u32x2 kv = *reinterpret_cast<const u32x2*>(qk + 256 + 2 * (32 * j + 8 * gq));
+                    wgt[j][gq][0] = lo_bf16(qv[0]) * lo_bf16(kv[0]);
+                    wgt[j][gq][1] = hi_bf16(qv[0]) * hi_bf16(kv[0]);
+                    wgt[j][gq][2] = lo_bf16(qv[1]) * lo_bf16(kv[1]);
+                    wgt[j][gq][3] = hi_bf16(qv[1]) * hi_bf16(kv[1]);
+                }
+        }
         float res[4][3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i == 0) own_wait(std::integral_constant<int, 12>{});  // round i landed; the later rounds may fly
-            if (i == 1) own_wait(std::integral_constant<int, 8>{});
-            if (i == 2) own_wait(std::integral_constant<int, 4>{});
-            if (i == 3) own_wait(std::integral_constant<int, 0>{});
-            const uint8_t* xl = round_base(i) + wave * kXArea;
+        auto reduce = [&](auto i_tag) {
+            constexpr int i = decltype(i_tag)::value;
+            const uint8_t* xl = round_base(i, st) + wave * kXArea;
             u32x2 xr[2][4];
             {
                 const int rr = l & 31, hx = l >> 5;
@@ -369,10 +392,16 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
             res[i][0] = hwk + __shfl_xor(hwk, 32, 64);
             res[i][1] = kk + __shfl_xor(kk, 32, 64);
             res[i][2] = hh + __shfl_xor(hh, 32, 64);
-        }
-        // hand-over: a loader wave leaves its sums in its own area of round 3 (read out above); its SIMD partner
+        };
+        reduce(std::integral_constant<int, 2>{});
+        reduce(std::integral_constant<int, 3>{});
+        own_wait(std::integral_constant<int, 4>{});
+        reduce(std::integral_constant<int, 0>{});
+        own_wait(std::integral_constant<int, 0>{});
+        reduce(std::integral_constant<int, 1>{});
+        // hand-over: a loader wave leaves its sums in its own area of round 1 (read out above); its SIMD partner
         // adds them to its own and stores both
-        uint8_t* const hand = round_base(3);
+        uint8_t* const hand = round_base(1, st);
         if (loader) {
             lds_fence();
             if (l < 32) {
@@ -401,7 +430,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 }
             }
         }
-        sync_epi();  // the partner's sums and every round's rows are read before the stages are refilled
+        sync_epi();  // the partner's sums, the stream rows and q and k are read before the stages are refilled
     };
 
     if (static_cast<int>(blockIdx.x) >= tiles) return;
@@ -507,19 +536,21 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
             }
         } else {
             // One slab: k-step 0, the barrier, k-step 1.  kIssue false: the loaders issue nothing (the held-back
-            // slabs of a key tile's end); kReload false: the tile's last slab, no fragments are reloaded.
-            // kFirst: the tile's first slab (zero C operand: the accumulators are dead between tiles)
-            auto slab = [&](auto first_tag, auto issue_tag, auto reload_tag) {
+            // slabs of a key tile's end); kReload false: the tile's last slab, no fragments are reloaded and no
+            // load is waited for (its slab has landed).  kFirst: the tile's first slab (zero C operand: the
+            // accumulators are dead between tiles).  hook(u): every wave's share of k-step 1's units in a slab
+            // that issues nothing (the tile's last two: the gate epilogue's loads)
+            auto slab = [&](auto first_tag, auto issue_tag, auto reload_tag, auto&& hook) {
                 constexpr bool kIssue = decltype(issue_tag)::value;
                 constexpr bool kReload = decltype(reload_tag)::value;
                 kstep(std::integral_constant<int, 0>{}, first_tag, acc, fa, fw, sa, sw, stage, 1, no_extra,
                       std::true_type{});
-                if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+                if (kLoader && kReload) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
                 sync();
                 uint32_t sa_n[4], sw_n[2];
                 const int nst = stage ^ 1;
                 if constexpr (!kReload) {
-                    kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, no_extra,
+                    kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, hook,
                           std::false_type{});
                 } else if (kLoader && kIssue) {
                     const int nn = n + 2;
@@ -532,6 +563,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 } else {
                     kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
                         if (u == 0) read_scales(nst, sa_n, sw_n);
+                        if constexpr (!kIssue) hook(u);
                     }, std::true_type{});
                 }
                 if constexpr (kReload) {
@@ -552,12 +584,17 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 const int n0 = tn * BN;
                 using T_ = std::true_type;
                 using F_ = std::false_type;
-                // a key tile (KT >= 3): its last two slabs hold back the next tile's first two
-                slab(T_{}, T_{}, T_{});
-                for (int kt = 1; kt < KT - 2; ++kt) slab(F_{}, T_{}, T_{});
-                slab(F_{}, F_{}, T_{});
-                const int st = stage;  // the last slab's stage
-                slab(F_{}, F_{}, F_{});
+                // a key tile (KT >= 3): its last two slabs hold back the next tile's first two and fetch what the
+                // gate epilogue reads, each into its own stage once its barrier has passed
+                slab(T_{}, T_{}, T_{}, no_extra);
+                for (int kt = 1; kt < KT - 2; ++kt) slab(F_{}, T_{}, T_{}, no_extra);
+                const int st = stage ^ 1;  // the last slab's stage
+                const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
+                slab(F_{}, F_{}, T_{}, [&](int u) {
+                    if (u < 2) dma_qk(n0, u);
+                    dma_piece(xr, 2 + (u >> 2), u & 3, st);
+                });
+                slab(F_{}, F_{}, F_{}, [&](int u) { dma_piece(xr, u >> 2, u & 3, st); });
                 gate_epilogue(acc, m0, n0, st);
                 // the held-back slabs n and n + 1 of the stream (past the workgroup's last: empty issues) into the
                 // two stages; the first must land before its fragments are read, the second may still fly
@@ -713,6 +750,8 @@ extern "C" int engram_wkv_mx_gate(const uint8_t* a, const uint8_t* a_scale, cons
     if (hc < 1 || hc > 64) return fail(ENGRAM_EINVAL, "%s: hc=%d outside [1, 64]", what, hc);
     if (dim < 256 || dim % 256 != 0)
         return fail(ENGRAM_EINVAL, "%s: dim=%d must be a positive multiple of 256", what, dim);
+    if (static_cast<int64_t>(hc + 1) * dim > (1 << 22))  // 128 rows of x stay under 2^31 bytes
+        return fail(ENGRAM_EINVAL, "%s: (hc + 1) * dim = %lld exceeds 2^22", what, static_cast<long long>(hc + 1) * dim);
     if (ld_value < dim || ld_value % 8 != 0)
         return fail(ENGRAM_EINVAL, "%s: ld_value=%lld must be >= dim and a multiple of 8", what, (long long)ld_value);
     const int64_t need = engram_wkv_gate_workspace_bytes(T, hc, dim);

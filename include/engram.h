@@ -468,8 +468,8 @@ int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, co
  * workspace  at least engram_wkv_gate_workspace_bytes(T, hc, dim) bytes, 16-byte
  *            aligned, caller-owned scratch (no initialisation needed)
  * Limits: T >= 0; K >= 384 and K % 128 == 0; 1 <= hc <= 64; dim >= 256 and
- * dim % 256 == 0; ld_value >= dim, ld_value % 8 == 0.  Too small a workspace ->
- * ENGRAM_ERANGE.
+ * dim % 256 == 0; (hc+1)*dim <= 2^22; ld_value >= dim, ld_value % 8 == 0.
+ * Too small a workspace -> ENGRAM_ERANGE.
  */
 int engram_wkv_mx_gate(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
                        const uint16_t* x, const uint16_t* q_weight, const uint16_t* k_weight, float eps,

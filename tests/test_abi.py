@@ -362,6 +362,7 @@ def test_mx_gate_validation():
     assert call(args(K=400)) == 1 and "K=400" in _err()
     assert call(args(hc=0)) == 1 and "hc=0" in _err()
     assert call(args(dim=320)) == 1 and "dim=320" in _err()
+    assert call(args(hc=64, dim=65536, ld=65536, ws_bytes=1 << 40)) == 1 and "2^22" in _err()  # 128 rows of x < 2 GiB
     assert call(args(ld=128)) == 1 and "ld_value" in _err()
     assert call(args(ws_bytes=need - 4)) == 2 and "workspace" in _err()
     assert call(args(x=None)) == 1 and "null" in _err()
