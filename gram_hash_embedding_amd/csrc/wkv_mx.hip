@@ -155,11 +155,17 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         __amdgpu_buffer_rsrc_t ra, rw, rs;
         uint32_t k0b;
     };
-    auto slab_rsrc = [&](int pid, int kt, bool live) {
-        int tm, tn;
-        tile_coords(p, pid, tm, tn);
-        const int64_t m0 = static_cast<int64_t>(tm) * BM;
-        const int n0 = tn * BN;
+    // a tile of this workgroup: its first row and column; `live` false past the workgroup's last tile, whose
+    // loads are then empty (the resources hold no bytes)
+    struct TileAt {
+        int64_t m0;
+        int n0;
+        bool live;
+    };
+    auto slab_rsrc = [&](const TileAt& ta, int kt) {
+        const int64_t m0 = ta.m0;
+        const int n0 = ta.n0;
+        const bool live = ta.live;
         const int a_bytes = live ? static_cast<int>(min<int64_t>(BM, p.M - m0)) * row_bytes : 0;
         const int w_bytes = live ? min(BN, p.N - n0) * row_bytes : 0;
         SlabRsrc r;
@@ -191,8 +197,8 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rs, st + 2 * kOpBytes + wave * kScBytes, 16,
                                                      static_cast<uint32_t>(lane_here() * 16), 0, 0, 0);
     };
-    auto issue_slab = [&](int pid, int kt, int stage, bool live) {
-        const SlabRsrc r = slab_rsrc(pid, kt, live);
+    auto issue_slab = [&](const TileAt& ta, int kt, int stage) {
+        const SlabRsrc r = slab_rsrc(ta, kt);
 #pragma unroll
         for (int q = 0; q < 8; ++q) issue_part(r, stage, q);
     };
@@ -435,9 +441,13 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
 
     if (static_cast<int>(blockIdx.x) >= tiles) return;
     const int my_tiles = (tiles - 1 - static_cast<int>(blockIdx.x)) / G + 1;
-    const int total = my_tiles * KT;  // slabs of this workgroup
-    // the slab stream of this workgroup: slab number n -> (tile pid, k slab)
-    auto slab_pid = [&](int n) { return static_cast<int>(blockIdx.x) + (n / KT) * G; };
+    // this workgroup's tile t (its tile coordinates are computed once per tile, not per slab: their integer
+    // divisions run on the scalar unit)
+    auto tile_at = [&](int t) {
+        int tm, tn;
+        tile_coords(p, static_cast<int>(blockIdx.x) + (t < my_tiles ? t : 0) * G, tm, tn);
+        return TileAt{static_cast<int64_t>(tm) * BM, tn * BN, t < my_tiles};
+    };
 
     // One k-step: acc[i][j] += (W fragment j) x (A fragment i) scaled by byte kSel of the lane's scale words,
     // in W-fragment-major order; each fragment is reloaded, for k-step `ns` of stage `nst`, right after its last
@@ -474,9 +484,14 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
 
     auto run = [&](auto loader_tag) {
         constexpr bool kLoader = decltype(loader_tag)::value;
+        // the workgroup's tiles t and t + 1
+        TileAt cur = tile_at(0), nx1 = tile_at(1);
         if (kLoader) {
-            issue_slab(slab_pid(0), 0, 0, true);
-            issue_slab(slab_pid(1 < total ? 1 : 0), 1 % KT, 1, 1 < total);
+            issue_slab(cur, 0, 0);
+            if (KT > 1)
+                issue_slab(cur, 1, 1);
+            else
+                issue_slab(nx1, 0, 1);
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
         }
         sync();
@@ -484,7 +499,6 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         i32x8 fa[4], fw[2];
         uint32_t sa[4], sw[2];
         int stage = 0;
-        int n = 0;  // slab number in this workgroup's stream
         read_scales(0, sa, sw);
         shift_scales(sa, sw);
 #pragma unroll
@@ -493,12 +507,9 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         fw[1] = read_w(0, 0, 1);
         if constexpr (!kGate) {
             for (int t = 0; t < my_tiles; ++t) {
-                const int pid = static_cast<int>(blockIdx.x) + t * G;
-                int tm, tn;
-                tile_coords(p, pid, tm, tn);
-                const int64_t m0 = static_cast<int64_t>(tm) * BM;
-                const int n0 = tn * BN;
-                for (int kt = 0; kt < KT; ++kt, ++n) {
+                const int64_t m0 = cur.m0;
+                const int n0 = cur.n0;
+                for (int kt = 0; kt < KT; ++kt) {
                     // k-step 0 of the slab (its fragments and scales already in registers), reloading k-step 1's
                     if (kt == 0)
                         kstep(std::integral_constant<int, 0>{}, std::true_type{}, acc, fa, fw, sa, sw, stage, 1, no_extra, std::true_type{});
@@ -513,8 +524,12 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                     uint32_t sa_n[4], sw_n[2];
                     const int nst = stage ^ 1;
                     if (kLoader) {
-                        const int nn = n + 2;
-                        const SlabRsrc r = slab_rsrc(slab_pid(nn < total ? nn : 0), nn % KT, nn < total);
+                        // the slab after next: slab kt + 2 of this tile, or of the next one (or, when KT = 1, of the
+                        // one after)
+                        const int k2 = kt + 2;
+                        const bool in1 = k2 >= KT, in2 = k2 >= 2 * KT;
+                        const SlabRsrc r = slab_rsrc(in2 ? tile_at(t + 2) : (in1 ? nx1 : cur),
+                                                     k2 - (in2 ? 2 * KT : (in1 ? KT : 0)));
                         const int st = stage;
                         kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
                             if (u == 0) read_scales(nst, sa_n, sw_n);  // (past the last slab: stale, unused)
@@ -533,6 +548,8 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                     stage ^= 1;
                 }
                 epilogue(acc, m0, n0);
+                cur = nx1;
+                nx1 = tile_at(t + 2);
             }
         } else {
             // One slab: k-step 0, the barrier, k-step 1.  kIssue false: the loaders issue nothing (the held-back
@@ -540,6 +557,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
             // load is waited for (its slab has landed).  kFirst: the tile's first slab (zero C operand: the
             // accumulators are dead between tiles).  hook(u): every wave's share of k-step 1's units in a slab
             // that issues nothing (the tile's last two: the gate epilogue's loads)
+            int kt = 0;  // the slab's index in its tile
             auto slab = [&](auto first_tag, auto issue_tag, auto reload_tag, auto&& hook) {
                 constexpr bool kIssue = decltype(issue_tag)::value;
                 constexpr bool kReload = decltype(reload_tag)::value;
@@ -553,8 +571,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                     kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, hook,
                           std::false_type{});
                 } else if (kLoader && kIssue) {
-                    const int nn = n + 2;
-                    const SlabRsrc r = slab_rsrc(slab_pid(nn < total ? nn : 0), nn % KT, nn < total);
+                    const SlabRsrc r = slab_rsrc(cur, kt + 2);  // (an issuing slab is followed by two more)
                     const int st = stage;
                     kstep(std::integral_constant<int, 2>{}, std::false_type{}, acc, fa, fw, sa, sw, nst, 0, [&](int u) {
                         if (u == 0) read_scales(nst, sa_n, sw_n);  // (past the last slab: stale, unused)
@@ -574,20 +591,18 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                     for (int j = 0; j < 2; ++j) sw[j] = sw_n[j];
                 }
                 stage ^= 1;
-                ++n;
+                ++kt;
             };
             for (int t = 0; t < my_tiles; ++t) {
-                const int pid = static_cast<int>(blockIdx.x) + t * G;
-                int tm, tn;
-                tile_coords(p, pid, tm, tn);
-                const int64_t m0 = static_cast<int64_t>(tm) * BM;
-                const int n0 = tn * BN;
+                const int64_t m0 = cur.m0;
+                const int n0 = cur.n0;
+                kt = 0;
                 using T_ = std::true_type;
                 using F_ = std::false_type;
                 // a key tile (KT >= 3): its last two slabs hold back the next tile's first two and fetch what the
                 // gate epilogue reads, each into its own stage once its barrier has passed
                 slab(T_{}, T_{}, T_{}, no_extra);
-                for (int kt = 1; kt < KT - 2; ++kt) slab(F_{}, T_{}, T_{}, no_extra);
+                while (kt < KT - 2) slab(F_{}, T_{}, T_{}, no_extra);
                 const int st = stage ^ 1;  // the last slab's stage
                 const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
                 slab(F_{}, F_{}, T_{}, [&](int u) {
@@ -596,11 +611,13 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 });
                 slab(F_{}, F_{}, F_{}, [&](int u) { dma_piece(xr, u >> 2, u & 3, st); });
                 gate_epilogue(acc, m0, n0, st);
-                // the held-back slabs n and n + 1 of the stream (past the workgroup's last: empty issues) into the
+                // the held-back slabs 0 and 1 of the next tile (past the workgroup's last: empty issues) into the
                 // two stages; the first must land before its fragments are read, the second may still fly
+                cur = nx1;
+                nx1 = tile_at(t + 2);
                 if (kLoader) {
-                    issue_slab(slab_pid(n < total ? n : 0), n % KT, stage, n < total);
-                    issue_slab(slab_pid(n + 1 < total ? n + 1 : 0), (n + 1) % KT, stage ^ 1, n + 1 < total);
+                    issue_slab(cur, 0, stage);
+                    issue_slab(cur, 1, stage ^ 1);
                     if (wave < 2)
                         __builtin_amdgcn_s_waitcnt(wait_vmcnt(17));  // (waves 0 and 1 also load a slab's scales)
                     else
