@@ -77,6 +77,8 @@ def algorithmic(cfg, has_mask: bool):
         "hash_bytes": 8 + (1 if has_mask else 0) + 8 + 8 + 8 * E * C,
         # per column: int64 id in, D fp8 bytes + D/blk fp32 scales gathered, D bf16 out
         "gather_bytes": C * (8 + D + 4 * (D // blk) + 2 * D),
+        # the same gathered, written as MX fp8: D E4M3 bytes and D/32 E8M0 bytes out per column
+        "gather_mx_bytes": C * (8 + D + 4 * (D // blk) + D + D // 32),
         "wkv_flops": 2 * cfg.K * cfg.n_out,
         # A row in, kv row out (the W read is once per launch, added separately)
         "wkv_bytes": 2 * cfg.K + 2 * cfg.n_out,
@@ -288,20 +290,20 @@ def measure_workload(cfg, args, dev, peaks, full: bool) -> dict:
     torch.cuda.synchronize()
     log(f"workload ready in {time.perf_counter() - t_build:.1f} s")
 
-    def make_step(fused, output, packed, hg=False, al=False, f8=False):
+    def make_step(fused, output, packed, hg=False, al=False, f8=False, gmx=False):
         def step(events=None):
             if cfg.decode_steps:
                 for s in range(cfg.decode_steps):
                     fwd.step(step_ids[s], cfg.start_pos + s, wl.x[s], None, events=events, output=output,
-                             fused=fused, packed=packed, hash_gather=hg, all_layers=al, fp8=f8)
+                             fused=fused, packed=packed, hash_gather=hg, all_layers=al, fp8=f8, gather_mx=gmx)
             else:
                 fwd.step(wl.input_ids, cfg.start_pos, wl.x[0], wl.token_mask, events=events, output=output,
-                         fused=fused, packed=packed, hash_gather=hg, all_layers=al, fp8=f8)
+                         fused=fused, packed=packed, hash_gather=hg, all_layers=al, fp8=f8, gather_mx=gmx)
         return step
 
-    def loop(fused, output, packed, hg=False, al=False, f8=False):
+    def loop(fused, output, packed, hg=False, al=False, f8=False, gmx=False):
         """warmup, then `steps` timed steps; (seconds per step, {kernel: [(start, end) events]})"""
-        step = make_step(fused, output, packed, hg, al, f8)
+        step = make_step(fused, output, packed, hg, al, f8, gmx)
         for _ in range(args.warmup):
             step()
         events = {}
@@ -326,21 +328,23 @@ def measure_workload(cfg, args, dev, peaks, full: bool) -> dict:
         variants.append(("fused_hash_gather", True, False))
     if cfg.n_layers > 1:
         variants += [(n + "_layers", hg, True) for n, hg, _ in variants]
-    runs = [(n, True, False, main_packed, hg, al, False) for n, hg, al in variants]
+    runs = [(n, True, False, main_packed, hg, al, False, False) for n, hg, al in variants]
     if full:
         runs += [("fused_" + ("pages_table" if main_packed else "packed_table"), True, False, not main_packed, False,
-                  False, False),
-                 ("unfused", False, False, main_packed, False, False, False),
-                 ("module_fused", True, True, main_packed, False, False, False),
-                 ("module_unfused", False, True, main_packed, False, False, False)]
+                  False, False, False),
+                 ("unfused", False, False, main_packed, False, False, False, False),
+                 ("module_fused", True, True, main_packed, False, False, False, False),
+                 ("module_unfused", False, True, main_packed, False, False, False, False)]
     if fp8:
         # the fp8 block-scaled projection (gathered rows quantised to MX fp8, engram_wkv_mx, engram_gate_dot)
-        runs.append(("fp8_unfused", False, False, main_packed, False, False, True))
-        # and fused (engram_wkv_mx_gate: keys reduced in the projection), where K allows it
+        runs.append(("fp8_unfused", False, False, main_packed, False, False, True, False))
+        # and fused (engram_wkv_mx_gate: keys reduced in the projection), where K allows it; then with the
+        # gathers writing MX fp8 rows themselves (engram_gather_mx: no bf16 rows, no quantiser pass)
         if cfg.K >= 384:
-            runs.append(("fp8_fused", True, False, main_packed, False, False, True))
-    for name, fused, output, packed, hg, al, f8 in runs:
-        sec, ev = loop(fused, output, packed, hg, al, f8)
+            runs.append(("fp8_fused", True, False, main_packed, False, False, True, False))
+            runs.append(("fp8_fused_gather_mx", True, False, main_packed, False, False, True, True))
+    for name, fused, output, packed, hg, al, f8, gmx in runs:
+        sec, ev = loop(fused, output, packed, hg, al, f8, gmx)
         paths[name] = {"ms_per_step": round(1e3 * sec, 4), "tokens_per_s": round(T / sec, 1),
                        "table": "packed" if packed else "pages"}
         if f8:
@@ -398,6 +402,11 @@ def measure_workload(cfg, args, dev, peaks, full: bool) -> dict:
         if name in kern:
             g = kern[name]
             g["GB/s"] = round(T_launch * algo["gather_bytes"] / (g["avg_us"] * 1e3), 1)
+            g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
+    for name in ("gather_mx", "gather_mx_packed"):
+        if name in kern:
+            g = kern[name]
+            g["GB/s"] = round(T_launch * algo["gather_mx_bytes"] / (g["avg_us"] * 1e3), 1)
             g["frac_hbm"] = round(g["GB/s"] / PEAK_HBM_GBS, 4)
     if "hash_gather" in kern:  # the hash and every layer's gather in one launch (ids not read back)
         hg = kern["hash_gather"]

@@ -21,6 +21,7 @@ an exception is raised.
     engram_wkv_gate_layers_noalloc -- the same with the library's own device scratch (allocates nothing)
     engram_gate_residual   -- gate, token mask and residual add from a given dot
     engram_mx_quant        -- bf16 rows -> OCP MX fp8 (E4M3 + E8M0 scale per 32 columns)
+    engram_gather_mx       -- the gather + dequant writing its rows as MX fp8 (no bf16 tensor)
     engram_wkv_mx          -- the wkv projection on MX fp8 operands (fp8 matrix cores with block scales)
     engram_wkv_mx_gate     -- engram_wkv_mx fused with the gate dot (keys reduced in the projection)
 """
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.engram_mx_scale_bytes.argtypes = [i64, i32]
         L.engram_mx_scale_bytes.restype = i64
         L.engram_mx_quant.argtypes = [p, i64, i32, p, p, p]
+        L.engram_gather_mx.argtypes = [p, i64, i64, i32, p, p, i64, i64, i32, i32, p, p, p]
+        L.engram_gather_mx_packed.argtypes = [p, i64, i64, i32, p, i64, i64, i32, i32, p, p, p]
         L.engram_wkv_mx.argtypes = [p, p, p, p, p, i64, i32, i32, p]
         L.engram_wkv_mx_gate.argtypes = [p, p, p, p, p, p, p, f32, p, i64, p, p, i64, i64, i32, i32, i32, p]
         L.engram_wkv_gate_workspace_bytes.argtypes = [i64, i32, i32]
@@ -441,6 +444,50 @@ def engram_mx_quant(x, q=None, scale=None, stream=None):
     return q, scale
 
 
+def engram_gather_mx(hash_ids, weight=None, scale=None, table=None, block_size=32, row_start=0, n_cols=None, layer=0,
+                     q=None, q_scale=None, stream=None):
+    """One layer's gathered rows as MX fp8: (q uint8 [T, C*D], q_scale uint8 [C*D/128, rows4, 4]) =
+    engram_mx_quant(engram_gather_dequant(...)) bit for bit, without the bf16 tensor.  The table is `weight`
+    (float8_e4m3fn or uint8 [R, D]) with `scale` (float32 [R, D/block_size]), or the packed `table`
+    (uint8 [R, 2*D]).  int64 ids as engram_gather_dequant's."""
+    import torch
+
+    if hash_ids.dtype != torch.int64:
+        raise ValueError("hash_ids must be int64")
+    T, C, stride, ids_ptr = _gather_ids(hash_ids, n_cols, layer)
+    if (table is None) == (weight is None):
+        raise ValueError("give either weight and scale or the packed table")
+    if table is not None:
+        R, D2 = table.shape
+        D = D2 // 2
+    else:
+        if weight.dtype == torch.float8_e4m3fn:
+            weight = weight.view(torch.uint8)
+        R, D = weight.shape
+        if scale is None or tuple(scale.shape) != (R, D // block_size):
+            raise ValueError("scale must be [R, D/block_size]")
+    K = C * D
+    nbytes = engram_mx_scale_bytes(T, K)
+    if q is None:
+        q = torch.empty((T, K), dtype=torch.uint8, device=hash_ids.device)
+    if q_scale is None:
+        q_scale = torch.empty((K // 128, (T + 3) // 4 * 4, 4), dtype=torch.uint8, device=hash_ids.device)
+    if q.numel() != T * K:
+        raise ValueError("q must hold T * C * D bytes")
+    if q_scale.numel() != nbytes:
+        raise ValueError(f"q_scale must hold {nbytes} bytes")
+    if table is not None:
+        _check(lib().engram_gather_mx_packed(
+            ids_ptr, T, stride, C, _dev(table, "table", torch.uint8, 2), R, int(row_start), D, int(block_size),
+            _dev(q, "q", torch.uint8), _dev(q_scale, "q_scale", torch.uint8), _stream(stream)))
+    else:
+        _check(lib().engram_gather_mx(
+            ids_ptr, T, stride, C, _dev(weight, "weight", torch.uint8, 2), _dev(scale, "scale", torch.float32, 2),
+            R, int(row_start), D, int(block_size), _dev(q, "q", torch.uint8), _dev(q_scale, "q_scale", torch.uint8),
+            _stream(stream)))
+    return q, q_scale
+
+
 def engram_wkv_mx(a, a_scale, w, w_scale, out=None, stream=None):
     """kv bf16 [T, Nout] from MX fp8 operands a (uint8 [T, K]) and w (uint8 [Nout, K]) with their scales."""
     import torch
@@ -661,6 +708,6 @@ def engram_gate_residual(x, value, dot, token_mask=None, out=None, stream=None):
 
 __all__ = ["engram_hash", "engram_hash_gather_packed", "engram_gather_dequant", "engram_wkv", "engram_gate_dot", "engram_gate_output",
            "engram_wkv_gate", "engram_wkv_gate_layers", "engram_wkv_gate_layers_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "engram_wkv_gate_workspace_bytes", "engram_gather_dequant_fmt", "SCALE_FORMATS", "engram_mx_quant", "engram_wkv_mx", "engram_wkv_mx_gate", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
+           "engram_wkv_gate_workspace_bytes", "engram_gather_dequant_fmt", "SCALE_FORMATS", "engram_mx_quant", "engram_gather_mx", "engram_wkv_mx", "engram_wkv_mx_gate", "engram_mx_scale_bytes", "engram_gate_residual", "engram_pack_table",
            "engram_gather_dequant_packed", "EngramError", "lib",
            "LIB_PATH"]

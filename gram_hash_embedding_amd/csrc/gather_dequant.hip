@@ -27,7 +27,14 @@
 //   for 72 used.  A packed record of 2*D bytes holds the row and then its
 //   scales (zero padded), aligned to its size: at D <= 64 a lookup touches one
 //   line.  The dequant is the same code, so the outputs are bit-identical.
+// - MX output (engram_gather_mx): the dequantised bf16 values are encoded
+//   as OCP MX fp8 in the kernel (mx.h, the quantiser's code) and written as
+//   the fp8 projection's A operand -- D bytes per row and one E8M0 byte per
+//   32 columns in the [K/128][rows4][4] scale layout -- instead of 2 D bytes
+//   of bf16 that a second pass would read back and quantise.  The two lanes
+//   of a 32-column block combine their amax with one lane swap.
 #include "dequant.h"
+#include "mx.h"
 
 namespace engram {
 namespace {
@@ -46,6 +53,9 @@ struct GatherArgs {
     uint16_t* out;
     uint8_t* out_fp8;
     void* out_scale;        // the gathered scale elements as stored, or null
+    uint8_t* mx_q;          // MX output: fp8 [T, C*D] and E8M0 [C*D/128][rows4][4]
+    uint8_t* mx_scale;
+    int64_t rows4;
 };
 
 // Block scale formats of the table: 32-bit float, E8M0 (2^(s-127); 0xFF NaN) and float8_e4m3fn.
@@ -61,7 +71,7 @@ __device__ inline float decode_scale(uint32_t s) {
         return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(s), 0);
 }
 
-template <int D, int U, bool kPacked, int SF = kScaleF32, typename IdT = int64_t>
+template <int D, int U, bool kPacked, int SF = kScaleF32, typename IdT = int64_t, bool kMx = false>
 __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) {
     constexpr int LPR = D / 16;              // lanes per row
     constexpr int RPS = kThreads / LPR;      // rows per step of the block
@@ -73,11 +83,15 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
     int64_t row[U];
     bool ok[U];
     bool live[U];
+    int64_t tok[U];
+    int col[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t w = base + static_cast<int64_t>(u) * RPS;
         live[u] = w < a.W;
         int64_t id = 0;
+        tok[u] = 0;
+        col[u] = 0;
         if (live[u]) {
             int64_t t, c;
             if (a.W <= 0xFFFFFFFFll) {
@@ -90,6 +104,8 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
                 c = w - t * a.C;
             }
             id = __builtin_nontemporal_load(static_cast<const IdT*>(a.ids) + t * a.stride + c);
+            tok[u] = t;
+            col[u] = static_cast<int>(c);
         }
         const int64_t local = id - a.row_start;
         ok[u] = live[u] && local >= 0 && local < a.R;
@@ -116,6 +132,38 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
         }
     }
 
+    if constexpr (kMx) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // every lane runs the block's amax exchange (its partner lane has the same row, hence the same
+            // `live`); only live rows store
+            u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+            if (ok[u]) dequant16(v[u], sc[u], o0, o1);
+            float f[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(o0[i] << 16);
+                f[2 * i + 1] = __uint_as_float(o0[i] & 0xFFFF0000u);
+                f[8 + 2 * i] = __uint_as_float(o1[i] << 16);
+                f[8 + 2 * i + 1] = __uint_as_float(o1[i] & 0xFFFF0000u);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // lanes 2j, 2j + 1 of a row: its 32-column block j
+            const int shared = mx_shared_exp(amax);
+            const u32x4 qv = {mx_encode4(f[0], f[1], f[2], f[3], shared), mx_encode4(f[4], f[5], f[6], f[7], shared),
+                              mx_encode4(f[8], f[9], f[10], f[11], shared),
+                              mx_encode4(f[12], f[13], f[14], f[15], shared)};
+            if (!live[u]) continue;
+            const int64_t w = base + static_cast<int64_t>(u) * RPS;
+            __builtin_nontemporal_store(qv, reinterpret_cast<u32x4*>(a.mx_q + w * D + lane_in_row * 16));
+            if ((lane_in_row & 1) == 0)
+                a.mx_scale[mx_scale_offset(tok[u], (col[u] * D + lane_in_row * 16) / 32, a.rows4)] =
+                    static_cast<uint8_t>(shared + 127);
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!live[u]) continue;
@@ -140,15 +188,26 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(GatherArgs a) 
     }
 }
 
-template <int D, bool kPacked, int SF = kScaleF32, typename IdT = int64_t>
+template <int D, bool kPacked, int SF = kScaleF32, typename IdT = int64_t, bool kMx = false>
 int launch(const GatherArgs& a, hipStream_t stream, const char* name) {
     constexpr int U = 1;
     constexpr int rows_per_block = (kThreads / (D / 16)) * U;
     const int64_t blocks = (a.W + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many rows", name);
-    hipLaunchKernelGGL((gather_dequant_kernel<D, U, kPacked, SF, IdT>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((gather_dequant_kernel<D, U, kPacked, SF, IdT, kMx>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a);
     return check_launch(name);
+}
+
+// the MX-output gather (fp32 scales, int64 ids), D dispatched here
+template <bool kPacked>
+int launch_mx(const GatherArgs& a, int D, hipStream_t s, const char* name) {
+    switch (D) {
+        case 32: return launch<32, kPacked, kScaleF32, int64_t, true>(a, s, name);
+        case 64: return launch<64, kPacked, kScaleF32, int64_t, true>(a, s, name);
+        case 128: return launch<128, kPacked, kScaleF32, int64_t, true>(a, s, name);
+        default: return launch<256, kPacked, kScaleF32, int64_t, true>(a, s, name);
+    }
 }
 
 // the two-tensor gather for a scale format and id type (D dispatched here)
@@ -196,7 +255,8 @@ namespace {
 int gather_entry(const char* name, bool packed, const void* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
                  const uint8_t* weight, const void* scale, int64_t R, int64_t row_start, int32_t D, int32_t blk,
                  uint16_t* out_bf16, uint8_t* out_fp8, void* out_scale, void* stream, int scale_format = 0,
-                 int id_bytes = 8) {
+                 int id_bytes = 8, uint8_t* mx_q = nullptr, uint8_t* mx_scale = nullptr) {
+    const bool mx = mx_q != nullptr || mx_scale != nullptr;
     if (T < 0) return fail(ENGRAM_EINVAL, "%s: T < 0", name);
     if (C < 1 || C > 1024) return fail(ENGRAM_EINVAL, "%s: C=%d outside [1, 1024]", name, C);
     if (id_token_stride < C) return fail(ENGRAM_EINVAL, "%s: id_token_stride < C", name);
@@ -205,11 +265,15 @@ int gather_entry(const char* name, bool packed, const void* hash_ids, int64_t T,
     if (blk < 16 || blk % 16 != 0 || D % blk != 0)
         return fail(ENGRAM_EINVAL, "%s: blk=%d must be a multiple of 16 dividing D=%d", name, blk, D);
     if (R < 1) return fail(ENGRAM_EINVAL, "%s: R < 1", name);
+    if (mx && (static_cast<int64_t>(C) * D) % 128 != 0)
+        return fail(ENGRAM_EINVAL, "%s: C*D=%lld must be a multiple of 128", name, static_cast<long long>(C) * D);
     if (T == 0) return ENGRAM_OK;
-    if (!hash_ids || !weight || (!packed && !scale) || !out_bf16) return fail(ENGRAM_EINVAL, "%s: null pointer", name);
+    if (!hash_ids || !weight || (!packed && !scale) || (mx ? (!mx_q || !mx_scale) : !out_bf16))
+        return fail(ENGRAM_EINVAL, "%s: null pointer", name);
     const int sbytes = scale_format == 0 ? 4 : 1;
     if (!aligned(hash_ids, id_bytes) || !aligned(weight, packed ? 2 * D : 16) || (!packed && !aligned(scale, sbytes)) ||
-        !aligned(out_bf16, 16) || (out_fp8 && !aligned(out_fp8, 16)) || (out_scale && !aligned(out_scale, sbytes)))
+        (out_bf16 && !aligned(out_bf16, 16)) || (out_fp8 && !aligned(out_fp8, 16)) ||
+        (out_scale && !aligned(out_scale, sbytes)) || (mx_q && !aligned(mx_q, 16)))
         return fail(ENGRAM_EINVAL, "%s: misaligned pointer", name);
 
     GatherArgs a;
@@ -225,7 +289,11 @@ int gather_entry(const char* name, bool packed, const void* hash_ids, int64_t T,
     a.out = out_bf16;
     a.out_fp8 = out_fp8;
     a.out_scale = out_scale;
+    a.mx_q = mx_q;
+    a.mx_scale = mx_scale;
+    a.rows4 = (T + 3) / 4 * 4;
     hipStream_t s = as_stream(stream);
+    if (mx) return packed ? launch_mx<true>(a, D, s, name) : launch_mx<false>(a, D, s, name);
     if (packed) {
         switch (D) {
             case 32: return launch<32, true>(a, s, name);
@@ -271,6 +339,20 @@ extern "C" int engram_gather_dequant_packed(const int64_t* hash_ids, int64_t T, 
                                             void* stream) {
     return gather_entry("engram_gather_dequant_packed", true, hash_ids, T, id_token_stride, C, table, nullptr, R,
                         row_start, D, blk, out_bf16, out_fp8, out_scale, stream);
+}
+
+extern "C" int engram_gather_mx(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                const uint8_t* weight, const float* scale, int64_t R, int64_t row_start, int32_t D,
+                                int32_t blk, uint8_t* q, uint8_t* q_scale, void* stream) {
+    return gather_entry("engram_gather_mx", false, hash_ids, T, id_token_stride, C, weight, scale, R, row_start, D,
+                        blk, nullptr, nullptr, nullptr, stream, 0, 8, q, q_scale);
+}
+
+extern "C" int engram_gather_mx_packed(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                                       const uint8_t* table, int64_t R, int64_t row_start, int32_t D, int32_t blk,
+                                       uint8_t* q, uint8_t* q_scale, void* stream) {
+    return gather_entry("engram_gather_mx_packed", true, hash_ids, T, id_token_stride, C, table, nullptr, R, row_start,
+                        D, blk, nullptr, nullptr, nullptr, stream, 0, 8, q, q_scale);
 }
 
 extern "C" int engram_pack_table(const uint8_t* weight, const float* scale, int64_t R, int32_t D, int32_t blk,

@@ -26,6 +26,7 @@
 #include <utility>
 
 #include "common.h"
+#include "mx.h"
 
 namespace engram {
 namespace {
@@ -646,10 +647,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_mx_gate_kernel(MxArgs p) { wk
 
 // ---- OCP MX quantisation of bf16 rows ----
 // A thread owns 8 consecutive columns (one 16-byte load); the 4 threads of a 32-column block reduce their
-// amax with two lane swaps.  The shared exponent floor(log2 amax) - 8 is read off amax's fp32 exponent field
-// (amax is a bf16 value, so it is normal or a bf16 subnormal, which fp32 holds exactly); the scaled element
-// x * 2^-e is formed exactly by ldexp, clamped to +-448 and rounded to E4M3 (nearest even) by the
-// hardware conversion.
+// amax with two lane swaps; the block is then encoded by mx_shared_exp / mx_encode4 (mx.h).
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* x, int64_t rows, int K, int64_t rows4,
                                                       uint8_t* q, uint8_t* scale) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -671,31 +669,12 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* x, int64_
     // the 4 threads of a block are lanes 4b .. 4b+3 of the wave (K / 8 is a multiple of 4)
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    int shared = -127;
-    if (amax > 0.f) {
-        const uint32_t au = __float_as_uint(amax);
-        const int ef = static_cast<int>(au >> 23);
-        const int fl = ef != 0 ? ef - 127 : 31 - __builtin_clz(au & 0x7FFFFFu) - 149;  // floor(log2 amax)
-        shared = max(-127, min(127, fl - 8));
-    }
-    // x 2^-shared is exact (a power of two; results below fp32's normal range round to 0 in E4M3 either way);
-    // clamped to +-448 it converts without overflow, rounded to nearest even by v_cvt_pk_fp8_f32 (OCP E4M3 on
-    // gfx950, subnormals included) -- the saturating conversion
-    float g[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) g[i] = __builtin_amdgcn_fmed3f(__builtin_ldexpf(f[i], -shared), -448.0f, 448.0f);
-    uint32_t packed[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(g[4 * h], g[4 * h + 1], 0, false);
-        packed[h] = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(g[4 * h + 2], g[4 * h + 3], lo, true));
-    }
+    const int shared = mx_shared_exp(amax);
+    const uint32_t p0 = mx_encode4(f[0], f[1], f[2], f[3], shared);
+    const uint32_t p1 = mx_encode4(f[4], f[5], f[6], f[7], shared);
     if (!ok) return;
-    *reinterpret_cast<u32x2*>(q + r * K + 8 * c8) = u32x2{packed[0], packed[1]};
-    if ((c8 & 3) == 0) {
-        const int b = c8 / 4;  // the 32-column block
-        scale[((static_cast<int64_t>(b / 4) * rows4 + r) * 4) + (b & 3)] = static_cast<uint8_t>(shared + 127);
-    }
+    *reinterpret_cast<u32x2*>(q + r * K + 8 * c8) = u32x2{p0, p1};
+    if ((c8 & 3) == 0) scale[mx_scale_offset(r, c8 / 4, rows4)] = static_cast<uint8_t>(shared + 127);
 }
 
 }  // namespace

@@ -18,9 +18,9 @@ import dataclasses
 from typing import List, Optional
 
 from . import (engram_gate_dot, engram_gate_output, engram_gate_residual, engram_gather_dequant,
-               engram_gather_dequant_packed, engram_hash, engram_hash_gather_packed, engram_mx_quant, engram_wkv,
-               engram_wkv_gate, engram_wkv_gate_layers, engram_wkv_gate_workspace_bytes, engram_wkv_mx,
-               engram_wkv_mx_gate)
+               engram_gather_dequant_packed, engram_gather_mx, engram_hash, engram_hash_gather_packed,
+               engram_mx_quant, engram_wkv, engram_wkv_gate, engram_wkv_gate_layers,
+               engram_wkv_gate_workspace_bytes, engram_wkv_mx, engram_wkv_mx_gate)
 
 
 @dataclasses.dataclass
@@ -140,10 +140,11 @@ class EngramForward:
                 hash_ids, lw.weight, lw.scale, lw.block_size, lw.row_start, layer=e, out=a))
         return a
 
-    def layer_fp8(self, e: int, hash_ids, x, events=None, packed=False, a=None, fused=False):
+    def layer_fp8(self, e: int, hash_ids, x, events=None, packed=False, a=None, fused=False, gather_mx=False):
         """(a bf16 [T, C*D], kv bf16 [T, Nout], dot fp32 [T, hc]) of layer e with the fp8 block-scaled projection:
         the gathered rows quantised to MX fp8 (engram_mx_quant), engram_wkv_mx against the layer's MX weights,
-        then engram_gate_dot; with `fused`, (a, value bf16 [T, dim], dot) from engram_wkv_mx_gate instead."""
+        then engram_gate_dot; with `fused`, (a, value bf16 [T, dim], dot) from engram_wkv_mx_gate instead.
+        With `gather_mx` (and no `a`), the gather writes the MX rows itself (engram_gather_mx) and `a` is None."""
         import torch
 
         lw = self.layers[e]
@@ -151,12 +152,24 @@ class EngramForward:
             raise ValueError(f"layer {e} has no fp8 (MX) projection weights")
         T = hash_ids.shape[0] * hash_ids.shape[1]
         dev = hash_ids.device
-        if a is None:
-            a = self.gather(e, hash_ids, events, packed)
-        K = a.numel() // T
+        K = self.C * lw.weight.shape[1]
         aq = self._buf(("a_mx", e), (T, K), torch.uint8, dev)
         asc = self._buf(("a_mx_scale", e), (K // 128, (T + 3) // 4 * 4, 4), torch.uint8, dev)
-        self._timed(events, "mx_quant", lambda: engram_mx_quant(a.view(T, K), q=aq, scale=asc))
+        if a is None and gather_mx:
+            if packed:
+                if lw.packed is None:
+                    raise ValueError(f"layer {e} has no packed table")
+                self._timed(events, "gather_mx_packed", lambda: engram_gather_mx(
+                    hash_ids, table=lw.packed, block_size=lw.block_size, row_start=lw.row_start, layer=e, q=aq,
+                    q_scale=asc))
+            else:
+                self._timed(events, "gather_mx", lambda: engram_gather_mx(
+                    hash_ids, lw.weight, lw.scale, block_size=lw.block_size, row_start=lw.row_start, layer=e, q=aq,
+                    q_scale=asc))
+        else:
+            if a is None:
+                a = self.gather(e, hash_ids, events, packed)
+            self._timed(events, "mx_quant", lambda: engram_mx_quant(a.view(T, K), q=aq, scale=asc))
         if fused:
             x3 = x.reshape(T, x.shape[-2], x.shape[-1])
             hc, dim = x3.shape[1], x3.shape[2]
@@ -216,14 +229,14 @@ class EngramForward:
         return a, kv, dot
 
     def step(self, input_ids, start_pos: int, xs, token_mask=None, events=None, output=False, fused=False,
-             packed=False, hash_gather=False, all_layers=False, fp8=False):
+             packed=False, hash_gather=False, all_layers=False, fp8=False, gather_mx=False):
         """One forward over all engram layers; xs[e] is layer e's residual stream [B, L, hc, dim]
         (or one tensor shared by all layers).  Returns the per-layer gate pre-activations, or with
         `output` the per-layer output streams (the pre-activations are then in the "dot" buffers).
         With `hash_gather`, the hash and every layer's packed gather are one launch; with `all_layers`
         (fused only), every layer's projection and gate pre-activation are one launch (their tiles share
         the CUs); with `fp8`, the projection is the fp8 block-scaled form (layer_fp8, fused or not; pre-activations
-        only).
+        only), and with `gather_mx` its gathers write MX fp8 rows directly.
         `events`: optional dict that collects (start, end) timing events per entry point."""
         if hash_gather:
             ids, rows = self.hash_gather(input_ids, start_pos, token_mask, events)
@@ -233,7 +246,7 @@ class EngramForward:
             if output or all_layers:
                 raise ValueError("the fp8 projection runs up to the pre-activation, one launch per layer")
             return [self.layer_fp8(e, ids, xs[e] if isinstance(xs, (list, tuple)) else xs, events, packed,
-                                   rows[e], fused=fused)[-1] for e in range(self.E)]
+                                   rows[e], fused=fused, gather_mx=gather_mx)[-1] for e in range(self.E)]
         if all_layers:
             if not fused:
                 raise ValueError("all_layers needs the fused projection")

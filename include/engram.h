@@ -35,7 +35,11 @@
  * the fp8 block-scaled (OCP MX) form of the `wkv` Linear:
  *
  *   engram_mx_quant        -- bf16 rows to MX fp8 (E4M3 + an E8M0 scale per 32 columns)
+ *   engram_gather_mx, engram_gather_mx_packed
+ *                          -- the gather + dequant writing its rows as MX fp8
+ *                             (engram_mx_quant of engram_gather_dequant's rows)
  *   engram_wkv_mx          -- the projection on MX fp8 operands
+ *   engram_wkv_mx_gate     -- engram_wkv_mx fused with the gate pre-activation
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -431,6 +435,32 @@ int64_t engram_mx_scale_bytes(int64_t rows, int32_t K);
  * Limits: rows >= 0; K >= 128 and K % 128 == 0.
  */
 int engram_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* q, uint8_t* scale, void* stream);
+
+/*
+ * engram_gather_mx -- engram_gather_dequant's rows as MX fp8, without the bf16
+ * tensor: q, q_scale = engram_mx_quant(engram_gather_dequant(...)) viewed as
+ * [T, K], K = C*D, bit for bit (the same bf16 values, the same encoding; an id
+ * outside the rank's rows gives a zero row: bytes 0 and scale 0).  The fp8
+ * projection's A operand straight from the table (stack-hashes page,
+ * ParallelEngramEmbedding.forward, followed by the fp8 `wkv` Linear's
+ * activation quantisation).
+ *
+ * hash_ids, T, id_token_stride, C, weight, scale, R, row_start, D, blk
+ *          as engram_gather_dequant
+ * q        uint8 [T, C*D] E4M3FN bytes, out; 16-byte aligned; caller-owned
+ * q_scale  uint8, engram_mx_scale_bytes(T, C*D) bytes in the MX scale layout,
+ *          out; caller-owned (its padding rows are not written)
+ * Limits and errors: as engram_gather_dequant, and C*D % 128 == 0.
+ */
+int engram_gather_mx(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C, const uint8_t* weight,
+                     const float* scale, int64_t R, int64_t row_start, int32_t D, int32_t blk, uint8_t* q,
+                     uint8_t* q_scale, void* stream);
+
+/* engram_gather_mx on a packed table (engram_pack_table's layout; `table` as in
+ * engram_gather_dequant_packed): the same outputs, bit for bit. */
+int engram_gather_mx_packed(const int64_t* hash_ids, int64_t T, int64_t id_token_stride, int32_t C,
+                            const uint8_t* table, int64_t R, int64_t row_start, int32_t D, int32_t blk, uint8_t* q,
+                            uint8_t* q_scale, void* stream);
 
 /*
  * engram_wkv_mx -- the projection on MX fp8 operands:

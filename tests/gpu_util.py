@@ -85,3 +85,9 @@ def compact_rows(ids: np.ndarray, R: int, table_seed: int, D: int, blk: int):
     import synth
 
     return synth.compact_table(ids, R, table_seed, D, blk)
+
+
+def mx_scales_rowmajor(scale_dev, rows: int, K: int) -> np.ndarray:
+    """An MX scale tensor in the library's layout [K/128, rows4, 4] -> uint8 [rows, K/32] (the oracle's)."""
+    s = scale_dev.cpu().numpy().reshape(K // 128, -1, 4)
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(-1, K // 32)[:rows])

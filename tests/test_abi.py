@@ -156,6 +156,32 @@ def test_gather_packed_validation(kw, msg):
     assert "engram_gather_dequant_packed" in _err()
 
 
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("kw,msg", [
+    (dict(D=48), "D=48"),
+    (dict(blk=8), "blk=8"),
+    (dict(C=3, stride=3), "C*D=192"),  # the MX scale layout needs whole 128-column groups
+    (dict(R=0), "R < 1"),
+    (dict(q=None), "null"),
+    (dict(q_scale=None), "null"),
+    (dict(q=ctypes.c_void_p(0x100008)), "misaligned"),
+])
+def test_gather_mx_validation(kw, msg, packed):
+    a = dict(ids=FAKE, T=10, stride=24, C=24, weight=FAKE, scale=FAKE, R=100, row_start=0, D=64, blk=32, q=FAKE,
+             q_scale=FAKE)
+    a.update(kw)
+    L = g.lib()
+    if packed:
+        rc = L.engram_gather_mx_packed(a["ids"], a["T"], a["stride"], a["C"], a["weight"], a["R"], a["row_start"],
+                                       a["D"], a["blk"], a["q"], a["q_scale"], None)
+    else:
+        rc = L.engram_gather_mx(a["ids"], a["T"], a["stride"], a["C"], a["weight"], a["scale"], a["R"],
+                                a["row_start"], a["D"], a["blk"], a["q"], a["q_scale"], None)
+    assert rc == 1
+    assert msg in _err()
+    assert ("engram_gather_mx_packed" if packed else "engram_gather_mx") in _err()
+
+
 @pytest.mark.parametrize("kw,msg", [(dict(D=40), "D=40"), (dict(blk=24), "blk=24"), (dict(R=-1), "R < 0"),
                                     (dict(packed=None), "null"), (dict(packed=ctypes.c_void_p(0x100040)), "misaligned")])
 def test_pack_table_validation(kw, msg):

@@ -8,15 +8,12 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import assert_close, bf16_tensor, bits, compact_rows, sample_tokens
+from tests.gpu_util import assert_close, bf16_tensor, bits, compact_rows, mx_scales_rowmajor, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
 
-def _scales_rowmajor(scale_dev, rows, K):
-    """[K/128, rows4, 4] (the library's layout) -> [rows, K/32] (the oracle's)."""
-    s = scale_dev.cpu().numpy().reshape(K // 128, -1, 4)
-    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(-1, K // 32)[:rows])
+_scales_rowmajor = mx_scales_rowmajor
 
 
 def _scales_tiled(scale_rowmajor, K, device):
@@ -184,6 +181,23 @@ def test_fp8_pipeline(gpu_device, cfg_index, n_sample):
                                       err_msg=f"fused fp8 value columns, layer {e}")
         assert_close(dots_f[e].view(T, -1)[sidx].cpu().numpy(), dots_u[e], rtol=1e-3, atol=1e-4,
                      what=f"fused fp8 dot, layer {e}")
+    # the same fused step with the gathers writing MX rows directly (engram_gather_mx): the same A operand
+    # (every token), hence the same value columns and dots, bit for bit
+    keep = {k: [wl.fwd._bufs[(k, e)].clone() for e in range(cfg.n_layers)] for k in ("a_mx", "a_mx_scale", "value")}
+    dots_f = [d.clone() for d in dots_f]
+    for k in ("a_mx", "a_mx_scale"):
+        for e in range(cfg.n_layers):
+            wl.fwd._bufs[(k, e)].fill_(0x5A)  # every byte the gather must write is overwritten
+    dots_g = wl.fwd.step(wl.input_ids, 0, wl.x[0], wl.token_mask, packed=True, fp8=True, fused=True,
+                         gather_mx=True)
+    torch.cuda.synchronize()
+    for e in range(cfg.n_layers):
+        assert torch.equal(wl.fwd._bufs[("a_mx", e)], keep["a_mx"][e]), f"MX rows from the gather, layer {e}"
+        np.testing.assert_array_equal(_scales_rowmajor(wl.fwd._bufs[("a_mx_scale", e)], T, K),
+                                      _scales_rowmajor(keep["a_mx_scale"][e], T, K),
+                                      err_msg=f"MX scales from the gather, layer {e}")
+        assert torch.equal(wl.fwd._bufs[("value", e)], keep["value"][e]), f"value columns, layer {e}"
+        assert torch.equal(dots_g[e], dots_f[e]), f"dot, layer {e}"
 
 
 # (T, K, hc, dim): ragged token counts, one token, grids of more tiles than CUs (several key tiles per workgroup,
