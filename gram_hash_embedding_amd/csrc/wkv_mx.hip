@@ -38,7 +38,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int kSlabCols = 128;              // fp8 columns (= bytes) per slab row
-constexpr int kMxBlock = 32;                // columns per E8M0 scale
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kOpBytes = 256 * kSlabCols;   // one operand's slab: 32 KB
@@ -118,9 +117,14 @@ __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// kGate: the fused projection + gate pre-activation over the key columns only (every tile is reduced against
-// the stream in its epilogue instead of stored; the value columns are a plain launch of their own).
-template <bool kGate>
+// Kernel modes.  kStream: the slab loads stream across tile boundaries and each tile is stored through the
+// 16 KB exchange in eight rounds (any K).  kHold: a tile's last two slabs hold back the next tile's first two,
+// so both stages are free at its end and the whole tile is stored in one round through them (K >= 384).
+// kGate: kHold's loop over the key columns only, every tile reduced against the stream in its epilogue
+// instead of stored (the fused projection + gate pre-activation; the value columns are a launch of their own).
+constexpr int kStream = 0, kHold = 1, kGate = 2;
+
+template <int kMode>
 __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes + kExBytes];
     const int tiles = p.tiles_m * p.tiles_n;
@@ -281,6 +285,45 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 sync_epi();
             }
         }
+    };
+
+    // ---- one-round epilogue of a held-back tile (kHold): both stages are free.  Every wave writes its 128
+    // tokens x 64 outputs as bf16 into stage wm (row t: token 128 wm + t, 512 bytes = the tile's 256 outputs,
+    // 16-byte piece c at slot c ^ (t % 32)); after a barrier the storer waves read 64 rows each and write them
+    // with full-line non-temporal 16-byte stores (two rows per instruction), and a second barrier frees the
+    // stages for the held-back slabs.  The stores drain while the next tile computes.
+    auto store_epilogue = [&](const f32x16 (&acc)[4][2], int64_t m0, int n0) {
+        const int l = lane_id();
+        uint8_t* sb = lds + wm * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 32 * i + (l & 31);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int c = wn * 8 + 4 * j + gq;  // the 16-byte piece of the row (8 outputs)
+                    const u32x2 v = {pack_bf16(acc[i][j][4 * gq + 0], acc[i][j][4 * gq + 1]),
+                                     pack_bf16(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3])};
+                    *reinterpret_cast<u32x2*>(sb + t * 512 + ((c ^ (t & 31)) << 4) + (l >> 5) * 8) = v;
+                }
+        }
+        sync_epi();
+        if (!loader) {
+            const int s = wave - 4;
+            const int c = l & 31;
+            const int ncol = n0 + 8 * c;
+#pragma unroll 4
+            for (int ins = 0; ins < 32; ++ins) {
+                const int r = 64 * s + 2 * ins + (l >> 5);  // row of the tile: token m0 + r
+                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (r >> 7) * kStageBytes + (r & 127) * 512 +
+                                                               ((c ^ (r & 31)) << 4));
+                const int64_t m = m0 + r;
+                if (m < p.M && ncol < p.N)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + ncol));
+            }
+        }
+        sync_epi();
     };
 
     // ---- fused gate epilogue of a key tile (kGate): the product is not stored.  The tile's 256 columns lie in
@@ -506,7 +549,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         for (int i = 0; i < 4; ++i) fa[i] = read_a(0, 0, i);
         fw[0] = read_w(0, 0, 0);
         fw[1] = read_w(0, 0, 1);
-        if constexpr (!kGate) {
+        if constexpr (kMode == kStream) {
             for (int t = 0; t < my_tiles; ++t) {
                 const int64_t m0 = cur.m0;
                 const int n0 = cur.n0;
@@ -557,7 +600,7 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
             // slabs of a key tile's end); kReload false: the tile's last slab, no fragments are reloaded and no
             // load is waited for (its slab has landed).  kFirst: the tile's first slab (zero C operand: the
             // accumulators are dead between tiles).  hook(u): every wave's share of k-step 1's units in a slab
-            // that issues nothing (the tile's last two: the gate epilogue's loads)
+            // that issues nothing (the tile's last two: the gate epilogue's loads, if any)
             int kt = 0;  // the slab's index in its tile
             auto slab = [&](auto first_tag, auto issue_tag, auto reload_tag, auto&& hook) {
                 constexpr bool kIssue = decltype(issue_tag)::value;
@@ -600,18 +643,24 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
                 kt = 0;
                 using T_ = std::true_type;
                 using F_ = std::false_type;
-                // a key tile (KT >= 3): its last two slabs hold back the next tile's first two and fetch what the
-                // gate epilogue reads, each into its own stage once its barrier has passed
+                // KT >= 3: the tile's last two slabs hold back the next tile's first two (and, for a key tile,
+                // fetch what the gate epilogue reads, each into its own stage once its barrier has passed)
                 slab(T_{}, T_{}, T_{}, no_extra);
                 while (kt < KT - 2) slab(F_{}, T_{}, T_{}, no_extra);
-                const int st = stage ^ 1;  // the last slab's stage
-                const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
-                slab(F_{}, F_{}, T_{}, [&](int u) {
-                    if (u < 2) dma_qk(n0, u);
-                    dma_piece(xr, 2 + (u >> 2), u & 3, st);
-                });
-                slab(F_{}, F_{}, F_{}, [&](int u) { dma_piece(xr, u >> 2, u & 3, st); });
-                gate_epilogue(acc, m0, n0, st);
+                if constexpr (kMode == kGate) {
+                    const int st = stage ^ 1;  // the last slab's stage
+                    const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
+                    slab(F_{}, F_{}, T_{}, [&](int u) {
+                        if (u < 2) dma_qk(n0, u);
+                        dma_piece(xr, 2 + (u >> 2), u & 3, st);
+                    });
+                    slab(F_{}, F_{}, F_{}, [&](int u) { dma_piece(xr, u >> 2, u & 3, st); });
+                    gate_epilogue(acc, m0, n0, st);
+                } else {
+                    slab(F_{}, F_{}, T_{}, no_extra);
+                    slab(F_{}, F_{}, F_{}, no_extra);
+                    store_epilogue(acc, m0, n0);
+                }
                 // the held-back slabs 0 and 1 of the next tile (past the workgroup's last: empty issues) into the
                 // two stages; the first must land before its fragments are read, the second may still fly
                 cur = nx1;
@@ -642,8 +691,9 @@ __device__ __forceinline__ void wkv_mx_body(const MxArgs& p) {
         run(std::false_type{});
 }
 
-__global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) { wkv_mx_body<false>(p); }
-__global__ __launch_bounds__(kThreads, 1) void wkv_mx_gate_kernel(MxArgs p) { wkv_mx_body<true>(p); }
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_kernel(MxArgs p) { wkv_mx_body<kStream>(p); }
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_hold_kernel(MxArgs p) { wkv_mx_body<kHold>(p); }
+__global__ __launch_bounds__(kThreads, 1) void wkv_mx_gate_kernel(MxArgs p) { wkv_mx_body<kGate>(p); }
 
 // ---- OCP MX quantisation of bf16 rows ----
 // A thread owns 8 consecutive columns (one 16-byte load); the 4 threads of a 32-column block reduce their
@@ -730,7 +780,10 @@ extern "C" int engram_wkv_mx(const uint8_t* a, const uint8_t* a_scale, const uin
     p.tiles_m = static_cast<int>(tiles_m);
     const int64_t tiles = tiles_m * p.tiles_n;
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
-    hipLaunchKernelGGL(wkv_mx_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    if (K >= 3 * kSlabCols)  // three slabs or more: the held-back loop and its one-round epilogue
+        hipLaunchKernelGGL(wkv_mx_hold_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
+    else
+        hipLaunchKernelGGL(wkv_mx_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), p);
     return check_launch(what);
 }
 
@@ -805,7 +858,7 @@ extern "C" int engram_wkv_mx_gate(const uint8_t* a, const uint8_t* a_scale, cons
     v.tiles_m = p.tiles_m;
     v.tiles_n = dim / BN;
     tiles = tiles_m * v.tiles_n;
-    hipLaunchKernelGGL(wkv_mx_kernel, dim3(static_cast<unsigned>(tiles < kCUs ? tiles : kCUs)), dim3(kThreads),
+    hipLaunchKernelGGL(wkv_mx_hold_kernel, dim3(static_cast<unsigned>(tiles < kCUs ? tiles : kCUs)), dim3(kThreads),
                        0, as_stream(stream), v);
     rc = check_launch(what);
     if (rc != ENGRAM_OK) return rc;
