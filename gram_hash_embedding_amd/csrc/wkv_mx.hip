@@ -7,6 +7,9 @@
 //                       nearest even and saturated at 448
 //   engram_wkv_mx    -- kv = A * W^T with v_mfma_scale_f32_32x32x64_f8f6f4 (the block scales applied by the
 //                       matrix core), fp32 accumulation, one bf16 rounding
+//   engram_wkv_mx_gate -- engram_wkv_mx fused with the gate pre-activation (Engram.forward's rstd and dot):
+//                       the key columns reduced against the stream in the kernel's epilogue, the value columns
+//                       stored, the bf16 path's finalize (wkv.hip) adding the partial sums
 //
 // Scale layout (both operands): uint8 [K/128][rows4][4], rows4 = rows rounded up to a multiple of 4; byte
 // [s][r][b] scales row r's columns 128 s + 32 b .. +32.  A 128-column slab of a 256-row tile then has its
@@ -16,7 +19,9 @@
 // waves (two per SIMD, loader waves 0-3 issue every slab load, storer waves 4-7 every store), slabs of 128
 // fp8 columns (128-byte rows, the same XOR swizzle as the bf16 slabs of 64 columns) in two stages, XCD-grouped
 // tile order.  A stage holds 66 KB (A and W slabs and their scales), so the epilogue exchange is 16 KB and
-// runs in eight rounds of 32 tokens x 128 outputs per wave pair.  Each wave: 128 tokens x 64 outputs = 4 x 2
+// runs in eight rounds of 32 tokens x 128 outputs per wave pair -- or, at K >= 384, a tile's last two slabs
+// hold back the next tile's first two and the tile leaves in one round through both freed stages (the fused
+// kernel's stream rows use them the same way).  Each wave: 128 tokens x 64 outputs = 4 x 2
 // MFMA blocks of 32x32 (K 64 per MFMA: two per slab).  Lane l of a 32x32x64 fragment holds row l % 32: in
 // its first 16 bytes columns 16h .. 16h + 15 and in its last 16 bytes columns 32 + 16h .. 32 + 16h + 15 of
 // the step (h = l / 32); the scale operand of lane half h scales the step's 32-column block h of the row (the
