@@ -68,8 +68,11 @@ def test_mx_quant_matches_the_oracle(gpu_device, rows, K):
     np.testing.assert_array_equal(_scales_rowmajor(sc, rows, K), want_s)
 
 
+# K < 384: the streaming kernel; K >= 384: the held-back one (one token, ragged T and N, several tiles per
+# workgroup in both)
 @pytest.mark.parametrize("T,K,N", [(1, 128, 8), (37, 256, 264), (255, 128, 256), (257, 1536, 1280),
-                                   (600, 384, 520), (1000, 1536, 25600), (4173, 1536, 2048), (300, 6144, 512)])
+                                   (600, 384, 520), (1000, 1536, 25600), (4173, 1536, 2048), (300, 6144, 512),
+                                   (1, 384, 8), (3, 512, 264), (700, 256, 25600)])
 def test_wkv_mx_matches_the_oracle(gpu_device, T, K, N):
     import torch
 
