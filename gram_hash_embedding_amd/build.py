@@ -37,6 +37,7 @@ HIPCC_FLAGS = [
 # so its epilogues use them in place instead of copying each one out of an AGPR first
 FILE_FLAGS = {
     "wkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "wkv16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1040,6 +1040,17 @@ int tile_ni(int64_t T, int tiles_n, int K, int layers) {
 template <bool kGate>
 int launch_main(WkvArgs& p, int64_t T, int layers, hipStream_t stream, const char* what) {
     const int ni = tile_ni(T, p.tiles_n, p.K, layers);
+    // 256-token tiles, three slabs or more and launches large enough: the 16 x 16 x 32 form (wkv16.hip), one
+    // layer at a time
+    if (ni == 4 && wkv16_takes(T, p.K, p.N, p.hc, p.dim, kGate)) {
+        for (int e = 0; e < layers; ++e) {
+            const LayerPtrs& L = p.lay[e];
+            const int rc = launch_wkv16(L.a, L.w, L.kv, p.ld_out, T, p.K, p.N, L.x, L.q, L.k, L.part, p.hc, p.dim,
+                                        kGate, stream, what);
+            if (rc != ENGRAM_OK) return rc;
+        }
+        return ENGRAM_OK;
+    }
     const int64_t bm = 64 * ni;
     const int64_t tiles_ml = (T + bm - 1) / bm;
     if (tiles_ml * layers * p.tiles_n > 0x7FFFFFFF) return fail(ENGRAM_EINVAL, "%s: too many tiles", what);
