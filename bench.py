@@ -93,19 +93,22 @@ def algorithmic(cfg, has_mask: bool):
     }
 
 
-def source_sha(name: str) -> str:
-    path = os.path.join(ROOT, "gram_hash_embedding_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_sha(names) -> str:
+    """First 16 hex digits of the SHA-256 of the named csrc files' contents, concatenated in order."""
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "gram_hash_embedding_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_file: str, kernel: str, workload: str):
+def load_traffic(kernel_files, kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary, if it was taken
-    on the current source of `kernel_file`; else None."""
+    on the current source of `kernel_files`; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha") != source_sha(kernel_file):
+    if rec.get("source_sha") != source_sha(kernel_files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -596,7 +599,7 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": wg["frac_mfma"],
-        "traffic": load_traffic("wkv.hip", "wkv_gate", cfg.name),
+        "traffic": load_traffic(("wkv.hip", "wkv16.hip"), "wkv_gate", cfg.name),
         "algorithmic_bytes_per_launch": T_launch * algo["wkv_gate_bytes"] + W_bytes,
     }
     if peaks:
