@@ -9,15 +9,15 @@
 //
 // Design (gfx950): the fp8 projection's held-back persistent loop (wkv_mx.hip) on bf16 slabs of 64 columns --
 // the same 128-byte LDS rows with 16-byte pieces XOR-swizzled by (row / 2) mod 8, two stages of 64 KB (A and
-// W slabs), eight waves (loader waves 0-3 issue every slab load, waves 4-7 the stores), 256 x 256 tiles in
-// XCD-grouped order.  A tile's last two slabs hold back the next tile's first two, so both stages are free at
+// W slabs), eight waves (loader waves 0-3 issue every slab load), 256 x 256 tiles in XCD-grouped order.  A tile's last two slabs hold back the next tile's first two, so both stages are free at
 // its end: the whole tile leaves in one store round through them (kHold), or they take the stream rows of the
 // fused gate epilogue (kGate).  Each wave: 128 tokens x 64 outputs = 8 x 4 MFMA blocks of 16 x 16, issued as
 // W fragment x token fragment, so that lane l holds, per block, token l % 16 and the four consecutive outputs
 // 4 (l / 16) .. +3 (the lane layout measured on gfx950: operand lane l holds row l % 16 and K elements
 // 8 (l / 16) .. +7; result lane l holds rows 4 (l / 16) .. +3 of column l % 16).  A slab is two k-steps of 32
 // columns, 32 MFMAs each; the 12 fragments of a k-step (16 bytes a lane each) are reloaded in place right
-// after their last use.
+// after their last use.  The slab's one barrier sits seven MFMAs into its second k-step, where the next slab's
+// first fragment read follows it.
 #include <type_traits>
 #include <utility>
 
@@ -46,6 +46,7 @@ constexpr int kNonTemporal = 2;             // cache-policy operand of a load: s
 constexpr int kWaitLgkmcnt0 = 0xC07F;
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kSlabLoads = 16;              // direct-to-LDS loads per loader wave and slab
+constexpr int kBar = 7;                     // the slab barrier precedes unit kBar of a slab's second k-step
 
 constexpr int kHold = 1, kGate = 2;
 
@@ -193,10 +194,11 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
 
     // ---- one-round store epilogue (kHold): both stages are free.  Every wave writes its 128 tokens x 64
     // outputs as bf16 into stage wm (row t: token 128 wm + t, 512 bytes = the tile's 256 outputs, 16-byte
-    // piece c at slot c ^ (t % 32)); after a barrier the storer waves read 64 rows each and write them with
-    // full-line non-temporal 16-byte stores (two rows per instruction), and a second barrier frees the stages
-    // for the held-back slabs.  The stores drain while the next tile computes.
-    auto store_epilogue = [&](const f32x4 (&acc)[8][4], int64_t m0, int n0) {
+    // piece c at slot c ^ (t % 32)); after a barrier every wave reads 32 rows into registers (the accumulators
+    // are dead by then), a second barrier frees the stages, `refill()` issues the held-back slabs, and every
+    // wave writes its rows with full-line non-temporal 16-byte stores (two rows per instruction), which drain
+    // while the held-back slabs land and the next tile computes.
+    auto store_epilogue = [&](const f32x4 (&acc)[8][4], int64_t m0, int n0, auto&& refill) {
         const int l = lane_id();
         const int g = l >> 4;
         uint8_t* sb = lds + wm * kStageBytes;
@@ -211,21 +213,22 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             }
         }
         sync_epi();
-        if (!loader) {
-            const int s = wave - 4;
-            const int c = l & 31;
-            const int ncol = n0 + 8 * c;
-#pragma unroll 4
-            for (int ins = 0; ins < 32; ++ins) {
-                const int r = 64 * s + 2 * ins + (l >> 5);  // row of the tile: token m0 + r
-                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (r >> 7) * kStageBytes + (r & 127) * 512 +
-                                                               ((c ^ (r & 31)) << 4));
-                const int64_t m = m0 + r;
-                if (m < p.M && ncol < p.N)
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + ncol));
-            }
+        const int c = l & 31;
+        u32x4 v[16];
+#pragma unroll
+        for (int ins = 0; ins < 16; ++ins) {
+            const int r = 32 * wave + 2 * ins + (l >> 5);  // row of the tile: token m0 + r
+            v[ins] = *reinterpret_cast<const u32x4*>(lds + (r >> 7) * kStageBytes + (r & 127) * 512 + ((c ^ (r & 31)) << 4));
         }
         sync_epi();
+        const int ncol = n0 + 8 * c;
+#pragma unroll
+        for (int ins = 0; ins < 16; ++ins) {
+            const int64_t m = m0 + 32 * wave + 2 * ins + (l >> 5);
+            if (m < p.M && ncol < p.N)
+                __builtin_nontemporal_store(v[ins], reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + ncol));
+        }
+        refill();
     };
 
     // ---- fused gate epilogue of a key tile (kGate): the product is not stored.  The tile's 256 columns lie in
@@ -453,20 +456,32 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             constexpr bool kIssue = decltype(issue_tag)::value;
             constexpr bool kReload = decltype(reload_tag)::value;
             kstep(first_tag, acc, fa, fw, stage, 1, no_extra, std::true_type{});
-            if (kLoader && kReload) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-            sync();
             const int nst = stage ^ 1;
+            // The slab barrier sits after unit kBar - 1 of k-step 1, just before its first LDS read (W fragment
+            // 0's reload at unit 7): the k-step's first MFMAs run while this wave's last reads of the stage
+            // complete and the other waves arrive.  Everything that writes the freed stage comes after it.
+            auto bar = [&]() {
+                if (kLoader && kReload) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+                sync();
+            };
             if constexpr (!kReload) {
-                kstep(std::false_type{}, acc, fa, fw, nst, 0, hook, std::false_type{});
+                kstep(std::false_type{}, acc, fa, fw, nst, 0, [&](int u) {
+                    if (u == kBar - 1) bar();
+                    if (u >= kBar) hook(u - kBar);
+                }, std::false_type{});
             } else if (kLoader && kIssue) {
                 const SlabRsrc r = slab_rsrc(cur, kt + 2);  // (an issuing slab is followed by two more)
                 const int st = stage;
                 kstep(std::false_type{}, acc, fa, fw, nst, 0, [&](int u) {
-                    if ((u & 3) == 0) issue_part(r, st, u >> 2);
+                    if (u == kBar - 1) bar();
+                    if (u >= kBar && (u - kBar) % 3 == 0 && (u - kBar) / 3 < 8) issue_part(r, st, (u - kBar) / 3);
                 }, std::true_type{});
             } else {
                 kstep(std::false_type{}, acc, fa, fw, nst, 0, [&](int u) {
-                    if constexpr (!kIssue) hook(u);
+                    if (u == kBar - 1) bar();
+                    if constexpr (!kIssue) {
+                        if (u >= kBar) hook(u - kBar);
+                    }
                 }, std::true_type{});
             }
             stage ^= 1;
@@ -482,6 +497,17 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             // what the gate epilogue reads, each into its own stage once its barrier has passed)
             slab(T_{}, T_{}, T_{}, no_extra);
             while (kt < KT - 2) slab(F_{}, T_{}, T_{}, no_extra);
+            // the held-back slabs 0 and 1 of the next tile (past the workgroup's last: empty issues), issued into
+            // the two stages once the epilogue has freed them; the first must land before its fragments are
+            // read, the second may still fly (a loader's vmcnt also counts the stores it issued before them)
+            cur = nx1;
+            nx1 = tile_at(t + 2);
+            auto refill = [&]() {
+                if (kLoader) {
+                    issue_slab(cur, 0, stage);
+                    issue_slab(cur, 1, stage ^ 1);
+                }
+            };
             if constexpr (kMode == kGate) {
                 const int st = stage ^ 1;  // the last slab's stage
                 const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
@@ -497,20 +523,13 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
                     if ((u & 1) == 0 && n < 8) dma_piece(xr, n >> 2, n & 3, st);
                 });
                 gate_epilogue(acc, m0, n0, st);
+                refill();
             } else {
                 slab(F_{}, F_{}, T_{}, no_extra);
                 slab(F_{}, F_{}, F_{}, no_extra);
-                store_epilogue(acc, m0, n0);
+                store_epilogue(acc, m0, n0, refill);
             }
-            // the held-back slabs 0 and 1 of the next tile (past the workgroup's last: empty issues) into the
-            // two stages; the first must land before its fragments are read, the second may still fly
-            cur = nx1;
-            nx1 = tile_at(t + 2);
-            if (kLoader) {
-                issue_slab(cur, 0, stage);
-                issue_slab(cur, 1, stage ^ 1);
-                __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));
-            }
+            if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));
             sync();
             const uint32_t fo = frag_off();
 #pragma unroll
