@@ -368,7 +368,8 @@ def test_probe_library_exports_and_validates():
     L.engram_probe_read.argtypes = [P, ctypes.c_int64, P, P]
     L.engram_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
     assert L.engram_probe_read_grid() > 0
-    assert L.engram_probe_mfma(2, FAKE, FAKE, 256, 8, 10, None) != 0   # unknown kind
+    assert L.engram_probe_mfma(5, FAKE, FAKE, 256, 8, 10, None) != 0   # unknown kind
+    assert L.engram_probe_mfma(-1, FAKE, FAKE, 256, 8, 10, None) != 0
     assert L.engram_probe_mfma(0, FAKE, FAKE, 256, 9, 10, None) != 0   # more than 8 waves
     assert L.engram_probe_mfma(0, None, FAKE, 256, 8, 10, None) != 0
     assert L.engram_probe_read(FAKE, 24, FAKE, None) != 0              # not a multiple of 16
