@@ -3,8 +3,8 @@
 chosen to take it -- ragged token counts (a last tile of 1 to 255 rows), a ragged last column tile, the
 smallest K (three slabs) and long K, one and many copies, dims up to 8,192 -- against the oracle (the bf16
 bar), the fused form's value columns bit for bit against the plain launch's, its dot against the unfused
-path (fp32 summation order only) and against the oracle fed the device's keys (the tight bar), and
-run-to-run identity."""
+path (fp32 summation order only) and against the oracle fed the device's keys (the tight bar),
+run-to-run identity, and a row-strided value output."""
 import numpy as np
 import pytest
 
@@ -80,3 +80,27 @@ def test_wkv16_gate_matches_the_plain_launch_and_the_oracle(gpu_device, T, K, hc
     assert_close(oracle.bf16_bits_to_float(kv_bits), kv_want, what="kv vs oracle")
     assert_close(dot.cpu().numpy()[rows], oracle.gate_dot(x_bits, _kv_bf16(kv_want), bits(q), bits(k), 1e-20),
                  what="dot vs oracle")
+
+
+def test_wkv16_gate_strided_value_leaves_the_padding(gpu_device):
+    """The fused launch's value columns into a row-strided view (ld = dim + 384): equal to the plain launch's
+    bit for bit, and the columns past dim in each row untouched."""
+    import torch
+
+    import gram_hash_embedding_amd as g
+
+    T, K, hc, dim, ld = 4099, 768, 2, 8192, 8192 + 384
+    rng = np.random.default_rng(41)
+    a = _rand_bf16(rng, (T, K), 0.1).to(gpu_device)
+    w = _rand_bf16(rng, ((hc + 1) * dim, K), 0.02).to(gpu_device)
+    x = _rand_bf16(rng, (T, hc, dim)).to(gpu_device)
+    q = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(gpu_device)
+    k = _rand_bf16(rng, (hc, dim), 0.1, 1.0).to(gpu_device)
+    buf = torch.full((T, ld), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    _, dot = g.engram_wkv_gate(a, w, x, q, k, 1e-20, value=buf[:, :dim])
+    kv = g.engram_wkv(a, w)
+    dot2 = g.engram_gate_dot(x, kv, q, k, 1e-20)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(buf[:, :dim]), bits(kv)[:, hc * dim:], err_msg="value columns")
+    assert bool((buf[:, dim:] == 7.0).all()), "padding columns written"
+    assert_close(dot.cpu().numpy(), dot2.cpu().numpy(), rtol=1e-3, atol=1e-4, what="dot vs unfused")
