@@ -9,9 +9,10 @@
 //
 // Design (gfx950): the fp8 projection's held-back persistent loop (wkv_mx.hip) on bf16 slabs of 64 columns --
 // the same 128-byte LDS rows with 16-byte pieces XOR-swizzled by (row / 2) mod 8, two stages of 64 KB (A and
-// W slabs), eight waves (loader waves 0-3 issue every slab load), 256 x 256 tiles in XCD-grouped order.  A tile's last two slabs hold back the next tile's first two, so both stages are free at
-// its end: the whole tile leaves in one store round through them (kHold), or they take the stream rows of the
-// fused gate epilogue (kGate).  Each wave: 128 tokens x 64 outputs = 8 x 4 MFMA blocks of 16 x 16, issued as
+// W slabs), eight waves (loader waves 0-3 issue every slab load), 256 x 256 tiles in XCD-grouped order.  A
+// tile's last two slabs hold back the next tile's first two, so both stages are free at its end: the whole tile
+// leaves in one store round through them (kHold), or they take the stream rows of the fused gate epilogue
+// (kGate).  Each wave: 128 tokens x 64 outputs = 8 x 4 MFMA blocks of 16 x 16, issued as
 // W fragment x token fragment, so that lane l holds, per block, token l % 16 and the four consecutive outputs
 // 4 (l / 16) .. +3 (the lane layout measured on gfx950: operand lane l holds row l % 16 and K elements
 // 8 (l / 16) .. +7; result lane l holds rows 4 (l / 16) .. +3 of column l % 16).  A slab is two k-steps of 32
