@@ -17,8 +17,8 @@
 // 4 (l / 16) .. +3 (the lane layout measured on gfx950: operand lane l holds row l % 16 and K elements
 // 8 (l / 16) .. +7; result lane l holds rows 4 (l / 16) .. +3 of column l % 16).  A slab is two k-steps of 32
 // columns, 32 MFMAs each; the 12 fragments of a k-step (16 bytes a lane each) are reloaded in place right
-// after their last use.  The slab's one barrier sits seven MFMAs into its second k-step, where the next slab's
-// first fragment read follows it.
+// after their last use.  The slab's one barrier sits fourteen MFMAs into its second k-step, where the next
+// slab's first fragment read follows it.
 #include <type_traits>
 #include <utility>
 
@@ -47,7 +47,7 @@ constexpr int kNonTemporal = 2;             // cache-policy operand of a load: s
 constexpr int kWaitLgkmcnt0 = 0xC07F;
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kSlabLoads = 16;              // direct-to-LDS loads per loader wave and slab
-constexpr int kBar = 7;                     // the slab barrier precedes unit kBar of a slab's second k-step
+constexpr int kBar = 14;                     // the slab barrier precedes unit kBar of a slab's second k-step
 
 constexpr int kHold = 1, kGate = 2;
 
@@ -401,11 +401,13 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
         return TileAt{static_cast<int64_t>(tm) * BM, tn * BN, t < my_tiles};
     };
 
-    // One k-step: acc[i][j] += (W fragment j) x (token fragment i), W-fragment-major; each fragment is reloaded,
-    // for k-step `ns` of stage `nst`, right after its last use here (token fragments in the last W pass, each
-    // seven or more MFMAs before its next use; W fragments at the end of their pass).  Each MFMA with its
-    // reloads and `extra(u)` (u = 0..31) is one scheduling unit.  kReload false (the last slab of a tile): no
-    // reloads, the fragments are dead after the k-step.
+    // One k-step: acc[i][j] += (W fragment j) x (token fragment i) in two halves, W fragments 0-1 then 2-3, each
+    // walking the 8 token fragments against its pair; each fragment is reloaded, for k-step `ns` of stage `nst`,
+    // right after its last use here (token fragment i after its block (i, 3); W fragments 0-1 at the end of the
+    // first half, 2-3 at the end of the second), so every reload is issued fifteen or more MFMAs before its next
+    // use, and the k-step's first LDS read comes at unit 14.  Each MFMA with its reloads and `extra(u)` (u = 0..31)
+    // is one scheduling unit.  kReload false (the last slab of a tile): no reloads, the fragments are dead after
+    // the k-step.
     auto kstep = [&](auto zero_tag, f32x4 (&acc)[8][4], bf16x8 (&fa)[8], bf16x8 (&fw)[4], int nst, int ns,
                      auto&& extra, auto reload_tag) {
         constexpr bool kZero = decltype(zero_tag)::value;
@@ -413,15 +415,19 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
         const f32x4 z = {};
         const uint32_t fo = kReload ? frag_off() : 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fa[i], kZero ? z : acc[i][j], 0, 0, 0);
-                if (kReload && j == 3) fa[i] = read_a(fo, nst, ns, i);
-                if (kReload && i == 7) fw[j] = read_w(fo, nst, ns, j);
-                extra(8 * j + i);
-                asm volatile("" ::: "memory");  // keeps the unit's LDS reads and loads in the unit
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const int j = 2 * jj + jb;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fa[i], kZero ? z : acc[i][j], 0, 0, 0);
+                    if (kReload && j == 3) fa[i] = read_a(fo, nst, ns, i);
+                    if (kReload && i == 7) fw[j] = read_w(fo, nst, ns, j);
+                    extra(16 * jj + 2 * i + jb);
+                    asm volatile("" ::: "memory");  // keeps the unit's LDS reads and loads in the unit
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
@@ -459,8 +465,9 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             kstep(first_tag, acc, fa, fw, stage, 1, no_extra, std::true_type{});
             const int nst = stage ^ 1;
             // The slab barrier sits after unit kBar - 1 of k-step 1, just before its first LDS read (W fragment
-            // 0's reload at unit 7): the k-step's first MFMAs run while this wave's last reads of the stage
-            // complete and the other waves arrive.  Everything that writes the freed stage comes after it.
+            // 0's reload at unit 14): the k-step's first MFMAs run while this wave's last reads of the stage
+            // complete and the other waves arrive.  Everything that writes the freed stage comes after it: the
+            // loaders' slab loads (one part every second unit) or the gate's loads (hook(n), one per unit).
             auto bar = [&]() {
                 if (kLoader && kReload) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
                 sync();
@@ -475,7 +482,7 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
                 const int st = stage;
                 kstep(std::false_type{}, acc, fa, fw, nst, 0, [&](int u) {
                     if (u == kBar - 1) bar();
-                    if (u >= kBar && (u - kBar) % 3 == 0 && (u - kBar) / 3 < 8) issue_part(r, st, (u - kBar) / 3);
+                    if (u >= kBar && (u - kBar) % 2 == 0 && (u - kBar) / 2 < 8) issue_part(r, st, (u - kBar) / 2);
                 }, std::true_type{});
             } else {
                 kstep(std::false_type{}, acc, fa, fw, nst, 0, [&](int u) {
@@ -513,15 +520,13 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
                 const int st = stage ^ 1;  // the last slab's stage
                 const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
                 // every second unit takes one load: q, k, then round 2's and round 3's four
-                slab(F_{}, F_{}, T_{}, [&](int u) {
-                    const int n = u >> 1;
-                    if ((u & 1) == 0 && n < 2) dma_qk(n0, n);
-                    if ((u & 1) == 0 && n >= 2 && n < 10) dma_piece(xr, 2 + ((n - 2) >> 2), (n - 2) & 3, st);
+                slab(F_{}, F_{}, T_{}, [&](int n) {
+                    if (n < 2) dma_qk(n0, n);
+                    else if (n < 10) dma_piece(xr, 2 + ((n - 2) >> 2), (n - 2) & 3, st);
                 });
                 // rounds 0 and 1
-                slab(F_{}, F_{}, F_{}, [&](int u) {
-                    const int n = u >> 1;
-                    if ((u & 1) == 0 && n < 8) dma_piece(xr, n >> 2, n & 3, st);
+                slab(F_{}, F_{}, F_{}, [&](int n) {
+                    if (n < 8) dma_piece(xr, n >> 2, n & 3, st);
                 });
                 gate_epilogue(acc, m0, n0, st);
                 refill();
