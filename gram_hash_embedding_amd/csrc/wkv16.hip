@@ -519,7 +519,7 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             if constexpr (kMode == kGate) {
                 const int st = stage ^ 1;  // the last slab's stage
                 const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
-                // every second unit takes one load: q, k, then round 2's and round 3's four
+                // one load per unit after the slab barrier: q, k, then round 2's and round 3's four
                 slab(F_{}, F_{}, T_{}, [&](int n) {
                     if (n < 2) dma_qk(n0, n);
                     else if (n < 10) dma_piece(xr, 2 + ((n - 2) >> 2), (n - 2) & 3, st);
