@@ -249,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void hash_kernel(HashArgs a, GatherSide g
                     u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
                     if (ok[u]) dequant16(v[u], sc[u], o0, o1);
                     u32x4* d = reinterpret_cast<u32x4*>(dst[u]);
-                    __builtin_nontemporal_store(o0, d);
-                    __builtin_nontemporal_store(o1, d + 1);
+                    d[0] = o0;
+                    d[1] = o1;
                 }
             }
         }

@@ -599,8 +599,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void wkv_kernel(WkvArgs p) {
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
                         const float v = res[i][q] + partner[(i * 3 + q) * 32 + ls];
-                        // streamed past L2, which the operand panels need; the finalize reads them once
-                        if (t < p.M) __builtin_nontemporal_store(v, out + q * p.M + t);
+                        // ordinary stores: the finalize launch that follows reads them from L2 (the launches
+                        // this kernel serves are decode-sized, a few hundred KB of sums; the long ones take
+                        // wkv16.hip, which streams them)
+                        if (t < p.M) out[q * p.M + t] = v;
                     }
                 }
             }
