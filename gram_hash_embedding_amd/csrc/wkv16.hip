@@ -196,9 +196,9 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     // ---- one-round store epilogue (kHold): both stages are free.  Every wave writes its 128 tokens x 64
     // outputs as bf16 into stage wm (row t: token 128 wm + t, 512 bytes = the tile's 256 outputs, 16-byte
     // piece c at slot c ^ (t % 32)); after a barrier every wave reads 32 rows into registers (the accumulators
-    // are dead by then), a second barrier frees the stages, `refill()` issues the held-back slabs, and every
-    // wave writes its rows with full-line non-temporal 16-byte stores (two rows per instruction), which drain
-    // while the held-back slabs land and the next tile computes.
+    // are dead by then), a second barrier frees the stages, every wave writes its rows with full-line
+    // non-temporal 16-byte stores (two rows per instruction), and `refill()` issues the held-back slabs; the
+    // stores drain while those land and the next tile computes.
     auto store_epilogue = [&](const f32x4 (&acc)[8][4], int64_t m0, int n0, auto&& refill) {
         const int l = lane_id();
         const int g = l >> 4;
