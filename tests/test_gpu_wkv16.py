@@ -24,8 +24,9 @@ def _rows(rng, T):
     return np.unique(np.r_[0, 1, 255, 256, 511, 512, T - 2, T - 1, rng.integers(0, T, 90)])
 
 
-# (T, K, N): 9 x 65 tiles with an 8-column last one, 12 x 50, 32 x 16 at K = 6,144
-@pytest.mark.parametrize("T,K,N", [(2049, 192, 16392), (3000, 1536, 12800), (8191, 6144, 4096)])
+# (T, K, N): 9 x 65 tiles with an 8-column last one, 12 x 50, 32 x 16 at K = 6,144, 16 x 32 at an odd slab
+# count (25)
+@pytest.mark.parametrize("T,K,N", [(2049, 192, 16392), (3000, 1536, 12800), (8191, 6144, 4096), (4096, 1600, 8192)])
 def test_wkv16_plain_matches_the_oracle(gpu_device, T, K, N):
     import torch
 
@@ -50,8 +51,9 @@ def _kv_bf16(kv64):
 
 
 # (T, K, hc, dim): 33 x 16 value tiles at K = 192 (a 1-row last tile), the workload's layout at a ragged 9,000
-# tokens, two copies of dim 8,192
-@pytest.mark.parametrize("T,K,hc,dim", [(8193, 192, 1, 4096), (9000, 1536, 4, 5120), (16384, 384, 2, 8192)])
+# tokens, two copies of dim 8,192, an odd slab count (25) with a ragged last tile
+@pytest.mark.parametrize("T,K,hc,dim", [(8193, 192, 1, 4096), (9000, 1536, 4, 5120), (16384, 384, 2, 8192),
+                                        (8300, 1600, 2, 4096)])
 def test_wkv16_gate_matches_the_plain_launch_and_the_oracle(gpu_device, T, K, hc, dim):
     import torch
 
