@@ -22,10 +22,12 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // The bf16 projection on v_mfma_f32_16x16x32_bf16 (wkv16.hip) for one layer: whether it takes a launch of T
-// tokens (K a multiple of 64 with at least three slabs, enough tiles for two waves over the CUs in each of its
-// launches; for the gate, 128 rows of x under 2^31 bytes), and the launch.  Plain (gate false): kv [T, ld_out] = a [T, K] x w [N, K]^T.  Gate: w holds (hc + 1) dim rows; the
-// key rows are reduced against x into `part` ([hc][dim/128][3][T] fp32, what launch_gate_finalize reads) and
-// the dim value rows stored into kv [T, ld_out].  Arguments are checked by the caller.
+// tokens (K a multiple of 64 with at least three slabs, and enough tiles of all N = (hc + 1) dim columns for two
+// waves over the CUs, so that a fused launch takes it exactly when the plain one of the same weights does; for
+// the gate, 128 rows of x under 2^31 bytes), and the launch.  Plain (gate false): kv [T, ld_out] = a [T, K] x
+// w [N, K]^T.  Gate: w holds (hc + 1) dim rows; the key rows are reduced against x into `part`
+// ([hc][dim/128][3][T] fp32, what launch_gate_finalize reads) and the dim value rows stored into kv [T, ld_out].
+// Arguments are checked by the caller.
 bool wkv16_takes(int64_t T, int K, int N, int hc, int dim, bool gate);
 int launch_wkv16(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t ld_out, int64_t T, int K, int N,
                  const uint16_t* x, const uint16_t* q, const uint16_t* k, float* part, int hc, int dim, bool gate,

@@ -573,11 +573,12 @@ bool wkv16_takes(int64_t T, int K, int N, int hc, int dim, bool gate) {
     if (T < 1 || K % kSlabCols != 0 || K < 3 * kSlabCols || K > (1 << 20)) return false;
     const int64_t tiles_m = (T + BM - 1) / BM;
     if (tiles_m > 0x7FFFFF) return false;
-    // its launches (a fused one is two: key tiles, then value tiles) each at least two waves of tiles over the
-    // CUs, so that no launch ends in a mostly idle last wave
+    // at least two waves of tiles over the CUs; a fused launch counts all (hc + 1) dim columns, so that it takes
+    // these kernels exactly when the plain launch of the same weights does (its value columns are then those of
+    // the plain launch, bit for bit)
     if (!gate) return tiles_m * ((N + BN - 1) / BN) >= 2 * kCUs;
     return static_cast<int64_t>(hc + 1) * dim <= (1 << 22) &&  // 128 rows of x under 2^31 bytes
-           tiles_m * (dim / BN) >= 2 * kCUs;
+           tiles_m * ((hc + 1) * dim / BN) >= 2 * kCUs;
 }
 
 int launch_wkv16(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t ld_out, int64_t T, int K, int N,

@@ -51,9 +51,10 @@ def _kv_bf16(kv64):
 
 
 # (T, K, hc, dim): 33 x 16 value tiles at K = 192 (a 1-row last tile), the workload's layout at a ragged 9,000
-# tokens, two copies of dim 8,192, an odd slab count (25) with a ragged last tile
+# tokens, two copies of dim 8,192, an odd slab count (25) with a ragged last tile, and 12 x 20 value tiles (under
+# one wave: the fused launch follows the plain one's choice of kernel, taken on all 12 x 100 tiles)
 @pytest.mark.parametrize("T,K,hc,dim", [(8193, 192, 1, 4096), (9000, 1536, 4, 5120), (16384, 384, 2, 8192),
-                                        (8300, 1600, 2, 4096)])
+                                        (8300, 1600, 2, 4096), (3000, 1536, 4, 5120)])
 def test_wkv16_gate_matches_the_plain_launch_and_the_oracle(gpu_device, T, K, hc, dim):
     import torch
 
