@@ -1,4 +1,8 @@
 // engram_wkv: kv = A * W^T on bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+// Launches long enough for two waves of 256 x 256 tiles over the CUs per layer
+// (K a multiple of 64, at least three slabs) run wkv16.hip's
+// v_mfma_f32_16x16x32_bf16 kernels instead, layer by layer; the kernels here
+// serve decode-sized launches (one layer or several) and K not a multiple of 64.
 //
 // Computes the `wkv` Linear of Engram.forward on the DeepSeek V4.1
 // "stack-hashes" page: [T, C*D] gathered rows -> [T, dim*(hc_mult+1)] (the hc

@@ -1,7 +1,8 @@
 // The bf16 `wkv` projection, and its fused gate pre-activation, on v_mfma_f32_16x16x32_bf16: the form the
 // main launches take (DeepSeek V4.1 "stack-hashes" page: Engram.__init__'s `wkv`, and Engram.forward's
 // kv = self.wkv(...) with the gate's rstd and dot).  wkv.hip's entry points launch it for one layer's 256-token
-// tiles when K is a multiple of 64 with at least three slabs; other shapes keep wkv.hip's own kernels.
+// tiles when K is a multiple of 64 with at least three slabs and the layer makes at least two waves of tiles over
+// the CUs (a several-layer launch, layer by layer); decode-sized launches and other K keep wkv.hip's own kernels.
 //
 // Why 16 x 16 x 32: on gfx950 a register-only loop of v_mfma_f32_16x16x32_bf16 on random operands sustains
 // about 14 % more flops than one of v_mfma_f32_32x32x16_bf16 (about 1.99 against 1.74 PF on one box; the
