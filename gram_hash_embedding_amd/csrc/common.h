@@ -33,6 +33,26 @@ int launch_wkv16(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t ld_
                  const uint16_t* x, const uint16_t* q, const uint16_t* k, float* part, int hc, int dim, bool gate,
                  hipStream_t stream, const char* what);
 
+// One layer's tensors in a several-layer launch of the fused projection: a [T, K], w [(hc + 1) dim, K], the value
+// rows out kv [T, ld_out], x [T, hc, dim], q and k [hc, dim], part [hc][dim/128][3][T] fp32.
+struct W16Layer {
+    const uint16_t* a;
+    const uint16_t* w;
+    uint16_t* kv;
+    const uint16_t* x;
+    const uint16_t* q;
+    const uint16_t* k;
+    float* part;
+};
+constexpr int kW16MaxLayers = 8;
+// The fused projection of `layers` layers (at most kW16MaxLayers) as one launch of the 16 x 16 x 32 kernels, key
+// and value tiles of every layer sharing the CUs: whether it takes such a launch (K a multiple of 64 with at least
+// three slabs, dim a multiple of 256, 128 rows of x under 2^31 bytes), and the launch.  Each layer's results are
+// those of launch_wkv16 with gate true on that layer, bit for bit.  Arguments are checked by the caller.
+bool wkv16_layers_takes(int64_t T, int K, int hc, int dim, int layers);
+int launch_wkv16_layers(const W16Layer* lay, int layers, int64_t ld_out, int64_t T, int K, int hc, int dim,
+                        hipStream_t stream, const char* what);
+
 // The second launch of a fused projection + gate (wkv.hip): per (token, copy), the per-128-column partial sums
 // [hc][dim/128][3][T] of each of `layers` layers (layer e's at part + e * part_stride floats) added in slice
 // order, then dot = sum(h w key) * rsqrt(mean h^2 + eps) * rsqrt(mean key^2 + eps) * dim^-1/2.

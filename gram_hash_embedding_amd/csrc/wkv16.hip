@@ -2,7 +2,9 @@
 // main launches take (DeepSeek V4.1 "stack-hashes" page: Engram.__init__'s `wkv`, and Engram.forward's
 // kv = self.wkv(...) with the gate's rstd and dot).  wkv.hip's entry points launch it for one layer's 256-token
 // tiles when K is a multiple of 64 with at least three slabs and the layer makes at least two waves of tiles over
-// the CUs (a several-layer launch, layer by layer); decode-sized launches and other K keep wkv.hip's own kernels.
+// the CUs (a several-layer launch of long layers, layer by layer); several shorter layers of the fused projection
+// (a decode step's two) go as one launch of the mixed form, whose workgroups take every layer's key and value
+// tiles.  Launches small enough for one pass of 128-token tiles, and other K, keep wkv.hip's own kernels.
 //
 // Why 16 x 16 x 32: on gfx950 a register-only loop of v_mfma_f32_16x16x32_bf16 on random operands sustains
 // about 14 % more flops than one of v_mfma_f32_32x32x16_bf16 (about 1.99 against 1.74 PF on one box; the
@@ -50,7 +52,7 @@ constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; 
 constexpr int kSlabLoads = 16;              // direct-to-LDS loads per loader wave and slab
 constexpr int kBar = 14;                     // the slab barrier precedes unit kBar of a slab's second k-step
 
-constexpr int kHold = 1, kGate = 2;
+constexpr int kHold = 1, kGate = 2, kMixed = 3;
 
 struct W16Args {
     const uint16_t* a;   // [M, K] bf16
@@ -66,6 +68,13 @@ struct W16Args {
     const uint16_t* k;   // [hc, dim] bf16
     float* part;         // [hc][dim/128][3][M] fp32: per 128-column slice pair sum(h w key), sum(key^2), sum(h^2)
     int hc, dim;
+    // kMixed: the key and value tiles of several layers in one launch.  tiles_m = layers x tiles_ml (layer e's M
+    // tiles are e tiles_ml .. e tiles_ml + tiles_ml - 1, each starting at its own token 0); every layer's w holds
+    // N = (hc + 1) dim rows, a tile of columns below n_key = hc dim is a key tile (kGate's epilogue), any other a
+    // value tile (kHold's, into kv columns n0 - n_key).  Layer e's tensors are lay[e]'s (a, w, kv, x, q, k and
+    // part above are unused).
+    int tiles_ml, n_key;
+    W16Layer lay[kW16MaxLayers];
 };
 
 // pid -> (tm, tn): contiguous runs per XCD (pid % 8 is the XCD a workgroup lands on), grouped kGroupM deep
@@ -148,17 +157,31 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     // a tile of this workgroup: its first row and column; `live` false past the workgroup's last tile, whose
     // loads are then empty (the resources hold no bytes)
     struct TileAt {
-        int64_t m0;
+        int64_t m0;  // first token of the tile (in its layer)
         int n0;
-        bool live;
+        int flags;   // bit 0: live; kMixed: bit 1 a key tile, bits 2.. its layer
+        __device__ bool live() const { return (flags & 1) != 0; }
+        __device__ bool key() const { return (flags & 2) != 0; }
+        __device__ int e() const { return flags >> 2; }
     };
+    // layer e's tensors (kMixed), else the launch's own; e is wave-uniform
+    auto a_of = [&](int e) -> const uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].a; else return p.a; };
+    auto w_of = [&](int e) -> const uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].w; else return p.w; };
+    auto kv_of = [&](int e) -> uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].kv; else return p.kv; };
+    auto x_of = [&](int e) -> const uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].x; else return p.x; };
+    auto q_of = [&](int e) -> const uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].q; else return p.q; };
+    auto k_of = [&](int e) -> const uint16_t* { if constexpr (kMode == kMixed) return p.lay[e].k; else return p.k; };
+    auto part_of = [&](int e) -> float* { if constexpr (kMode == kMixed) return p.lay[e].part; else return p.part; };
     auto slab_rsrc = [&](const TileAt& ta, int kt) {
-        const int a_bytes = ta.live ? static_cast<int>(min<int64_t>(BM, p.M - ta.m0)) * row_bytes : 0;
-        const int w_bytes = ta.live ? min(BN, p.N - ta.n0) * row_bytes : 0;
+        int e = ta.e();
+        if constexpr (kMode == kMixed) asm volatile("" : "+s"(e));
+        const int a_bytes = ta.live() ? static_cast<int>(min<int64_t>(BM, p.M - ta.m0)) * row_bytes : 0;
+        const int w_bytes = ta.live() ? min(BN, p.N - ta.n0) * row_bytes : 0;
         SlabRsrc r;
-        r.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a + ta.m0 * p.K), 0, a_bytes, kBufferWord3);
-        r.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w + static_cast<int64_t>(ta.n0) * p.K), 0,
-                                                 w_bytes, kBufferWord3);
+        r.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a_of(e) + ta.m0 * p.K), 0, a_bytes,
+                                                 kBufferWord3);
+        r.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w_of(e) + static_cast<int64_t>(ta.n0) * p.K),
+                                                 0, w_bytes, kBufferWord3);
         r.k0b = static_cast<uint32_t>(kt * kSlabCols * 2);
         return r;
     };
@@ -200,16 +223,20 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     // are dead by then), a second barrier frees the stages, every wave writes its rows with full-line
     // non-temporal 16-byte stores (two rows per instruction), and `refill()` issues the held-back slabs; the
     // stores drain while those land and the next tile computes.
-    auto store_epilogue = [&](const f32x4 (&acc)[8][4], int64_t m0, int n0, auto&& refill) {
-        const int l = lane_id();
+    auto store_epilogue = [&](const f32x4 (&acc)[8][4], int e, int64_t m0, int n0, auto&& refill) {
+        const int l = kMode == kMixed ? lane_here() : lane_id();  // kMixed: nothing of it hoisted over the loop
         const int g = l >> 4;
-        uint8_t* sb = lds + wm * kStageBytes;
+        // kMixed: the wave's index formed here, so that nothing derived from it is held over the tile loop
+        int wv = wave;
+        if constexpr (kMode == kMixed) asm volatile("" : "+s"(wv));
+        const int wmv = kMode == kMixed ? (wv & 1) : wm, wnv = kMode == kMixed ? (wv >> 1) : wn;
+        uint8_t* sb = lds + wmv * kStageBytes;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = 16 * i + (l & 15);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int c = wn * 8 + 2 * j + (g >> 1);  // outputs 64 wn + 16 j + 4 g .. +3
+                const int c = wnv * 8 + 2 * j + (g >> 1);  // outputs 64 wn + 16 j + 4 g .. +3
                 const u32x2 v = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
                 *reinterpret_cast<u32x2*>(sb + t * 512 + ((c ^ (t & 31)) << 4) + (g & 1) * 8) = v;
             }
@@ -219,16 +246,17 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
         u32x4 v[16];
 #pragma unroll
         for (int ins = 0; ins < 16; ++ins) {
-            const int r = 32 * wave + 2 * ins + (l >> 5);  // row of the tile: token m0 + r
+            const int r = 32 * wv + 2 * ins + (l >> 5);  // row of the tile: token m0 + r
             v[ins] = *reinterpret_cast<const u32x4*>(lds + (r >> 7) * kStageBytes + (r & 127) * 512 + ((c ^ (r & 31)) << 4));
         }
         sync_epi();
-        const int ncol = n0 + 8 * c;
+        // kMixed: a value tile's columns n0 - n_key .. of layer e's value rows
+        const int ncol = (kMode == kMixed ? n0 - p.n_key : n0) + 8 * c;
 #pragma unroll
         for (int ins = 0; ins < 16; ++ins) {
-            const int64_t m = m0 + 32 * wave + 2 * ins + (l >> 5);
-            if (m < p.M && ncol < p.N)
-                __builtin_nontemporal_store(v[ins], reinterpret_cast<u32x4*>(p.kv + m * p.ld_out + ncol));
+            const int64_t m = m0 + 32 * wv + 2 * ins + (l >> 5);
+            if (m < p.M && ncol < (kMode == kMixed ? p.N - p.n_key : p.N))
+                __builtin_nontemporal_store(v[ins], reinterpret_cast<u32x4*>(kv_of(e) + m * p.ld_out + ncol));
         }
         refill();
     };
@@ -269,13 +297,13 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     // for odd groups (the swizzle key of group g's rows is 4 g + l / 16, mod 8).
     const uint32_t x_row_bytes = static_cast<uint32_t>(p.hc * p.dim * 2);  // < 2^24
     const uint32_t x_voff = (lane >> 3) * x_row_bytes + (((lane & 7) ^ (lane >> 4)) << 4);
-    auto x_rsrc = [&](int64_t m0, int n0) {
+    auto x_rsrc = [&](int e, int64_t m0, int n0, bool on) {
         const int64_t t0 = m0 + wm * 128;
         const int64_t rows = min<int64_t>(128, p.M - t0);
         const int64_t col = n0 + wn * 64;
-        const int bytes = rows > 0 ? static_cast<int>(rows * x_row_bytes - 2 * col) : 0;  // < 2^31
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + t0 * (x_row_bytes / 2) + col), 0, bytes,
-                                                 kBufferWord3);
+        const int bytes = on && rows > 0 ? static_cast<int>(rows * x_row_bytes - 2 * col) : 0;  // < 2^31
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x_of(e) + t0 * (x_row_bytes / 2) + col), 0,
+                                                 bytes, kBufferWord3);
     };
     // load `ins` (0..3) of round r: rows 8 ins .. 8 ins + 7 of the round's 32 tokens (the whole offset in the
     // range-checked VGPR operand; the host keeps 128 rows of x under 2^31 bytes)
@@ -288,16 +316,16 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     };
     // the slice's 64 q and 64 k elements into the wave's 512 bytes of the q/k area: q column j at byte 2 j, k
     // column j at 256 + 2 j; two loads of 4 bytes a lane whose upper 32 lanes fall outside their 128-byte resource
-    auto dma_qk = [&](int n0, int which) {
-        const uint16_t* src = (which == 0 ? p.q : p.k) + (n0 + wn * 64);
+    auto dma_qk = [&](int e, int n0, int which, bool on) {
+        const uint16_t* src = (which == 0 ? q_of(e) : k_of(e)) + (on ? n0 + wn * 64 : 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, 128, kBufferWord3),
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, on ? 128 : 0, kBufferWord3),
             qk_area + wave * 512 + which * 256, 4, static_cast<uint32_t>(lane_here() * 4), 0, 0, 0);
     };
     // The accumulators of a key tile whose last two slabs issued, in this order, the q and k loads and rounds 2
     // and 3 (10 loads), then rounds 0 and 1 (8 loads): rounds 2 and 3 are reduced first.
-    auto gate_epilogue = [&](const f32x4 (&acc)[8][4], int64_t m0, int n0, int st) {
-        const int l = lane_id();
+    auto gate_epilogue = [&](const f32x4 (&acc)[8][4], int e, int64_t m0, int n0, int st) {
+        const int l = kMode == kMixed ? lane_here() : lane_id();
         const int g = l >> 4;
         const int c = n0 / p.dim;
         own_wait(std::integral_constant<int, 8>{});  // q, k and rounds 2 and 3 (rounds 0 and 1 may fly)
@@ -379,7 +407,7 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
             const float* partner = reinterpret_cast<const float*>(hand + (wave - 4) * kXArea);
             const int64_t tbase = m0 + wm * 128 + l;
             const int pair = (n0 - c * p.dim) / 128 + (wn - 2);
-            float* out = p.part + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
+            float* out = part_of(e) + (static_cast<int64_t>(c) * (p.dim / 128) + pair) * 3 * p.M;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t t = tbase + 32 * r;
@@ -399,7 +427,16 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
     auto tile_at = [&](int t) {
         int tm, tn;
         tile_coords(p, static_cast<int>(blockIdx.x) + (t < my_tiles ? t : 0) * G, tm, tn);
-        return TileAt{static_cast<int64_t>(tm) * BM, tn * BN, t < my_tiles};
+        int flags = t < my_tiles ? 1 : 0;
+        if constexpr (kMode == kMixed) {
+            int e = 0;
+            while (tm >= p.tiles_ml) {  // at most kW16MaxLayers - 1 steps
+                tm -= p.tiles_ml;
+                ++e;
+            }
+            flags |= (tn * BN < p.n_key ? 2 : 0) | (e << 2);
+        }
+        return TileAt{static_cast<int64_t>(tm) * BM, tn * BN, flags};
     };
 
     // One k-step: acc[i][j] += (W fragment j) x (token fragment i) in two halves, W fragments 0-1 then 2-3, each
@@ -499,6 +536,8 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
         for (int t = 0; t < my_tiles; ++t) {
             const int64_t m0 = cur.m0;
             const int n0 = cur.n0;
+            const int e = cur.e();
+            const bool key_tile = cur.key();
             kt = 0;
             using T_ = std::true_type;
             using F_ = std::false_type;
@@ -517,24 +556,53 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
                     issue_slab(cur, 1, stage ^ 1);
                 }
             };
-            if constexpr (kMode == kGate) {
-                const int st = stage ^ 1;  // the last slab's stage
-                const __amdgpu_buffer_rsrc_t xr = x_rsrc(m0, n0);
-                // one load per unit after the slab barrier: q, k, then round 2's and round 3's four
+            if constexpr (kMode != kMixed) {
+                if constexpr (kMode == kGate) {
+                    const int st = stage ^ 1;  // the last slab's stage
+                    const __amdgpu_buffer_rsrc_t xr = x_rsrc(e, m0, n0, true);
+                    // one load per unit after the slab barrier: q, k, then round 2's and round 3's four
+                    slab(F_{}, F_{}, T_{}, [&](int n) {
+                        if (n < 2) dma_qk(e, n0, n, true);
+                        else if (n < 10) dma_piece(xr, 2 + ((n - 2) >> 2), (n - 2) & 3, st);
+                    });
+                    // rounds 0 and 1
+                    slab(F_{}, F_{}, F_{}, [&](int n) {
+                        if (n < 8) dma_piece(xr, n >> 2, n & 3, st);
+                    });
+                    gate_epilogue(acc, e, m0, n0, st);
+                    refill();
+                } else {
+                    slab(F_{}, F_{}, T_{}, no_extra);
+                    slab(F_{}, F_{}, F_{}, no_extra);
+                    store_epilogue(acc, e, m0, n0, refill);
+                }
+            } else {
+                // A value tile runs the key tile's last two slabs with empty resources for its loads (they write
+                // zeros), so that the slabs are one code for both kinds of tile; before the store epilogue
+                // writes the stages, every wave's loads have landed.  The whole workgroup takes one side of the
+                // test: n0 comes from the tile order alone.
+                const bool key = key_tile;
+                const int st = stage ^ 1;
+                // the layer's epilogue tensors are looked up here, not held in scalar registers over the tile
+                int el = e;
+                asm volatile("" : "+s"(el));
+                const __amdgpu_buffer_rsrc_t xr = x_rsrc(el, m0, n0, key);
                 slab(F_{}, F_{}, T_{}, [&](int n) {
-                    if (n < 2) dma_qk(n0, n);
+                    if (n < 2) dma_qk(el, n0, n, key);
                     else if (n < 10) dma_piece(xr, 2 + ((n - 2) >> 2), (n - 2) & 3, st);
                 });
-                // rounds 0 and 1
                 slab(F_{}, F_{}, F_{}, [&](int n) {
                     if (n < 8) dma_piece(xr, n >> 2, n & 3, st);
                 });
-                gate_epilogue(acc, m0, n0, st);
-                refill();
-            } else {
-                slab(F_{}, F_{}, T_{}, no_extra);
-                slab(F_{}, F_{}, F_{}, no_extra);
-                store_epilogue(acc, m0, n0, refill);
+                asm volatile("" : "+s"(el));
+                if (key) {
+                    gate_epilogue(acc, el, m0, n0, st);
+                    refill();
+                } else {
+                    own_wait(std::integral_constant<int, 0>{});
+                    sync_epi();
+                    store_epilogue(acc, el, m0, n0, refill);
+                }
             }
             if (kLoader) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));
             sync();
@@ -555,6 +623,7 @@ __device__ __forceinline__ void wkv16_body(const W16Args& p) {
 
 __global__ __launch_bounds__(kThreads, 1) void wkv16_hold_kernel(W16Args p) { wkv16_body<kHold>(p); }
 __global__ __launch_bounds__(kThreads, 1) void wkv16_gate_kernel(W16Args p) { wkv16_body<kGate>(p); }
+__global__ __launch_bounds__(kThreads, 1) void wkv16_mixed_kernel(W16Args p) { wkv16_body<kMixed>(p); }
 
 // one persistent launch over p's tiles (p.tiles_m, p.tiles_n set)
 template <int kMode>
@@ -563,6 +632,8 @@ int launch_one(const W16Args& p, hipStream_t stream, const char* what) {
     const unsigned grid = static_cast<unsigned>(tiles < kCUs ? tiles : kCUs);
     if constexpr (kMode == kGate)
         hipLaunchKernelGGL(wkv16_gate_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+    else if constexpr (kMode == kMixed)
+        hipLaunchKernelGGL(wkv16_mixed_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL(wkv16_hold_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
     return check_launch(what);
@@ -624,6 +695,32 @@ int launch_wkv16(const uint16_t* a, const uint16_t* w, uint16_t* kv, int64_t ld_
     v.tiles_m = p.tiles_m;
     v.tiles_n = dim / BN;
     return launch_one<kHold>(v, stream, what);
+}
+
+bool wkv16_layers_takes(int64_t T, int K, int hc, int dim, int layers) {
+    if (T < 1 || layers < 1 || layers > kW16MaxLayers) return false;
+    if (K % kSlabCols != 0 || K < 3 * kSlabCols || K > (1 << 20)) return false;
+    if (dim < BN || dim % BN != 0 || static_cast<int64_t>(hc + 1) * dim > (1 << 22)) return false;
+    const int64_t tiles_ml = (T + BM - 1) / BM;
+    return tiles_ml * layers * ((hc + 1) * dim / BN) <= 0x7FFFFFFF;
+}
+
+int launch_wkv16_layers(const W16Layer* lay, int layers, int64_t ld_out, int64_t T, int K, int hc, int dim,
+                        hipStream_t stream, const char* what) {
+    if (!wkv16_layers_takes(T, K, hc, dim, layers)) return fail(ENGRAM_EINVAL, "%s: no several-layer launch", what);
+    W16Args p = {};
+    p.M = T;
+    p.K = K;
+    p.N = (hc + 1) * dim;
+    p.ld_out = ld_out;
+    p.hc = hc;
+    p.dim = dim;
+    p.tiles_ml = static_cast<int>((T + BM - 1) / BM);
+    p.tiles_m = p.tiles_ml * layers;
+    p.tiles_n = p.N / BN;
+    p.n_key = hc * dim;
+    for (int e = 0; e < layers; ++e) p.lay[e] = lay[e];
+    return launch_one<kMixed>(p, stream, what);
 }
 
 }  // namespace engram

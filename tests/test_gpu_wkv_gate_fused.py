@@ -127,9 +127,11 @@ def test_gate_residual_matches_gate_output_bit_for_bit(gpu_device, T, hc, dim, m
 
 # (E, T, K, hc, dim): the decode step's two layers (one launch of 2 x 100 tiles of 256 tokens, where one layer
 # alone takes 200 tiles of 128), a ragged token count, three layers whose 128-token tiles still fit the CUs
-# together, and layers of several tiles per CU.
+# together, and layers of several tiles per CU.  On 256-token tiles with K a multiple of 64 of at least three
+# slabs (the first two, the fourth and the last two) the layers' key and value tiles share one launch of the
+# 16 x 16 x 32 kernel: two to eight layers, ragged last tiles, one to several tiles per workgroup.
 LAYER_SHAPES = [(2, 256, 1536, 4, 5120), (2, 130, 1536, 4, 5120), (3, 200, 256, 2, 512), (2, 700, 192, 3, 768),
-                (4, 64, 64, 1, 256), (8, 40, 256, 1, 256)]
+                (4, 64, 64, 1, 256), (8, 40, 256, 1, 256), (3, 1000, 192, 2, 512), (8, 300, 192, 1, 256)]
 
 
 @pytest.mark.parametrize("E,T,K,hc,dim", LAYER_SHAPES)
@@ -172,14 +174,16 @@ def test_wkv_gate_layers_workspace_and_layer_count_checked(gpu_device):
         g.engram_wkv_gate_layers(*[[c[0]] * 9 for c in cols], 1e-20)
 
 
-def test_wkv_gate_layers_strided_values(gpu_device):
-    """Row-strided value views (one stride for all layers): only each view's dim columns are written."""
+@pytest.mark.parametrize("K", [128, 192])
+def test_wkv_gate_layers_strided_values(gpu_device, K):
+    """Row-strided value views (one stride for all layers): only each view's dim columns are written (K = 192:
+    the layers' key and value tiles in one 16 x 16 x 32 launch)."""
     import torch
 
     import gram_hash_embedding_amd as g
 
-    rng = np.random.default_rng(17)
-    E, T, K, hc, dim = 3, 150, 128, 2, 256
+    rng = np.random.default_rng(17 + K)
+    E, T, hc, dim = 3, 150, 2, 256
     ins = [_inputs(rng, T, K, hc, dim, gpu_device) for _ in range(E)]
     wide = torch.full((E, T, dim + 48), 3.0, dtype=torch.bfloat16, device=gpu_device)
     views = [wide[e, :, 16:16 + dim] for e in range(E)]
